@@ -1,0 +1,258 @@
+/*
+ * paged_decode.h -- C-ABI of the MI355X (gfx950) paged-attention decode
+ * library: a CSR page table, a split-KV partial-attention kernel, a
+ * variable-length merge of (V, LSE) states, and the host plan that sizes the
+ * split.  Method: the mlxcel pages "fused paged-attention decode v2"
+ * (PR #984), "sparse paged decode" and "cascade attention".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Status: 0 on success, a negative PD_E_* code on failure.  A failing call
+ *    writes nothing to its outputs and launches nothing; pd_last_error()
+ *    returns a thread-local message for the last failure on this thread.
+ *  - HOST pointers are ordinary CPU memory, read or written before the call
+ *    returns.  DEVICE pointers are HIP device memory owned by the caller; the
+ *    library never allocates, frees or synchronizes, and launches only on the
+ *    caller's stream (a hipStream_t passed as void*; NULL = the null stream).
+ *    Kernel faults are asynchronous: they surface at the caller's next
+ *    synchronization of that stream.
+ *  - All integer arrays are int32, all sizes are in elements.
+ *  - LSE values are base-2 log-sum-exp ("log2 units"); multiply by ln 2 for
+ *    the natural-log value.
+ *  - Inputs are read-only; outputs must not alias inputs.
+ *  - Thread safety: no global mutable state apart from the per-thread error
+ *    message and a per-device property cache filled on first use.
+ */
+#ifndef PAGED_DECODE_H
+#define PAGED_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PD_OK = 0,
+    PD_E_NULL = -1,              /* a required pointer is NULL */
+    PD_E_ARG = -2,               /* a size or count is out of range */
+    PD_E_INDPTR = -3,            /* indptr does not start at 0, decreases, or disagrees with nnz */
+    PD_E_INDEX_RANGE = -4,       /* a page id is outside [0, num_pool_pages) */
+    PD_E_LAST_PAGE_LEN = -5,     /* last_page_len outside its range for the request */
+    PD_E_FIRST_PAGE_OFFSET = -6, /* first_page_offset outside its range */
+    PD_E_GEOMETRY = -7,          /* (pages-1)*page_size + lpl - fpo != seq_len */
+    PD_E_CAPACITY = -8,          /* an output array is too small */
+    PD_E_INFEASIBLE = -9,        /* no chunk size keeps the launch within its bound */
+    PD_E_UNSUPPORTED = -10,      /* a shape, dtype or alignment with no compiled kernel */
+    PD_E_HIP = -11               /* the HIP runtime reported an error at launch */
+};
+
+enum { PD_DTYPE_FP16 = 0, PD_DTYPE_FP32 = 1 };
+
+/* Largest number of chunks a plan may emit (the pages' grid-z launch bound). */
+#define PD_MAX_CHUNKS 65535
+
+/* Message for the last failure on the calling thread ("" if none). */
+const char *pd_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * csr_validate -- PR #984, commit "cache::paged_csr" and PR body item 1.
+ *
+ * Checks a CSR page table before it reaches a kernel, because every way it
+ * can be inconsistent is an out-of-bounds read inside the kernel.  Request r
+ * owns pages indices[indptr[r] .. indptr[r+1]); its first visible token sits
+ * at entry first_page_offset[r] of its first page and its last page holds
+ * last_page_len[r] valid entries.  Rules (all HOST arrays):
+ *   indptr[0] == 0, non-decreasing;
+ *   every page id in [0, num_pool_pages);
+ *   a request with no pages has last_page_len == first_page_offset == 0
+ *   (empty or fully trimmed);
+ *   otherwise 1 <= last_page_len <= page_size (an exactly-full last page is
+ *   page_size, never 0), 0 <= first_page_offset < page_size, and for a
+ *   one-page request first_page_offset < last_page_len (retired pages are
+ *   dropped, so a page with no visible token never appears);
+ *   if seq_lens != NULL: (pages-1)*page_size + last_page_len -
+ *   first_page_offset == seq_lens[r] (0 for no pages).
+ * Returns the code of the first violation; *bad_request (nullable) receives
+ * the request it was found in (-1 when not request-specific).
+ * ---------------------------------------------------------------------- */
+int csr_validate(int32_t batch, int32_t page_size, int32_t num_pool_pages,
+                 const int32_t *indptr, const int32_t *indices,
+                 const int32_t *last_page_len, const int32_t *first_page_offset,
+                 const int32_t *seq_lens, int32_t *bad_request);
+
+/* ------------------------------------------------------------------------
+ * paged_csr_build -- PR #984, commit "cache::paged_csr" (the builder).
+ *
+ * Builds the CSR view from per-request block tables: block_tables[
+ * bt_offsets[r] + b] is the pool page of logical block b of request r (-1 for
+ * a released page); tokens [logical_start[r], written_len[r]) are visible.
+ * Fully retired pages are dropped, first_page_offset = logical_start mod
+ * page_size, last_page_len in [1, page_size], seq_lens = written_len -
+ * logical_start, rope_offsets = written_len (the absolute next position).
+ * A request with nothing visible gets no pages and lpl = fpo = 0.  All HOST;
+ * `indices` has room for `capacity` ids.  The result is validated before
+ * returning (PD_E_INDEX_RANGE if a visible block is released or beyond
+ * num_pool_pages).
+ * ---------------------------------------------------------------------- */
+int paged_csr_build(int32_t batch, int32_t page_size, int32_t num_pool_pages,
+                    const int32_t *bt_offsets, const int32_t *block_tables,
+                    const int32_t *logical_start, const int32_t *written_len,
+                    int32_t capacity, int32_t *indptr, int32_t *indices,
+                    int32_t *last_page_len, int32_t *first_page_offset,
+                    int32_t *seq_lens, int32_t *rope_offsets);
+
+/* ------------------------------------------------------------------------
+ * paged_decode_plan -- PR #984 body item 4 and commit "plan + launch";
+ * issue #898 "four composable pieces" item 4.
+ *
+ * Chooses pages_per_chunk c and emits the flat chunk list.  With P_r =
+ * indptr[r+1]-indptr[r] pages, chunks(c) = sum_r max(1, ceil(P_r / c)); each
+ * chunk is launched as num_kv_heads * q_groups workgroups.  c lies in
+ * [c_min, c_max], c_max = max(1, max_r P_r), c_min the smallest c with
+ * chunks(c) <= PD_MAX_CHUNKS (PD_E_INFEASIBLE if even c_max exceeds it).  The
+ * plan takes the largest c in that range whose workgroup count reaches
+ * target_wgs (binary search: chunks(c) is non-increasing), or c_min when
+ * none does.  fixed_pages_per_chunk > 0 pins c instead (e.g. 1 to force every
+ * request through the merge).  target_wgs <= 0 uses
+ * paged_decode_default_target_wgs() of the current device.
+ *
+ * Outputs (HOST): request_indices[n] / kv_tile_indices[n] for n < N, in
+ * request order (chunk t of request r covers its pages [t*c, (t+1)*c));
+ * o_indptr[B+1] groups each request's chunks for the merge.  Pass NULL for
+ * request_indices / kv_tile_indices to query only `info` (sizes); otherwise
+ * they must hold `capacity` >= N entries (indptr[B] + batch always suffices).
+ * info->needs_merge is 0 when every request has exactly one chunk: then the
+ * partial output, in request order, already is the answer.
+ * info->workspace_bytes = N*Hq*(D+1)*4, the fp32 partial V and LSE.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t pages_per_chunk;
+    int32_t num_chunks;
+    int32_t num_wgs;          /* num_chunks * num_kv_heads * q_groups */
+    int32_t q_groups;         /* 1: a workgroup owns every query head of its KV head */
+    int32_t needs_merge;
+    int32_t target_wgs;       /* the target actually used */
+    int64_t workspace_bytes;
+} paged_decode_plan_info;
+
+int paged_decode_plan(int32_t batch, const int32_t *indptr,
+                      int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t target_wgs, int32_t fixed_pages_per_chunk,
+                      int32_t capacity, int32_t *request_indices,
+                      int32_t *kv_tile_indices, int32_t *o_indptr,
+                      paged_decode_plan_info *info);
+
+/* ------------------------------------------------------------------------
+ * paged_decode_partial -- PR #984 kernel commit and body item 2; issue #898
+ * items 1 and 2; sparse-paged-decode doc "Indirection".
+ *
+ * One workgroup per (chunk n, KV head g): it attends the G = Hq/Hkv query
+ * heads of KV head g of request r = request_indices[n] over that chunk's
+ * visible tokens, reading every K and V row once for all G heads.  Visible
+ * token i of request r lives in page indices[indptr[r] + (fpo_r + i) /
+ * page_size] at entry (fpo_r + i) % page_size; the chunk t =
+ * kv_tile_indices[n] covers tokens [max(0, t*c*ps - fpo_r), min(n_r,
+ * (t+1)*c*ps - fpo_r)).  Scores are q.k * sm_scale (sm_scale in natural
+ * units, e.g. 1/sqrt(D)), evaluated in base 2; the output row is normalized
+ * by its own softmax denominator and its LSE is in log2 units.  A chunk with
+ * no visible token writes zeros and -inf.
+ *
+ * Layouts (DEVICE): q [batch, Hq, D] contiguous; k_pool and v_pool share
+ * element strides: element d of token entry e of page p, KV head g is at
+ * p*page_stride + e*token_stride + g*head_stride + d (D contiguous); this
+ * covers the [pages, page_size, Hkv, D] pool and the page_size=1 view of a
+ * dense [B, H, Cap, D] allocation.  q and the pools share `dtype`
+ * (PD_DTYPE_FP16 or PD_DTYPE_FP32) and must be 16-byte aligned, strides
+ * multiples of 16 bytes.  indices/indptr/last_page_len/first_page_offset
+ * are the (validated) CSR; request_indices/kv_tile_indices the plan's.
+ * Outputs: v_partial [num_chunks, Hq, D] fp32 and lse_partial [num_chunks,
+ * Hq] fp32.  Supported: D in {64, 128}; G in {1, 2, 4, 8, 12, 16}; other
+ * shapes return PD_E_UNSUPPORTED before any launch.
+ * ---------------------------------------------------------------------- */
+int paged_decode_partial(const void *q, const void *k_pool, const void *v_pool,
+                         int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                         int32_t dtype,
+                         const int32_t *indices, const int32_t *indptr,
+                         const int32_t *last_page_len, const int32_t *first_page_offset,
+                         const int32_t *request_indices, const int32_t *kv_tile_indices,
+                         int32_t num_chunks, int32_t pages_per_chunk, int32_t batch,
+                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, float sm_scale,
+                         float *v_partial, float *lse_partial, void *stream);
+
+/* ------------------------------------------------------------------------
+ * paged_merge_states -- PR #984 body item 3; issue #898 item 3;
+ * cascade-attention doc "Softmax states compose".
+ *
+ * For output row o and head h, combines input rows i in [o_indptr[o],
+ * o_indptr[o+1]): m = max_i lse_in[i,h] over finite values, w_i = 2^(lse_i -
+ * m), v_out[o,h,:] = sum_i w_i v_in[i,h,:] / sum_i w_i, lse_out[o,h] = m +
+ * log2(sum_i w_i).  Rows with lse = -inf carry no weight; a group with no
+ * finite row (or no row) gives zeros and -inf.  A NaN lse propagates.
+ * DEVICE: v_in [N, H, D] fp32 (each row already normalized), lse_in [N, H]
+ * fp32, o_indptr [num_out_rows+1] int32 (non-decreasing, o_indptr[M] <= N),
+ * v_out [M, H, D], lse_out [M, H].  Any D >= 1.
+ * ---------------------------------------------------------------------- */
+int paged_merge_states(const float *v_in, const float *lse_in, const int32_t *o_indptr,
+                       int32_t num_out_rows, int32_t num_heads, int32_t head_dim,
+                       float *v_out, float *lse_out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Cascade head stacking -- cascade-attention doc, "head stacking".
+ *
+ * Level 0 attends a page span shared by `members` requests once, as one
+ * request with members*G query heads per KV head.  Stacked head h0 =
+ * kv*(members*G) + m*G + g holds query head kv*G + g of member m, so the
+ * kernel's head-to-KV-head rule h0 / (members*G) reads KV head kv.
+ *
+ * paged_cascade_stack_q: q [members, Hq, D] (DEVICE, dtype as above) ->
+ *   q0 [1, members*Hq, D] in stacked order.
+ * paged_cascade_gather_states: builds the input of the cascade's single
+ *   merge.  Member m's merge group starts at row m*n0 + o1[m] (o1 = the
+ *   level-1 plan's o_indptr) and holds first the n0 level-0 partial rows of
+ *   v0 [n0, members*Hq, D] / lse0 [n0, members*Hq] un-stacked to [Hq, D],
+ *   then the member's level-1 rows from v1 [n1, Hq, D] / lse1 [n1, Hq]
+ *   (level-1 chunk n, of member req1[n], goes to row (req1[n]+1)*n0 + n).
+ *   v_dst [members*n0 + n1, Hq, D], lse_dst [members*n0 + n1, Hq] (fp32,
+ *   DEVICE); req1 is the level-1 plan's request_indices (DEVICE).
+ * ---------------------------------------------------------------------- */
+int paged_cascade_stack_q(const void *q, int32_t dtype, int32_t members,
+                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                          void *q0, void *stream);
+
+int paged_cascade_gather_states(const float *v0, const float *lse0, int32_t n0,
+                                const float *v1, const float *lse1, int32_t n1,
+                                const int32_t *req1, int32_t members, int32_t num_qo_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                float *v_dst, float *lse_dst, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Helpers shared by the plan and the launcher, so the two cannot drift
+ * (PR #984 kernel commit: the query-heads-per-workgroup and wave-count
+ * helpers exported next to the kernels).
+ * ---------------------------------------------------------------------- */
+/* Query heads one workgroup serves for group size G and head dim D (always
+ * G: one workgroup per KV head), or a negative code if unsupported. */
+int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dtype);
+
+/* Device target for the plan: compute units x resident partial-kernel
+ * workgroups per CU (HIP occupancy query) for the given shape on `device`.
+ * Returns the count, or a negative code. */
+int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t head_dim,
+                                    int32_t dtype);
+
+/* Host evaluation of the kernels' invariant-integer division by d
+ * (Granlund & Montgomery 1994): q[i] = n[i] / d, r[i] = n[i] % d, for
+ * n[i] < 2^31.  For testing the division on the CPU. */
+int paged_fastdiv_eval(int32_t d, const uint32_t *n, int64_t count, uint32_t *q,
+                       uint32_t *r);
+
+/* Library version string. */
+const char *pd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_DECODE_H */

@@ -1,0 +1,251 @@
+"""Thin ctypes binding of libpaged_decode.so (the C-ABI in include/paged_decode.h).
+
+Each function has the C name and only marshals arguments: host arrays are
+numpy int32, device buffers are torch tensors (or raw device addresses), the
+stream defaults to torch's current stream.  A non-zero status raises
+``PagedDecodeError`` carrying the library's message.  The library must be
+built (``python -m paged_attention_decode_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_decode.so")
+
+PD_DTYPE_FP16 = 0
+PD_DTYPE_FP32 = 1
+PD_MAX_CHUNKS = 65535
+
+ERRORS = {
+    0: "PD_OK", -1: "PD_E_NULL", -2: "PD_E_ARG", -3: "PD_E_INDPTR", -4: "PD_E_INDEX_RANGE",
+    -5: "PD_E_LAST_PAGE_LEN", -6: "PD_E_FIRST_PAGE_OFFSET", -7: "PD_E_GEOMETRY",
+    -8: "PD_E_CAPACITY", -9: "PD_E_INFEASIBLE", -10: "PD_E_UNSUPPORTED", -11: "PD_E_HIP",
+}
+CODES = {v: k for k, v in ERRORS.items()}
+
+EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
+            "paged_decode_plan", "paged_decode_partial", "paged_merge_states",
+            "paged_cascade_stack_q", "paged_cascade_gather_states",
+            "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
+            "paged_fastdiv_eval"]
+
+
+class PagedDecodeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, message))
+        self.code = code
+        self.name = ERRORS.get(code, "?")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("pages_per_chunk", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("num_wgs", ctypes.c_int32), ("q_groups", ctypes.c_int32),
+                ("needs_merge", ctypes.c_int32), ("target_wgs", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+i32p = ctypes.POINTER(ctypes.c_int32)
+u32p = ctypes.POINTER(ctypes.c_uint32)
+vp = ctypes.c_void_p
+i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+_SIGS = {
+    "pd_last_error": (ctypes.c_char_p, []),
+    "pd_version": (ctypes.c_char_p, []),
+    "csr_validate": (i32, [i32, i32, i32, i32p, i32p, i32p, i32p, i32p, i32p]),
+    "paged_csr_build": (i32, [i32, i32, i32, i32p, i32p, i32p, i32p, i32, i32p, i32p, i32p,
+                              i32p, i32p, i32p]),
+    "paged_decode_plan": (i32, [i32, i32p, i32, i32, i32, i32, i32, i32, i32p, i32p, i32p,
+                                ctypes.POINTER(PlanInfo)]),
+    "paged_decode_partial": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
+                                   i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]),
+    "paged_merge_states": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
+    "paged_cascade_stack_q": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
+    "paged_cascade_gather_states": (i32, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, vp,
+                                          vp, vp]),
+    "paged_decode_q_heads_per_wg": (i32, [i32, i32, i32]),
+    "paged_decode_default_target_wgs": (i32, [i32, i32, i32, i32]),
+    "paged_fastdiv_eval": (i32, [i32, u32p, i64, u32p, u32p]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError("libpaged_decode.so is not built (run "
+                               "`python -m paged_attention_decode_amd.build`); there is no "
+                               "fallback path")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = load().pd_last_error().decode()
+        raise PagedDecodeError(rc, msg)
+    return rc
+
+
+def _host_i32(a) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return a
+
+
+def _hp(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(i32p)
+
+
+def _dev(x) -> Optional[int]:
+    """Device address of a torch tensor (or an int address, or None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def version() -> str:
+    return load().pd_version().decode()
+
+
+def csr_validate(batch, page_size, num_pool_pages, indptr, indices, last_page_len,
+                 first_page_offset, seq_lens=None, raise_on_error=True):
+    """Returns (status, bad_request); raises PagedDecodeError by default."""
+    lib = load()
+    ip, ix = _host_i32(indptr), _host_i32(indices)
+    lp, fo = _host_i32(last_page_len), _host_i32(first_page_offset)
+    sl = None if seq_lens is None else _host_i32(seq_lens)
+    if ix.size == 0:
+        ix = np.zeros(1, np.int32)
+    bad = ctypes.c_int32(-2)
+    rc = lib.csr_validate(batch, page_size, num_pool_pages, _hp(ip), _hp(ix), _hp(lp), _hp(fo),
+                          _hp(sl), ctypes.byref(bad))
+    if raise_on_error:
+        _check(rc)
+    return rc, bad.value
+
+
+def paged_csr_build(block_tables, logical_start, written_len, page_size, num_pool_pages):
+    """Block tables (list of int32 arrays, -1 = released) -> CSR dict."""
+    lib = load()
+    b = len(block_tables)
+    off = np.zeros(b + 1, np.int32)
+    for r, t in enumerate(block_tables):
+        off[r + 1] = off[r] + len(t)
+    bt = _host_i32(np.concatenate([np.asarray(t, np.int32) for t in block_tables])
+                   if off[-1] else np.zeros(1, np.int32))
+    ls, wl = _host_i32(logical_start), _host_i32(written_len)
+    cap = max(1, int(off[-1]))
+    indptr = np.zeros(b + 1, np.int32)
+    indices = np.zeros(cap, np.int32)
+    lpl, fpo, sl, ro = (np.zeros(b, np.int32) for _ in range(4))
+    _check(lib.paged_csr_build(b, page_size, num_pool_pages, _hp(off), _hp(bt), _hp(ls),
+                               _hp(wl), cap, _hp(indptr), _hp(indices), _hp(lpl), _hp(fpo),
+                               _hp(sl), _hp(ro)))
+    return dict(indptr=indptr, indices=indices[:indptr[-1]].copy(), last_page_len=lpl,
+                first_page_offset=fpo, seq_lens=sl, rope_offsets=ro)
+
+
+def paged_decode_plan(indptr, num_qo_heads, num_kv_heads, head_dim, target_wgs=0,
+                      fixed_pages_per_chunk=0, sizes_only=False):
+    """Returns (info: PlanInfo, request_indices, kv_tile_indices, o_indptr)."""
+    lib = load()
+    ip = _host_i32(indptr)
+    b = ip.size - 1
+    info = PlanInfo()
+    oi = np.zeros(b + 1, np.int32)
+    _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, target_wgs,
+                                 fixed_pages_per_chunk, 0, None, None, _hp(oi),
+                                 ctypes.byref(info)))
+    if sizes_only:
+        return info, None, None, oi
+    cap = max(1, info.num_chunks)
+    ri = np.zeros(cap, np.int32)
+    ti = np.zeros(cap, np.int32)
+    _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, target_wgs,
+                                 fixed_pages_per_chunk, cap, _hp(ri), _hp(ti), _hp(oi),
+                                 ctypes.byref(info)))
+    return info, ri[:info.num_chunks], ti[:info.num_chunks], oi
+
+
+def paged_decode_partial(q, k_pool, v_pool, page_stride, token_stride, head_stride, dtype,
+                         indices, indptr, last_page_len, first_page_offset, request_indices,
+                         kv_tile_indices, num_chunks, pages_per_chunk, batch, num_qo_heads,
+                         num_kv_heads, head_dim, page_size, sm_scale, v_partial, lse_partial,
+                         stream=None):
+    lib = load()
+    _check(lib.paged_decode_partial(
+        _dev(q), _dev(k_pool), _dev(v_pool), page_stride, token_stride, head_stride, dtype,
+        _dev(indices), _dev(indptr), _dev(last_page_len), _dev(first_page_offset),
+        _dev(request_indices), _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch,
+        num_qo_heads, num_kv_heads, head_dim, page_size, float(sm_scale), _dev(v_partial),
+        _dev(lse_partial), _stream(stream)))
+
+
+def paged_merge_states(v_in, lse_in, o_indptr, num_out_rows, num_heads, head_dim, v_out,
+                       lse_out, stream=None):
+    lib = load()
+    _check(lib.paged_merge_states(_dev(v_in), _dev(lse_in), _dev(o_indptr), num_out_rows,
+                                  num_heads, head_dim, _dev(v_out), _dev(lse_out),
+                                  _stream(stream)))
+
+
+def paged_cascade_stack_q(q, dtype, members, num_qo_heads, num_kv_heads, head_dim, q0,
+                          stream=None):
+    _check(load().paged_cascade_stack_q(_dev(q), dtype, members, num_qo_heads, num_kv_heads,
+                                        head_dim, _dev(q0), _stream(stream)))
+
+
+def paged_cascade_gather_states(v0, lse0, n0, v1, lse1, n1, req1, members, num_qo_heads,
+                                num_kv_heads, head_dim, v_dst, lse_dst, stream=None):
+    _check(load().paged_cascade_gather_states(_dev(v0), _dev(lse0), n0, _dev(v1), _dev(lse1), n1,
+                                              _dev(req1), members, num_qo_heads, num_kv_heads,
+                                              head_dim, _dev(v_dst), _dev(lse_dst),
+                                              _stream(stream)))
+
+
+def paged_decode_q_heads_per_wg(group_size, head_dim, dtype):
+    return _check_nonneg(load().paged_decode_q_heads_per_wg(group_size, head_dim, dtype))
+
+
+def paged_decode_default_target_wgs(device, group_size, head_dim, dtype):
+    return _check_nonneg(load().paged_decode_default_target_wgs(device, group_size, head_dim,
+                                                                dtype))
+
+
+def _check_nonneg(v):
+    if v < 0:
+        _check(v)
+    return v
+
+
+def paged_fastdiv_eval(d, n):
+    n = np.ascontiguousarray(np.asarray(n, dtype=np.uint32))
+    q = np.zeros_like(n)
+    r = np.zeros_like(n)
+    _check(load().paged_fastdiv_eval(d, n.ctypes.data_as(u32p), n.size, q.ctypes.data_as(u32p),
+                                     r.ctypes.data_as(u32p)))
+    return q, r

@@ -1,0 +1,139 @@
+// Variable-length merge of (V, LSE) attention states, for gfx950.
+//
+// Method: mlxcel PR #984 body item 3 and issue #898 item 3; the algebra is
+// the cascade-attention doc's "Softmax states compose": for rows i of a
+// group, m = max lse_i, w_i = 2^(lse_i - m), V = sum w_i V_i / sum w_i, and
+// the group's LSE is m + log2(sum w_i) (base 2).  A row with lse = -inf is an
+// empty chunk and carries no weight; a group without a finite row gives
+// zeros and -inf rather than NaN.
+//
+// One thread owns four consecutive dims of one (output row, head) and walks
+// the group's rows once for the max and once for the weighted sum; the lse
+// values it reads are shared by the D/4 threads of the head and come from
+// cache.  No LDS and no barrier, so any grouping works (the cascade reuses
+// it with its own o_indptr).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pd_internal.h"
+
+namespace pd {
+namespace {
+
+template <int W>
+struct VecF;
+template <>
+struct VecF<4> {
+    using type = float4;
+};
+template <>
+struct VecF<1> {
+    using type = float;
+};
+
+__device__ __forceinline__ void fma_into(float4 &acc, float w, const float4 &v)
+{
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+}
+__device__ __forceinline__ void fma_into(float &acc, float w, const float &v) { acc = fmaf(w, v, acc); }
+__device__ __forceinline__ float4 scaled(const float4 &v, float s)
+{
+    return make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
+}
+__device__ __forceinline__ float scaled(const float &v, float s) { return v * s; }
+template <typename V>
+__device__ __forceinline__ V filled(float x);
+template <>
+__device__ __forceinline__ float4 filled<float4>(float x) { return make_float4(x, x, x, x); }
+template <>
+__device__ __forceinline__ float filled<float>(float x) { return x; }
+
+template <int W>
+__global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_in,
+                                                    const float *__restrict__ lse_in,
+                                                    const int32_t *__restrict__ o_indptr,
+                                                    int32_t num_out, int32_t num_heads,
+                                                    int32_t head_dim, float *__restrict__ v_out,
+                                                    float *__restrict__ lse_out)
+{
+    using V = typename VecF<W>::type;
+    const int per_head = head_dim / W;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(num_out) * num_heads * per_head;
+    if (idx >= total) return;
+    const int dv = int(idx % per_head);
+    const int64_t oh = idx / per_head;
+    const int h = int(oh % num_heads);
+    const int64_t o = oh / num_heads;
+    const int b = o_indptr[o];
+    const int e = o_indptr[o + 1];
+
+    float m = -INFINITY;
+    bool nan_seen = false;
+    for (int i = b; i < e; ++i) {
+        const float x = lse_in[int64_t(i) * num_heads + h];
+        nan_seen |= x != x;
+        m = fmaxf(m, x);
+    }
+    V *dst = reinterpret_cast<V *>(v_out + oh * head_dim) + dv;
+    if (nan_seen || m == -INFINITY) {
+        const float fill = nan_seen ? NAN : 0.f;
+        *dst = filled<V>(fill);
+        if (dv == 0) lse_out[oh] = nan_seen ? NAN : -INFINITY;
+        return;
+    }
+    float wsum = 0.f;
+    V acc = filled<V>(0.f);
+    for (int i = b; i < e; ++i) {
+        const float x = lse_in[int64_t(i) * num_heads + h];
+        if (x == -INFINITY) continue;   // empty chunk: no weight, V never read
+        const float w = __builtin_amdgcn_exp2f(x - m);
+        wsum += w;
+        const V vi = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
+        fma_into(acc, w, vi);
+    }
+    *dst = scaled(acc, 1.f / wsum);
+    if (dv == 0) lse_out[oh] = m + __builtin_amdgcn_logf(wsum);
+}
+
+}  // namespace
+}  // namespace pd
+
+using namespace pd;
+
+extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
+                                  const int32_t *o_indptr, int32_t num_out_rows,
+                                  int32_t num_heads, int32_t head_dim, float *v_out,
+                                  float *lse_out, void *stream)
+{
+    if (!o_indptr || !v_out || !lse_out || (!v_in && num_out_rows > 0) ||
+        (!lse_in && num_out_rows > 0))
+        return fail(PD_E_NULL, "paged_merge_states: null pointer");
+    if (num_out_rows < 0 || num_heads < 1 || head_dim < 1)
+        return fail(PD_E_ARG, "paged_merge_states: bad sizes");
+    if (num_out_rows == 0) return PD_OK;
+    const bool vec4 = head_dim % 4 == 0 &&
+                      ((reinterpret_cast<uintptr_t>(v_in) | reinterpret_cast<uintptr_t>(v_out)) & 15u) == 0;
+    const int w = vec4 ? 4 : 1;
+    const int64_t total = int64_t(num_out_rows) * num_heads * (head_dim / w);
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (vec4)
+        hipLaunchKernelGGL(merge_kernel<4>, dim3(uint32_t(blocks)), dim3(256), 0, s, v_in, lse_in,
+                           o_indptr, num_out_rows, num_heads, head_dim, v_out, lse_out);
+    else
+        hipLaunchKernelGGL(merge_kernel<1>, dim3(uint32_t(blocks)), dim3(256), 0, s, v_in, lse_in,
+                           o_indptr, num_out_rows, num_heads, head_dim, v_out, lse_out);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PD_E_HIP, std::string("paged_merge_states: launch failed: ") +
+                                  hipGetErrorString(err));
+    return PD_OK;
+}

@@ -1,0 +1,194 @@
+"""Decode steps over the C-ABI: flat split-KV decode, cascade, token-sparse.
+
+Host work here is the pages' run step (mlxcel PR #984 body item 5 and the
+commit adding plan + launch): validate the CSR view, build the plan once, keep
+the int32 arrays and workspace resident on the device, then each step is one
+partial launch plus a merge launch when some request was split.  Every
+arithmetic step runs in the library's HIP kernels; this module only moves
+arguments and allocates caller-owned buffers with torch.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _pd_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return B.PD_DTYPE_FP16
+    if t.dtype == torch.float32:
+        return B.PD_DTYPE_FP32
+    raise TypeError("q and pools must be float16 or float32")
+
+
+def pool_strides(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    """Element strides (page, token, head) of a [pages, page_size, Hkv, D]
+    pool pair; D must be contiguous and both pools laid out alike."""
+    if k_pool.dim() != 4 or k_pool.shape != v_pool.shape:
+        raise ValueError("pools must be [pages, page_size, Hkv, D] and of one shape")
+    if k_pool.stride() != v_pool.stride() or k_pool.stride(3) != 1:
+        raise ValueError("K and V pools need identical strides and a contiguous head dim")
+    return k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+
+
+def _dev_i32(a, device):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
+
+
+class PagedDecode:
+    """One batch's validated page table, plan and workspace, reusable across
+    decode steps until a request crosses a page boundary."""
+
+    def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
+                 num_kv_heads: int, head_dim: int, target_wgs: int = 0,
+                 fixed_pages_per_chunk: int = 0, device="cuda"):
+        indptr = np.asarray(csr["indptr"], np.int32)
+        self.batch = indptr.size - 1
+        self.page_size = page_size
+        self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
+        B.csr_validate(self.batch, page_size, num_pool_pages, indptr, csr["indices"],
+                       csr["last_page_len"], csr["first_page_offset"], csr.get("seq_lens"))
+        info, ri, ti, oi = B.paged_decode_plan(indptr, num_qo_heads, num_kv_heads, head_dim,
+                                               target_wgs, fixed_pages_per_chunk)
+        self.info, self.request_indices, self.kv_tile_indices, self.o_indptr = info, ri, ti, oi
+        self.device = torch.device(device)
+        idx = np.asarray(csr["indices"], np.int32)
+        self.d_indices = _dev_i32(idx if idx.size else np.zeros(1, np.int32), self.device)
+        self.d_indptr = _dev_i32(indptr, self.device)
+        self.d_lpl = _dev_i32(csr["last_page_len"], self.device)
+        self.d_fpo = _dev_i32(csr["first_page_offset"], self.device)
+        self.d_req = _dev_i32(ri, self.device)
+        self.d_tile = _dev_i32(ti, self.device)
+        self.d_oindptr = _dev_i32(oi, self.device)
+        n = info.num_chunks
+        self.v_partial = torch.empty((n, num_qo_heads, head_dim), dtype=torch.float32,
+                                     device=self.device)
+        self.lse_partial = torch.empty((n, num_qo_heads), dtype=torch.float32, device=self.device)
+        if info.needs_merge:
+            self.out = torch.empty((self.batch, num_qo_heads, head_dim), dtype=torch.float32,
+                                   device=self.device)
+            self.lse = torch.empty((self.batch, num_qo_heads), dtype=torch.float32,
+                                   device=self.device)
+        else:   # write-O-directly: the partial, in request order, is the answer
+            self.out, self.lse = self.v_partial, self.lse_partial
+
+    def plan_summary(self) -> dict:
+        i = self.info
+        return dict(pages_per_chunk=i.pages_per_chunk, num_chunks=i.num_chunks,
+                    num_wgs=i.num_wgs, needs_merge=bool(i.needs_merge),
+                    target_wgs=i.target_wgs, workspace_bytes=i.workspace_bytes)
+
+    def partial(self, q, k_pool, v_pool, sm_scale, stream=None):
+        ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
+        B.paged_decode_partial(q, k_pool, v_pool, ps_, ts_, hs_, _pd_dtype(q), self.d_indices,
+                               self.d_indptr, self.d_lpl, self.d_fpo, self.d_req, self.d_tile,
+                               self.info.num_chunks, self.info.pages_per_chunk, self.batch,
+                               self.num_qo_heads, self.num_kv_heads, self.head_dim,
+                               self.page_size, sm_scale, self.v_partial, self.lse_partial,
+                               stream)
+
+    def merge(self, stream=None):
+        if self.info.needs_merge:
+            B.paged_merge_states(self.v_partial, self.lse_partial, self.d_oindptr, self.batch,
+                                 self.num_qo_heads, self.head_dim, self.out, self.lse, stream)
+
+    def run(self, q, k_pool, v_pool, sm_scale, stream=None):
+        """One decode step: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32,
+        log2 units); the tensors are this object's buffers."""
+        if q.shape != (self.batch, self.num_qo_heads, self.head_dim) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, D] tensor")
+        if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
+            raise TypeError("q and pools must share a dtype")
+        self.partial(q, k_pool, v_pool, sm_scale, stream)
+        self.merge(stream)
+        return self.out, self.lse
+
+
+class CascadeDecode:
+    """Cascade decode for `members` requests that share their first
+    `shared_pages` pages (cascade-attention doc): level 0 attends the shared
+    span once with stacked heads, level 1 attends each member's suffix, and
+    one merge pairs every member's level-0 and level-1 states."""
+
+    def __init__(self, block_tables, written_len, *, shared_pages: int, page_size: int,
+                 num_pool_pages: int, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                 target_wgs: int = 0, target_wgs_level0: int = 0, device="cuda"):
+        m = len(block_tables)
+        self.members = m
+        self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
+        prefix = np.asarray(block_tables[0][:shared_pages], np.int32)
+        for t in block_tables:
+            if not np.array_equal(np.asarray(t[:shared_pages]), prefix):
+                raise ValueError("members do not share the span")
+        wl = np.asarray(written_len, np.int64)
+        if np.any(wl < shared_pages * page_size):
+            raise ValueError("every member must hold the whole shared span")
+        csr0 = B.paged_csr_build([prefix], [0], [shared_pages * page_size], page_size,
+                                 num_pool_pages)
+        suffix = [np.asarray(t[shared_pages:], np.int32) for t in block_tables]
+        csr1 = B.paged_csr_build(suffix, [0] * m, (wl - shared_pages * page_size).astype(np.int32),
+                                 page_size, num_pool_pages)
+        self.level0 = PagedDecode(csr0, page_size=page_size, num_pool_pages=num_pool_pages,
+                                  num_qo_heads=m * num_qo_heads, num_kv_heads=num_kv_heads,
+                                  head_dim=head_dim,
+                                  target_wgs=target_wgs_level0 or target_wgs, device=device)
+        self.level1 = PagedDecode(csr1, page_size=page_size, num_pool_pages=num_pool_pages,
+                                  num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+                                  head_dim=head_dim, target_wgs=target_wgs, device=device)
+        n0 = self.level0.info.num_chunks
+        n1 = self.level1.info.num_chunks
+        o1 = self.level1.o_indptr
+        oi = np.array([k * n0 + o1[k] for k in range(m + 1)], np.int32)
+        self.n0, self.n1 = n0, n1
+        dev = self.level0.device
+        self.d_oindptr = _dev_i32(oi, dev)
+        self.q0 = None
+        self.v_cat = torch.empty((m * n0 + n1, num_qo_heads, head_dim), dtype=torch.float32,
+                                 device=dev)
+        self.lse_cat = torch.empty((m * n0 + n1, num_qo_heads), dtype=torch.float32, device=dev)
+        self.out = torch.empty((m, num_qo_heads, head_dim), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((m, num_qo_heads), dtype=torch.float32, device=dev)
+
+    def run(self, q, k_pool, v_pool, sm_scale, stream=None):
+        m, hq, d = self.members, self.num_qo_heads, self.head_dim
+        if self.q0 is None or self.q0.dtype != q.dtype:
+            self.q0 = torch.empty((1, m * hq, d), dtype=q.dtype, device=q.device)
+        B.paged_cascade_stack_q(q, _pd_dtype(q), m, hq, self.num_kv_heads, d, self.q0, stream)
+        self.level0.partial(self.q0, k_pool, v_pool, sm_scale, stream)
+        self.level1.partial(q, k_pool, v_pool, sm_scale, stream)
+        B.paged_cascade_gather_states(self.level0.v_partial, self.level0.lse_partial, self.n0,
+                                      self.level1.v_partial, self.level1.lse_partial, self.n1,
+                                      self.level1.d_req, m, hq, self.num_kv_heads, d,
+                                      self.v_cat, self.lse_cat, stream)
+        B.paged_merge_states(self.v_cat, self.lse_cat, self.d_oindptr, m, hq, d, self.out,
+                             self.lse, stream)
+        return self.out, self.lse
+
+
+def sparse_pool_view(k_dense: torch.Tensor, v_dense: torch.Tensor):
+    """Token-sparse decode over a dense [B, Hkv, Cap, D] allocation
+    (sparse-paged-decode doc, ContiguousCacheLayout): at page_size 1 and one
+    pool head the allocation is the pool [B*Hkv*Cap, 1, 1, D] -- a view, no
+    copy.  Request r = b*Hkv + h selects rows r*Cap + position."""
+    b, hkv, cap, d = k_dense.shape
+    if v_dense.shape != k_dense.shape or not k_dense.is_contiguous() or not v_dense.is_contiguous():
+        raise ValueError("K and V allocations must be contiguous and of one shape "
+                         "(shared row mapping)")
+    return k_dense.view(b * hkv * cap, 1, 1, d), v_dense.view(b * hkv * cap, 1, 1, d)
+
+
+def sparse_fold_query(q: torch.Tensor, num_kv_heads: int):
+    """[B, Hq, 1, D] -> [B*Hkv, Hq/Hkv, D]: query head i sits under KV head
+    i // (Hq/Hkv), so folding the KV-head axis into the request axis is a
+    reshape."""
+    b, hq, one, d = q.shape
+    return q.reshape(b * num_kv_heads, hq // num_kv_heads, d)
+
+
+def sparse_block_tables(positions, cap: int, batch: int = 1):
+    """Per folded request r = b*Hkv + h: its selected pool rows."""
+    del batch
+    return [(r * cap + np.asarray(pos, np.int64)).astype(np.int32)
+            for r, pos in enumerate(positions)]

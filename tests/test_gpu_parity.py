@@ -1,0 +1,368 @@
+"""GPU parity of the HIP path against the f64 oracle (needs an MI355X).
+
+Every case feeds the same seeded inputs to both sides.  The HIP side builds
+its page table and plan with the library; the oracle builds its own page table
+by token enumeration and its own plan by exhaustive scan, and the two plans
+must agree bit-exactly before any output is compared.  Final outputs and
+every partial row are compared element by element:
+  fp32 pools: max |diff| <= 1e-5 (outputs and log2 LSE);
+  fp16 pools: max |diff| <= 2e-3 on outputs, <= 1e-3 on log2 LSE;
+and -inf LSEs (empty chunks, empty requests) must match exactly.
+Unused pool rows are NaN in the random cases, so a read outside the page
+table shows up as NaN.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from paged_attention_decode_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from paged_attention_decode_amd import binding as B  # noqa: E402
+from paged_attention_decode_amd import decode as PD  # noqa: E402
+
+NTHREADS = min(16, os.cpu_count() or 1)
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tol(dtype):
+    return (1e-5, 1e-5) if dtype == workloads.FP32 else (2e-3, 1e-3)
+
+
+def check_close(got_v, got_l, ref_v, ref_l, dtype, what):
+    tv, tl = tol(dtype)
+    got_v = np.asarray(got_v, np.float64)
+    got_l = np.asarray(got_l, np.float64)
+    assert got_v.shape == ref_v.shape and got_l.shape == ref_l.shape, what
+    assert np.all(np.isfinite(got_v)), what + ": non-finite output"
+    dv = np.max(np.abs(got_v - ref_v)) if got_v.size else 0.0
+    inf_ref = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(got_l), inf_ref), what + ": -inf LSE pattern differs"
+    fin = ~inf_ref
+    dl = np.max(np.abs(got_l[fin] - ref_l[fin])) if fin.any() else 0.0
+    say("  %s: max|dv|=%.3g max|dlse|=%.3g" % (what, dv, dl))
+    assert dv <= tv, "%s: max |dv| %.3g > %.3g" % (what, dv, tv)
+    assert dl <= tl, "%s: max |dlse| %.3g > %.3g" % (what, dl, tl)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None):
+    """HIP flat decode of workload w vs the oracle; returns the decoder."""
+    say("case %s dtype=%s B=%d Hq=%d Hkv=%d D=%d ps=%d target=%d fixed=%d" % (
+        w.name, w.dtype, w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+        target, fixed))
+    pool_pages = w.k_pool.shape[0]
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            pool_pages)
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    for k in ocsr:
+        assert np.array_equal(csr[k], ocsr[k]), k
+    dec = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
+                         num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                         head_dim=w.head_dim, target_wgs=target, fixed_pages_per_chunk=fixed)
+    info = dec.info
+    say("  plan", dec.plan_summary())
+    oplan = orc.plan(ocsr["indptr"], w.num_kv_heads, info.target_wgs,
+                     fixed_pages_per_chunk=fixed)
+    assert oplan["pages_per_chunk"] == info.pages_per_chunk
+    assert np.array_equal(oplan["request_indices"], dec.request_indices)
+    assert np.array_equal(oplan["kv_tile_indices"], dec.kv_tile_indices)
+    assert np.array_equal(oplan["o_indptr"], dec.o_indptr)
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    if stream is not None:
+        with torch.cuda.stream(stream):
+            out, lse = dec.run(q, k, v, w.sm_scale)
+        stream.synchronize()
+    else:
+        out, lse = dec.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                                 nthreads=NTHREADS)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "final")
+    if check_partials:
+        pv, pl = orc.partial(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                             oplan["request_indices"], oplan["kv_tile_indices"],
+                             oplan["pages_per_chunk"], nthreads=NTHREADS)
+        check_close(dec.v_partial.cpu().numpy(), dec.lse_partial.cpu().numpy(), pv, pl,
+                    w.dtype, "partials")
+        # the merge on the GPU's own partial rows, against the oracle merge of
+        # those same rows: isolates the merge kernel's error
+        if info.needs_merge:
+            mv, ml = orc.merge(dec.v_partial.cpu().numpy().astype(np.float64),
+                               dec.lse_partial.cpu().numpy().astype(np.float64), dec.o_indptr)
+            check_close(out.cpu().numpy(), lse.cpu().numpy(), mv, ml, workloads.FP32,
+                        "merge-of-gpu-partials")
+    return dec
+
+
+# ---------------------------------------------------------------- configs
+
+def test_tiny_fp32_single_merge_of_four(orc):
+    w = workloads.tiny_fp32()
+    dec = run_flat(orc, w, target=8)
+    assert dec.info.pages_per_chunk == 10 and dec.info.num_chunks == 4
+    assert list(dec.o_indptr) == [0, 4] and dec.info.needs_merge
+    dec = run_flat(orc, w, target=8, fixed=8)
+    assert dec.info.num_chunks == 4
+
+
+def test_tiny_fp32_poisoned_pool(orc):
+    run_flat(orc, workloads.tiny_fp32(poison_unused=True), target=8)
+
+
+@pytest.mark.parametrize("target", [0, 64, 1024])
+def test_batched_fp16(orc, target):
+    w = workloads.batched_fp16(poison_unused=True)
+    assert w.written_len[0] % w.page_size == 0          # an exactly-full last page
+    run_flat(orc, w, target=target)
+
+
+@pytest.mark.parametrize("target", [0, 1024])
+def test_long_context_fp16_full_size(orc, target):
+    w = workloads.long_context_fp16(poison_unused=True)
+    dec = run_flat(orc, w, target=target)
+    assert dec.info.needs_merge
+
+
+def test_token_sparse_page_size_one(orc):
+    s = workloads.token_sparse_fp16()
+    hkv, cap, d = s.k_dense.shape[1], s.k_dense.shape[2], s.k_dense.shape[3]
+    hq = s.q.shape[1]
+    say("case token_sparse Hq=%d Hkv=%d cap=%d topk=%d" % (hq, hkv, cap, len(s.positions[0])))
+    kd, vd = to_dev(s.k_dense), to_dev(s.v_dense)
+    kp, vp = PD.sparse_pool_view(kd, vd)
+    qf = PD.sparse_fold_query(to_dev(s.q), hkv)
+    tables = PD.sparse_block_tables(s.positions, cap)
+    lens = [len(p) for p in s.positions]
+    csr = B.paged_csr_build(tables, [0] * hkv, lens, 1, kp.shape[0])
+    dec = PD.PagedDecode(csr, page_size=1, num_pool_pages=kp.shape[0], num_qo_heads=hq // hkv,
+                         num_kv_heads=1, head_dim=d)
+    say("  plan", dec.plan_summary())
+    out, lse = dec.run(qf, kp, vp, s.sm_scale)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(1, hq, d)
+    lse = lse.cpu().numpy().reshape(1, hq)
+    # oracle: the same selection gathered straight from the dense allocation
+    ref_v = np.zeros((1, hq, d))
+    ref_l = np.zeros((1, hq))
+    g = hq // hkv
+    for i in range(hq):
+        h = i // g
+        kr = s.k_dense[0, h, s.positions[h]]
+        vr = s.v_dense[0, h, s.positions[h]]
+        ref_v[0, i], ref_l[0, i] = orc.attention_dense_f64(s.q[0, i, 0], kr, vr, s.sm_scale)
+    check_close(out, lse, ref_v, ref_l, workloads.FP16, "sparse final")
+
+
+def test_cascade_matches_flat_and_oracle(orc):
+    w = workloads.cascade_fp16(poison_unused=True)
+    flat = run_flat(orc, w, target=0, check_partials=False)
+    sp = w.extra["shared_pages"]
+    say("case cascade members=%d shared_pages=%d suffix=%s" % (
+        w.batch, sp, list(w.extra["suffix_tokens"])))
+    cas = PD.CascadeDecode(w.block_tables, w.written_len, shared_pages=sp,
+                           page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                           num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                           head_dim=w.head_dim)
+    say("  level0", cas.level0.plan_summary(), "level1", cas.level1.plan_summary())
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    out, lse = cas.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                                 nthreads=NTHREADS)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "cascade")
+    fo, fl = flat.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), fo.cpu().numpy().astype(np.float64),
+                fl.cpu().numpy().astype(np.float64), w.dtype, "cascade-vs-flat")
+
+
+def test_cascade_member_major_stacking_is_wrong(orc):
+    """Negative control: stacking heads member-major (a plain reshape) launches
+    fine and reads the wrong KV heads, so it must not match."""
+    w = workloads.cascade_fp16(seed=6, prefix_tokens=1024, suffix_lo=64, suffix_hi=128)
+    sp = w.extra["shared_pages"]
+    cas = PD.CascadeDecode(w.block_tables, w.written_len, shared_pages=sp,
+                           page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                           num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                           head_dim=w.head_dim)
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    good, _ = cas.run(q, k, v, w.sm_scale)
+    good = good.cpu().numpy().copy()
+    wrong_q0 = q.reshape(1, -1, w.head_dim).contiguous()        # member-major
+    cas.level0.partial(wrong_q0, k, v, w.sm_scale)
+    cas.level1.partial(q, k, v, w.sm_scale)
+    B.paged_cascade_gather_states(cas.level0.v_partial, cas.level0.lse_partial, cas.n0,
+                                  cas.level1.v_partial, cas.level1.lse_partial, cas.n1,
+                                  cas.level1.d_req, cas.members, w.num_qo_heads,
+                                  w.num_kv_heads, w.head_dim, cas.v_cat, cas.lse_cat)
+    B.paged_merge_states(cas.v_cat, cas.lse_cat, cas.d_oindptr, cas.members, w.num_qo_heads,
+                         w.head_dim, cas.out, cas.lse)
+    torch.cuda.synchronize()
+    bad = cas.out.cpu().numpy()
+    assert np.max(np.abs(bad - good)) > 0.05
+
+
+# ------------------------------------------------------- invariance / edges
+
+@pytest.mark.parametrize("fixed", [1, 2, 4, 8, 0])
+def test_chunk_size_invariance(orc, fixed):
+    w = workloads.random_geometry(40, batch=5, page_size=16, max_len=3000, num_qo_heads=16,
+                                  num_kv_heads=4)
+    run_flat(orc, w, target=256, fixed=fixed)
+
+
+@pytest.mark.parametrize("seed,ps", [(50, 1), (51, 3), (52, 16), (53, 64), (54, 7)])
+def test_ragged_force_merge(orc, seed, ps):
+    """pages_per_chunk = 1: every request through the merge, maximally ragged."""
+    w = workloads.random_geometry(seed, batch=7, page_size=ps, max_len=700, num_qo_heads=8,
+                                  num_kv_heads=2, p_empty=0.2, p_trim=0.5)
+    run_flat(orc, w, fixed=1)
+
+
+def test_empty_requests_do_not_poison_neighbours(orc):
+    w = workloads.generic("empty-mix", seed=60, dtype=workloads.FP16, page_size=16,
+                          num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          logical_start=[0, 0, 40, 100, 0], written_len=[300, 0, 40, 777, 5],
+                          poison_unused=True)
+    for fixed in (0, 1, 3):
+        dec = run_flat(orc, w, target=64, fixed=fixed)
+        out = dec.out.cpu().numpy()
+        lse = dec.lse.cpu().numpy()
+        for r in (1, 2):
+            assert np.all(out[r] == 0) and np.all(np.isneginf(lse[r]))
+
+
+def test_reverse_order_pages(orc):
+    w = workloads.generic("reverse", seed=61, dtype=workloads.FP16, page_size=16,
+                          num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                          logical_start=[0, 9, 0], written_len=[2000, 1500, 33],
+                          poison_unused=True, reverse_pages=True)
+    run_flat(orc, w, target=128)
+
+
+def test_windows_start_mid_page_single_page(orc):
+    # one-page windows whose first entry is not 0, plus a page-crossing window
+    w = workloads.generic("midpage", seed=62, dtype=workloads.FP32, page_size=16,
+                          num_qo_heads=4, num_kv_heads=1, head_dim=64,
+                          logical_start=[3, 17, 30, 0], written_len=[9, 31, 34, 16],
+                          poison_unused=True)
+    run_flat(orc, w, fixed=1)
+    run_flat(orc, w, target=1)
+
+
+def test_many_pages_per_chunk_cross_lds_window(orc):
+    """A chunk with more page ids than one LDS staging round (page_size 1)."""
+    w = workloads.generic("long-ps1", seed=63, dtype=workloads.FP16, page_size=1,
+                          num_qo_heads=4, num_kv_heads=1, head_dim=128,
+                          logical_start=[0, 500], written_len=[3000, 2600], poison_unused=True)
+    run_flat(orc, w, target=1)
+
+
+@pytest.mark.parametrize("dtype", [workloads.FP16, workloads.FP32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 12, 16])
+def test_group_and_head_dim_variants(orc, dtype, d, g):
+    hkv = 2
+    w = workloads.random_geometry(70 + g + d, batch=3, page_size=16, max_len=900, dtype=dtype,
+                                  num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d)
+    run_flat(orc, w, target=32)
+
+
+def test_runs_on_a_side_stream(orc):
+    s = torch.cuda.Stream()
+    run_flat(orc, workloads.batched_fp16(), target=256, stream=s)
+
+
+def test_strided_pool_with_padding(orc):
+    """Pool rows padded in the page and head axes (non-contiguous strides)."""
+    w = workloads.generic("strided", seed=64, dtype=workloads.FP16, page_size=8,
+                          num_qo_heads=8, num_kv_heads=2, head_dim=64,
+                          logical_start=[0, 5], written_len=[100, 77])
+    pages = w.k_pool.shape[0]
+    kbig = np.full((pages, 9, 3, 64), np.nan, np.float16)
+    vbig = np.full((pages, 9, 3, 64), np.nan, np.float16)
+    kbig[:, :8, :2] = w.k_pool
+    vbig[:, :8, :2] = w.v_pool
+    kd, vd = to_dev(kbig)[:, :8, :2], to_dev(vbig)[:, :8, :2]
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, 8, pages)
+    dec = PD.PagedDecode(csr, page_size=8, num_pool_pages=pages, num_qo_heads=8,
+                         num_kv_heads=2, head_dim=64, target_wgs=8)
+    out, lse = dec.run(to_dev(w.q), kd, vd, w.sm_scale)
+    torch.cuda.synchronize()
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len, 8)
+    ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, 8, w.sm_scale)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "strided")
+
+
+# ------------------------------------------------------------ merge kernel
+
+def _merge_gpu(v, l, oi):
+    m = len(oi) - 1
+    h, d = l.shape[1], v.shape[2]
+    vo = torch.empty((m, h, d), dtype=torch.float32, device=DEV)
+    lo = torch.empty((m, h), dtype=torch.float32, device=DEV)
+    B.paged_merge_states(to_dev(v.astype(np.float32)), to_dev(l.astype(np.float32)),
+                         to_dev(np.asarray(oi, np.int32)), m, h, d, vo, lo)
+    torch.cuda.synchronize()
+    return vo.cpu().numpy(), lo.cpu().numpy()
+
+
+@pytest.mark.parametrize("d", [128, 64, 5])
+def test_merge_kernel_against_oracle(orc, d):
+    rng = np.random.default_rng(80 + d)
+    n, h = 60, 6
+    v = rng.standard_normal((n, h, d)).astype(np.float32)
+    l = (rng.standard_normal((n, h)) * 8).astype(np.float32)
+    l[rng.random((n, h)) < 0.2] = -np.inf
+    v[np.isneginf(l)] = 1e30                   # never read: carries no weight
+    l[10:14] = -np.inf                         # a group with no finite row
+    oi = [0, 1, 5, 5, 10, 14, 20, 33, 34, 60]  # includes an empty group
+    gv, gl = _merge_gpu(v, l, oi)
+    rv, rl = orc.merge(v.astype(np.float64), l.astype(np.float64), oi)
+    check_close(gv, gl, rv, rl, workloads.FP32, "merge d=%d" % d)
+    assert np.all(gv[4] == 0) and np.all(np.isneginf(gl[4]))
+    assert np.all(gv[2] == 0) and np.all(np.isneginf(gl[2]))
+
+
+def test_merge_kernel_regrouping(orc):
+    rng = np.random.default_rng(90)
+    n, h, d = 16, 4, 128
+    v = rng.standard_normal((n, h, d)).astype(np.float32)
+    l = (rng.standard_normal((n, h)) * 5).astype(np.float32)
+    whole_v, whole_l = _merge_gpu(v, l, [0, n])
+    pv, pl = _merge_gpu(v, l, [0, 3, 4, 9, 16])
+    gv, gl = _merge_gpu(pv, pl, [0, 4])
+    check_close(gv, gl, whole_v.astype(np.float64), whole_l.astype(np.float64),
+                workloads.FP32, "regrouped merge")
+
+
+def test_merge_kernel_nan_propagates(orc):
+    v = np.ones((2, 1, 4), np.float32)
+    l = np.array([[0.0], [np.nan]], np.float32)
+    gv, gl = _merge_gpu(v, l, [0, 2])
+    assert np.all(np.isnan(gv)) and np.isnan(gl[0, 0])
+
+
+def test_default_target_is_cu_multiple():
+    t = B.paged_decode_default_target_wgs(0, 4, 128, B.PD_DTYPE_FP16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert t >= cus and t % cus == 0

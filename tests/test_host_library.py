@@ -1,0 +1,210 @@
+"""CPU tests of the HIP library's host side (no GPU): it loads and exports
+every symbol of include/paged_decode.h; CSR building and the plan match the
+oracle bit-exactly; validation rejects every malformed table; the
+fast-divide used for page indirection matches / and %."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from paged_attention_decode_amd import binding as B
+from paged_attention_decode_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(os.path.join(ROOT, "include", "paged_decode.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    names.discard("typedef")
+    assert {"csr_validate", "paged_decode_plan", "paged_decode_partial",
+            "paged_merge_states"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTED) == names
+
+
+def test_version(lib):
+    assert "gfx950" in B.version()
+
+
+def _random_tables(rng, b, ps, max_len):
+    ls, wl, tables = [], [], []
+    for _ in range(b):
+        w = int(rng.integers(0, max_len))
+        u = rng.random()
+        s = w if u < 0.1 else (int(rng.integers(0, w + 1)) if u < 0.5 else 0)
+        if rng.random() < 0.2 and s == 0 and w >= ps:
+            w = (w // ps) * ps
+        nblk = -(-w // ps)
+        t = rng.permutation(5000)[:nblk].astype(np.int32)
+        t[: s // ps] = -1
+        ls.append(s)
+        wl.append(w)
+        tables.append(t)
+    return ls, wl, tables
+
+
+def test_csr_build_matches_oracle_bit_exact(orc):
+    rng = np.random.default_rng(21)
+    for _ in range(600):
+        ps = int(rng.choice([1, 2, 5, 8, 16, 32, 64]))
+        b = int(rng.integers(1, 7))
+        ls, wl, tables = _random_tables(rng, b, ps, 400)
+        got = B.paged_csr_build(tables, ls, wl, ps, 5000)
+        ref = orc.csr_from_block_tables(tables, ls, wl, ps)
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), k
+
+
+def test_csr_build_configs_match_oracle(orc):
+    for w in (workloads.tiny_fp32(), workloads.batched_fp16()):
+        got = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                                w.k_pool.shape[0])
+        ref = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                        w.page_size)
+        for k in ref:
+            assert np.array_equal(got[k], ref[k]), k
+
+
+def _good():
+    # two requests: 3 pages (fpo 2, lpl 5), 1 page (fpo 1, lpl 3); page size 8
+    return dict(indptr=[0, 3, 4], indices=[4, 0, 7, 2], last_page_len=[5, 3],
+                first_page_offset=[2, 1], seq_lens=[2 * 8 + 5 - 2, 2])
+
+
+@pytest.mark.parametrize("mutate,code,bad", [
+    (lambda c: c.update(indptr=[1, 3, 4]), "PD_E_INDPTR", -1),
+    (lambda c: c.update(indptr=[0, 3, 2]), "PD_E_INDPTR", 1),
+    (lambda c: c["indices"].__setitem__(2, 9), "PD_E_INDEX_RANGE", 0),
+    (lambda c: c["indices"].__setitem__(3, -1), "PD_E_INDEX_RANGE", 1),
+    (lambda c: c["last_page_len"].__setitem__(0, 0), "PD_E_LAST_PAGE_LEN", 0),
+    (lambda c: c["last_page_len"].__setitem__(0, 9), "PD_E_LAST_PAGE_LEN", 0),
+    (lambda c: c["first_page_offset"].__setitem__(0, 8), "PD_E_FIRST_PAGE_OFFSET", 0),
+    (lambda c: c["first_page_offset"].__setitem__(0, -1), "PD_E_FIRST_PAGE_OFFSET", 0),
+    (lambda c: c["first_page_offset"].__setitem__(1, 3), "PD_E_FIRST_PAGE_OFFSET", 1),
+    (lambda c: c["seq_lens"].__setitem__(1, 3), "PD_E_GEOMETRY", 1),
+])
+def test_csr_validate_rejections(lib, mutate, code, bad):
+    c = {k: list(v) for k, v in _good().items()}
+    assert B.csr_validate(2, 8, 8, **c)[0] == 0
+    mutate(c)
+    rc, where = B.csr_validate(2, 8, 8, raise_on_error=False, **c)
+    assert B.ERRORS[rc] == code
+    assert where == bad
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.csr_validate(2, 8, 8, **c)
+    assert ei.value.name == code
+
+
+def test_csr_validate_empty_request_encoding(lib):
+    ok = dict(indptr=[0, 0, 2], indices=[1, 2], last_page_len=[0, 4], first_page_offset=[0, 0],
+              seq_lens=[0, 12])
+    assert B.csr_validate(2, 8, 8, **ok)[0] == 0
+    bad = dict(ok, last_page_len=[1, 4])
+    assert B.ERRORS[B.csr_validate(2, 8, 8, raise_on_error=False, **bad)[0]] == "PD_E_LAST_PAGE_LEN"
+    bad = dict(ok, first_page_offset=[2, 0])
+    assert B.ERRORS[B.csr_validate(2, 8, 8, raise_on_error=False, **bad)[0]] == \
+        "PD_E_FIRST_PAGE_OFFSET"
+
+
+def test_csr_build_rejects(lib):
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_csr_build([np.array([-1, 3], np.int32)], [10], [20], 16, 8)
+    assert ei.value.name == "PD_E_INDEX_RANGE"
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_csr_build([np.array([0, 3], np.int32)], [0], [20], 8, 8)   # 3 blocks needed
+    assert ei.value.name == "PD_E_ARG"
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_csr_build([np.array([0, 9], np.int32)], [0], [10], 8, 8)   # page 9 not in pool
+    assert ei.value.name == "PD_E_INDEX_RANGE"
+
+
+def _plan_equal(orc, indptr, hkv, target, fixed=0, hq=None):
+    hq = hq or hkv * 4
+    info, ri, ti, oi = B.paged_decode_plan(indptr, hq, hkv, 128, target, fixed)
+    ref = orc.plan(indptr, hkv, target, fixed_pages_per_chunk=fixed)
+    assert info.pages_per_chunk == ref["pages_per_chunk"]
+    assert info.num_chunks == ref["num_chunks"]
+    assert np.array_equal(ri, ref["request_indices"])
+    assert np.array_equal(ti, ref["kv_tile_indices"])
+    assert np.array_equal(oi, ref["o_indptr"])
+    assert info.num_wgs == info.num_chunks * hkv and info.q_groups == 1
+    assert info.needs_merge == int(info.num_chunks != len(indptr) - 1)
+    assert info.workspace_bytes == info.num_chunks * hq * (128 + 1) * 4
+    return info
+
+
+def test_plan_matches_oracle_random(orc):
+    rng = np.random.default_rng(31)
+    for _ in range(400):
+        b = int(rng.integers(1, 10))
+        pages = rng.integers(0, 400, size=b)
+        pages[rng.random(b) < 0.15] = 0
+        indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        target = int(rng.integers(1, 5000))
+        _plan_equal(orc, indptr, hkv, target)
+        if rng.random() < 0.3:
+            _plan_equal(orc, indptr, hkv, target, fixed=int(rng.integers(1, 50)))
+
+
+def test_plan_long_context_targets(orc):
+    indptr = np.array([0, 2048, 4096, 6144, 6401], np.int32)
+    for t, (c, n) in {256: (227, 32), 512: (102, 66), 1024: (51, 129), 2048: (25, 257),
+                      4096: (12, 535)}.items():
+        info = _plan_equal(orc, indptr, 8, t)
+        assert (info.pages_per_chunk, info.num_chunks) == (c, n)
+
+
+def test_plan_launch_floor_and_infeasible(orc):
+    info = _plan_equal(orc, np.array([0, 100000], np.int32), 1, 10 ** 9)
+    assert info.pages_per_chunk == 2 and info.num_chunks == 50000
+    big = np.arange(0, 70000, dtype=np.int32)
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_decode_plan(big, 4, 1, 128, 1)
+    assert ei.value.name == "PD_E_INFEASIBLE"
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_decode_plan(np.array([0, 100000], np.int32), 4, 1, 128, 1, 1)
+    assert ei.value.name == "PD_E_INFEASIBLE"
+
+
+def test_plan_single_chunk_needs_no_merge(orc):
+    indptr = np.array([0, 3, 5, 5], np.int32)
+    info = _plan_equal(orc, indptr, 2, 1)
+    assert info.needs_merge == 0 and info.num_chunks == 3
+
+
+def test_q_heads_per_wg_and_unsupported(lib):
+    for g in (1, 2, 4, 8, 12, 16):
+        for d in (64, 128):
+            for dt in (0, 1):
+                assert B.paged_decode_q_heads_per_wg(g, d, dt) == g
+    for g, d in ((3, 128), (4, 96), (32, 128)):
+        with pytest.raises(B.PagedDecodeError) as ei:
+            B.paged_decode_q_heads_per_wg(g, d, 0)
+        assert ei.value.name == "PD_E_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("d", list(range(1, 257)))
+def test_fastdiv_exhaustive_small(lib, d):
+    n = np.arange(0, 1 << 16, dtype=np.uint32)
+    q, r = B.paged_fastdiv_eval(d, n)
+    assert np.array_equal(q, n // d) and np.array_equal(r, n % d)
+
+
+def test_fastdiv_wide_and_random(lib):
+    rng = np.random.default_rng(0)
+    n = np.concatenate([np.arange(0, 1 << 20, dtype=np.uint32),
+                        rng.integers(0, 1 << 31, size=1 << 20, dtype=np.uint32),
+                        np.array([(1 << 31) - 1, (1 << 31) - 2], np.uint32)])
+    for d in [1, 2, 3, 7, 16, 17, 64, 100, 128, 255, 256, 1000, 4096, 65537, (1 << 30) + 3]:
+        q, r = B.paged_fastdiv_eval(d, n)
+        assert np.array_equal(q, n // d) and np.array_equal(r, n % d), d
