@@ -1,0 +1,281 @@
+"""Benchmark: paged-attention decode (split-KV partial + merge) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload long_context_fp16]
+
+Prints ONE JSON line.  A step is one decode step of the whole batch: the
+partial kernel over every chunk of every request plus the merge.  Inputs (Q,
+K/V pools, page table, plan arrays, workspace) are resident in HBM before
+timing; the plan is built outside the timed region, as the pages' microbench
+does (PR #984, commit adding the three-way microbench).
+
+Before each timed step the L2 and the 256 MB last-level cache are flushed by
+reading a 1 GiB buffer, so every step streams its KV bytes from HBM; the step
+time is taken with HIP events on the launch stream around partial + merge
+(flush excluded).  `value` = algorithmic KV bytes / mean step time.  A warm
+(unflushed) figure is reported beside it.
+
+The GPU result is checked against the f64 oracle on the same inputs before
+anything is reported (`parity`); the oracle's own time on the host cores is
+`cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV GB/s and % of HBM peak, paged decode B=4 ctx=32k GQA fp16"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "partial_long_context_fp16_counters.md")
+PARTIAL_SRC = os.path.join(ROOT, "paged_attention_decode_amd", "csrc", "pd_partial.hip")
+
+
+def kernel_sha() -> str:
+    with open(PARTIAL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per partial launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sha") != kernel_sha():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="long_context_fp16",
+                   choices=["long_context_fp16", "batched_fp16", "tiny_fp32", "cascade_fp16"])
+    p.add_argument("--target-wgs", type=int, default=0, help="plan target (0: device default)")
+    p.add_argument("--fixed-pages-per-chunk", type=int, default=0)
+    p.add_argument("--mode", default="two-launch", choices=["fused", "two-launch"],
+                   help="fused: one launch, the last chunk of each request merges; "
+                        "two-launch: partial kernel then merge kernel")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="approximate CPU work budget of the oracle baseline")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (for counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (the decode path has no "
+              "cross-GPU exchange); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_attention_decode_amd import binding as B
+    from paged_attention_decode_amd import decode as PD
+    from paged_attention_decode_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    B.load()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = getattr(workloads, args.workload)()
+    pool_pages = w.k_pool.shape[0]
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            pool_pages)
+    if args.workload == "cascade_fp16":
+        runner = PD.CascadeDecode(w.block_tables, w.written_len,
+                                  shared_pages=w.extra["shared_pages"], page_size=w.page_size,
+                                  num_pool_pages=pool_pages, num_qo_heads=w.num_qo_heads,
+                                  num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                  target_wgs=args.target_wgs, device=dev)
+        plan = dict(level0=runner.level0.plan_summary(), level1=runner.level1.plan_summary())
+        partial_only = None
+        kv_bytes = (w.extra["shared_pages"] * w.page_size + int(w.extra["suffix_tokens"].sum())) \
+            * w.num_kv_heads * w.head_dim * 2 * 2
+    else:
+        runner = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
+                                num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                                head_dim=w.head_dim, target_wgs=args.target_wgs,
+                                fixed_pages_per_chunk=args.fixed_pages_per_chunk,
+                                fused=args.mode == "fused", device=dev)
+        plan = runner.plan_summary()
+        plan["mode"] = args.mode
+        partial_only = runner
+        kv_bytes = w.kv_bytes()
+    q = torch.from_numpy(w.q).to(dev)
+    k = torch.from_numpy(w.k_pool).to(dev)
+    v = torch.from_numpy(w.v_pool).to(dev)
+    flush = torch.empty(1 << 29, dtype=torch.float16, device=dev).normal_()   # 1 GiB
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def step():
+        return runner.run(q, k, v, w.sm_scale)
+
+    # parity gate before timing (the pages' bench refuses to time arms that disagree)
+    out, lse = step()
+    torch.cuda.synchronize()
+    got_v = out.cpu().numpy().astype(np.float64)
+    got_l = lse.cpu().numpy().astype(np.float64)
+
+    import oracle
+    ocsr = oracle.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                        w.page_size)
+    cores = len(os.sched_getaffinity(0))
+    tc = time.time()
+    ref_v, ref_l = oracle.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                                    nthreads=cores)
+    first_oracle_s = time.time() - tc
+    tv, tl = (1e-5, 1e-5) if w.dtype == workloads.FP32 else (2e-3, 1e-3)
+    dv = float(np.max(np.abs(got_v - ref_v)))
+    fin = np.isfinite(ref_l)
+    dl = float(np.max(np.abs(got_l[fin] - ref_l[fin]))) if fin.any() else 0.0
+    parity_ok = dv <= tv and dl <= tl and np.array_equal(np.isneginf(got_l), ~fin)
+    if not parity_ok:
+        print(json.dumps({"error": "parity failed", "max_abs_v": dv, "max_abs_lse": dl}))
+        sys.exit(1)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(n, do_flush):
+        tot, part = [], []
+        for _ in range(n):
+            if do_flush:
+                flush.max()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if partial_only is not None and not partial_only.fused:
+                partial_only.partial(q, k, v, w.sm_scale)
+                e1.record(stream)
+                partial_only.merge()
+            else:
+                step()
+                e1.record(stream)
+            e2.record(stream)
+            tot.append((e0, e2))
+            part.append((e0, e1))
+        torch.cuda.synchronize()
+        return ([a.elapsed_time(b) * 1e-3 for a, b in tot],
+                [a.elapsed_time(b) * 1e-3 for a, b in part])
+
+    timed(args.warmup, True)
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    step_s, part_s = timed(args.steps, True)
+    torch.cuda.synchronize()
+    wall_s = time.time() - wall0
+    warm_step_s, warm_part_s = timed(args.steps, False)
+
+    mean_step = float(np.mean(step_s))
+    value = kv_bytes / mean_step / 1e9
+    total_tokens = int(w.visible_tokens.sum())
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, random page ids from a 2x pool)",
+        "config": {
+            "workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+            "visible_tokens": [int(x) for x in w.visible_tokens],
+            "kv_bytes_per_step": int(kv_bytes), "accumulate": "fp32",
+            "cache": "L2 + LLC flushed (1 GiB read) before every timed step",
+            "plan": plan,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(total_tokens / mean_step, 1),
+        "step_us": {"mean": round(mean_step * 1e6, 2),
+                    "p10": round(float(np.percentile(step_s, 10)) * 1e6, 2),
+                    "p50": round(float(np.median(step_s)) * 1e6, 2),
+                    "p90": round(float(np.percentile(step_s, 90)) * 1e6, 2)},
+        "warm": {"step_us_mean": round(float(np.mean(warm_step_s)) * 1e6, 2),
+                 "kv_gbs": round(kv_bytes / float(np.mean(warm_step_s)) / 1e9, 2)},
+        "wall_s_timed_region_incl_flush": round(wall_s, 4),
+        "setup_s": round(setup_s, 1),
+        "parity": {"max_abs_v": dv, "max_abs_lse2": dl, "tol_v": tv, "tol_lse2": tl,
+                   "ok": bool(parity_ok)},
+    }
+    if partial_only is not None:
+        mean_part = float(np.mean(part_s))
+        achieved = kv_bytes / mean_part / 1e9
+        res["partial_us_mean"] = round(mean_part * 1e6, 2)
+        res["merge_and_gap_us_mean"] = round((mean_step - mean_part) * 1e6, 2)
+        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": counter_traffic(),
+                           "kernel": "paged_decode_partial", "kernel_sha": kernel_sha(),
+                           "bytes_per_launch": int(kv_bytes)}
+
+    if not args.no_cpu_baseline:
+        # the oracle as it stands on all host cores, repeated to fill the budget
+        reps = max(1, min(20, int(args.cpu_seconds / max(1e-3, first_oracle_s * cores))))
+        ts = [first_oracle_s]
+        for _ in range(reps - 1):
+            tc = time.time()
+            oracle.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                             nthreads=cores)
+            ts.append(time.time() - tc)
+        med = float(np.median(ts))
+        res["cpu_baseline"] = {"value": round(kv_bytes / med / 1e9, 4), "unit": "GB/s",
+                               "cores": cores, "kind": "oracle",
+                               "sample": "the whole %s step (%d visible tokens, all heads), "
+                                         "f64 oracle, %d run(s), median %.3f s wall"
+                                         % (w.name, total_tokens, len(ts), med),
+                               "cpu_model": cpu_model()}
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = int(src.numel() * 2)
+
+    print(json.dumps(res), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

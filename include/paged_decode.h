@@ -182,6 +182,35 @@ int paged_decode_partial(const void *q, const void *k_pool, const void *v_pool,
                          float *v_partial, float *lse_partial, void *stream);
 
 /* ------------------------------------------------------------------------
+ * paged_decode_fused -- the partial and the merge in one launch (PR #984 body
+ * item 5 "write O directly" for single-chunk requests; issue #898 items 2-3).
+ *
+ * Same inputs as paged_decode_partial.  A request with one chunk writes its
+ * result straight to out[r] / lse_out[r].  A request with several chunks
+ * writes its partial rows to v_partial / lse_partial (as paged_decode_partial
+ * would), then the last of its workgroups to finish -- counted per (request,
+ * KV head) in `counters` with agent-scope atomics -- merges them into out[r]
+ * exactly as paged_merge_states does and sets its counter back to zero.
+ * DEVICE: counters int32 [batch * num_kv_heads], all zero before the first
+ * call (zero them once; every completed launch leaves them zero again; after
+ * an aborted launch zero them again); out [batch, Hq, D] fp32, lse_out
+ * [batch, Hq] fp32 (log2).  request_indices must list every request's chunks
+ * contiguously with tiles 0..k-1 in order (the plan's layout).  Launches that
+ * share a counters buffer must not overlap in time.
+ * ---------------------------------------------------------------------- */
+int paged_decode_fused(const void *q, const void *k_pool, const void *v_pool,
+                       int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                       int32_t dtype,
+                       const int32_t *indices, const int32_t *indptr,
+                       const int32_t *last_page_len, const int32_t *first_page_offset,
+                       const int32_t *request_indices, const int32_t *kv_tile_indices,
+                       int32_t num_chunks, int32_t pages_per_chunk, int32_t batch,
+                       int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t page_size, float sm_scale,
+                       float *v_partial, float *lse_partial, int32_t *counters,
+                       float *out, float *lse_out, void *stream);
+
+/* ------------------------------------------------------------------------
  * paged_merge_states -- PR #984 body item 3; issue #898 item 3;
  * cascade-attention doc "Softmax states compose".
  *
@@ -241,6 +270,17 @@ int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dt
  * Returns the count, or a negative code. */
 int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t head_dim,
                                     int32_t dtype);
+
+/* Which partial kernel serves a shape: 1 = page kernel (256-byte K/V rows,
+ * group 4, 8 or 16, page_size a power-of-two multiple of 64/group slots),
+ * 0 = token kernel (every other supported shape), negative = unsupported. */
+int paged_decode_kernel_kind(int32_t dtype, int32_t head_dim, int32_t group_size,
+                             int32_t page_size, int64_t token_stride);
+
+/* Testing hook: nonzero routes every later launch in this process to the
+ * token kernel (so both kernels can be checked on the same shapes); 0
+ * restores the normal choice.  Not thread-safe with concurrent launches. */
+int paged_decode_set_kernel_choice(int32_t force_token_kernel);
 
 /* Host evaluation of the kernels' invariant-integer division by d
  * (Granlund & Montgomery 1994): q[i] = n[i] / d, r[i] = n[i] % d, for

@@ -29,7 +29,8 @@ ERRORS = {
 CODES = {v: k for k, v in ERRORS.items()}
 
 EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
-            "paged_decode_plan", "paged_decode_partial", "paged_merge_states",
+            "paged_decode_plan", "paged_decode_partial", "paged_decode_fused",
+            "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
             "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
             "paged_fastdiv_eval"]
@@ -64,7 +65,12 @@ _SIGS = {
                                 ctypes.POINTER(PlanInfo)]),
     "paged_decode_partial": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
                                    i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]),
+    "paged_decode_fused": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
+                                 i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                 vp]),
     "paged_merge_states": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
+    "paged_decode_kernel_kind": (i32, [i32, i32, i32, i32, i64]),
+    "paged_decode_set_kernel_choice": (i32, [i32]),
     "paged_cascade_stack_q": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
     "paged_cascade_gather_states": (i32, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, vp,
                                           vp, vp]),
@@ -203,6 +209,29 @@ def paged_decode_partial(q, k_pool, v_pool, page_stride, token_stride, head_stri
         _dev(request_indices), _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch,
         num_qo_heads, num_kv_heads, head_dim, page_size, float(sm_scale), _dev(v_partial),
         _dev(lse_partial), _stream(stream)))
+
+
+def paged_decode_fused(q, k_pool, v_pool, page_stride, token_stride, head_stride, dtype,
+                       indices, indptr, last_page_len, first_page_offset, request_indices,
+                       kv_tile_indices, num_chunks, pages_per_chunk, batch, num_qo_heads,
+                       num_kv_heads, head_dim, page_size, sm_scale, v_partial, lse_partial,
+                       counters, out, lse_out, stream=None):
+    lib = load()
+    _check(lib.paged_decode_fused(
+        _dev(q), _dev(k_pool), _dev(v_pool), page_stride, token_stride, head_stride, dtype,
+        _dev(indices), _dev(indptr), _dev(last_page_len), _dev(first_page_offset),
+        _dev(request_indices), _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch,
+        num_qo_heads, num_kv_heads, head_dim, page_size, float(sm_scale), _dev(v_partial),
+        _dev(lse_partial), _dev(counters), _dev(out), _dev(lse_out), _stream(stream)))
+
+
+def paged_decode_kernel_kind(dtype, head_dim, group_size, page_size, token_stride):
+    return _check_nonneg(load().paged_decode_kernel_kind(dtype, head_dim, group_size, page_size,
+                                                         token_stride))
+
+
+def paged_decode_set_kernel_choice(force_token_kernel):
+    _check(load().paged_decode_set_kernel_choice(1 if force_token_kernel else 0))
 
 
 def paged_merge_states(v_in, lse_in, o_indptr, num_out_rows, num_heads, head_dim, v_out,

@@ -42,6 +42,17 @@ __device__ __forceinline__ void fma_into(float4 &acc, float w, const float4 &v)
     acc.w = fmaf(w, v.w, acc.w);
 }
 __device__ __forceinline__ void fma_into(float &acc, float w, const float &v) { acc = fmaf(w, v, acc); }
+__device__ __forceinline__ void fma_live(float4 &acc, bool live, float w, const float4 &v)
+{
+    acc.x = live ? fmaf(w, v.x, acc.x) : acc.x;
+    acc.y = live ? fmaf(w, v.y, acc.y) : acc.y;
+    acc.z = live ? fmaf(w, v.z, acc.z) : acc.z;
+    acc.w = live ? fmaf(w, v.w, acc.w) : acc.w;
+}
+__device__ __forceinline__ void fma_live(float &acc, bool live, float w, const float &v)
+{
+    acc = live ? fmaf(w, v, acc) : acc;
+}
 __device__ __forceinline__ float4 scaled(const float4 &v, float s)
 {
     return make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
@@ -53,6 +64,11 @@ template <>
 __device__ __forceinline__ float4 filled<float4>(float x) { return make_float4(x, x, x, x); }
 template <>
 __device__ __forceinline__ float filled<float>(float x) { return x; }
+
+// Rows are visited kUnroll at a time with no branch in the loop body, so the
+// loads of several rows are in flight together: the merge runs right after
+// the partial kernel and is bound by load latency, not bandwidth.
+constexpr int kUnroll = 8;
 
 template <int W>
 __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_in,
@@ -76,10 +92,14 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
 
     float m = -INFINITY;
     bool nan_seen = false;
-    for (int i = b; i < e; ++i) {
-        const float x = lse_in[int64_t(i) * num_heads + h];
-        nan_seen |= x != x;
-        m = fmaxf(m, x);
+    for (int i0 = b; i0 < e; i0 += kUnroll) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = min(i0 + u, e - 1);
+            const float x = lse_in[int64_t(i) * num_heads + h];
+            nan_seen |= x != x;
+            m = fmaxf(m, x);
+        }
     }
     V *dst = reinterpret_cast<V *>(v_out + oh * head_dim) + dv;
     if (nan_seen || m == -INFINITY) {
@@ -90,13 +110,24 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
     }
     float wsum = 0.f;
     V acc = filled<V>(0.f);
-    for (int i = b; i < e; ++i) {
-        const float x = lse_in[int64_t(i) * num_heads + h];
-        if (x == -INFINITY) continue;   // empty chunk: no weight, V never read
-        const float w = __builtin_amdgcn_exp2f(x - m);
-        wsum += w;
-        const V vi = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
-        fma_into(acc, w, vi);
+    for (int i0 = b; i0 < e; i0 += kUnroll) {
+        float x[kUnroll];
+        V vi[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = min(i0 + u, e - 1);
+            x[u] = lse_in[int64_t(i) * num_heads + h];
+            vi[u] = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            // a row past the group end or with lse = -inf (empty chunk) has no
+            // weight, and its V (possibly not finite) is never multiplied in
+            const bool live = i0 + u < e && x[u] != -INFINITY;
+            const float w = live ? __builtin_amdgcn_exp2f(x[u] - m) : 0.f;
+            wsum += w;
+            fma_live(acc, live, w, vi[u]);
+        }
     }
     *dst = scaled(acc, 1.f / wsum);
     if (dv == 0) lse_out[oh] = m + __builtin_amdgcn_logf(wsum);

@@ -9,19 +9,37 @@
 // "Indirection": visible token i of request r is entry (fpo_r + i) %
 // page_size of page indices[indptr[r] + (fpo_r + i) / page_size].
 //
-// gfx950 mapping (not the pages' Metal/CUDA shape):
-//  - a K or V row of one head is D * sizeof(T) bytes; L = row_bytes / 16
-//    lanes load it with one dwordx4 each, so a 64-lane wave covers R = 64 / L
-//    token rows per load instruction (L = 16, R = 4 for fp16 D = 128);
-//  - q . k partial sums are reduced inside each L-lane row with DPP
-//    (quad_perm, row_half_mirror, row_mirror), leaving every lane of the row
-//    with the same score;
-//  - each row keeps its own online-softmax state (m, l, acc) per query head
-//    and updates it once per J tokens; rows are combined with lane shuffles
-//    and the four waves through LDS at the end;
-//  - the chunk's page ids are staged in LDS once, so the per-token page
-//    lookup is an LDS read rather than a dependent global load; the K/V loads
-//    of the next step are in flight while the current step computes.
+// gfx950 mapping (not the pages' Metal/CUDA shape).  A K or V row of one head
+// is D * sizeof(T) bytes; L = row_bytes / 16 lanes load it with one dwordx4
+// each, so a 64-lane wave covers R = 64 / L token rows per load instruction.
+// Two kernels share one epilogue:
+//
+//  * page kernel (rows of 256 B, i.e. L = 16: fp16 D = 128 or fp32 D = 64;
+//    G in {4, 8, 16}; page_size a multiple of the 64/G slots of one step).
+//    A wave step covers 64/G consecutive slots of ONE page, so the page id is
+//    wave-uniform: it comes from LDS into an SGPR and the load address is a
+//    scalar page base plus a per-lane offset fixed for the whole kernel (no
+//    per-token division or 64-bit multiply).  Each lane loads J = 16/G token
+//    rows; the J*G = 16 partial dot products of a 16-lane row are
+//    reduce-scattered with DPP so that lane i ends up owning the score of one
+//    (token, head) pair; the softmax then runs once per score instead of on
+//    all 16 lanes, and the probabilities reach the PV lanes by DPP
+//    row_newbcast.  The running max is only raised when a block's max exceeds
+//    it by more than 2^8 (probabilities stay <= 256 in between), so the
+//    accumulator rescale is rare.  Slots outside the visible range (before
+//    first_page_offset in the first page, from last_page_len on in the last)
+//    get score -inf and V = 0, so whatever those entries hold is never used.
+//
+//  * token kernel (any D in {64, 128}, any G, any page_size): each lane
+//    resolves its own token through a fast divide by page_size and the page
+//    ids staged in LDS; partial dots are all-reduced inside the row with DPP.
+//
+// Epilogue: the R rows of a wave are combined with lane shuffles, the four
+// waves through LDS, and the result is either written as the chunk's partial
+// row, or -- in the fused mode -- written straight to the output when the
+// request has one chunk, else written as a partial after which the last
+// workgroup of the request (found with an agent-scope atomic counter that it
+// resets to zero) merges the request's partial rows into the output.
 
 #include <hip/hip_runtime.h>
 
@@ -35,7 +53,20 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPageWindow = 1024;   // page ids staged in LDS per round
+constexpr int kPageWindow = 1024;     // page ids staged in LDS per round
+constexpr float kLazyMargin = 8.0f;   // log2 units: p <= 2^8 between rescales
+constexpr float kNoMax = -1e30f;      // finite "no score yet" running max
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer descriptor dword 3 (32-bit data)
+constexpr int kLoadNT = 2;                 // cache policy "nt": K/V rows are read exactly once
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// streaming (non-temporal) 16-byte load
+__device__ __forceinline__ uint4 load_nt(const void *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -50,13 +81,18 @@ struct PartialArgs {
     const void *q;
     const void *k;
     const void *v;
-    int64_t page_stride, token_stride, head_stride;
+    int64_t page_stride, token_stride, head_stride;   // elements
     const int32_t *indices, *indptr, *lpl, *fpo, *req_idx, *tile_idx;
     int32_t num_kv_heads, num_qo_heads, page_size, pages_per_chunk;
+    int32_t spp_log2;                                  // page kernel: steps per page = 2^spp_log2
     FastDiv fd;
     float scale_log2;
-    float *v_out;
-    float *lse_out;
+    float *v_out;        // partial rows [N, Hq, D]
+    float *lse_out;      // [N, Hq]
+    // fused mode
+    float *o_final;      // [B, Hq, D]
+    float *lse_final;    // [B, Hq]
+    int32_t *counters;   // [B, Hkv], zero between launches
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -69,18 +105,87 @@ __device__ __forceinline__ float dpp(float x)
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
+// DPP controls (gfx9 encoding)
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kRowHalfMirror = 0x141; // lane ^ 7 inside each 8 lanes
+constexpr int kRowMirror = 0x140;     // lane ^ 15 inside each 16 lanes
+constexpr int kRowRor4 = 0x124;       // lane (i + 4) mod 16 of the row
+constexpr int kRowRor8 = 0x128;       // lane (i + 8) mod 16 of the row
+template <int K>
+__device__ __forceinline__ float row_bcast(float x)   // lane K of each 16-lane row
+{
+    return dpp<0x150 + K>(x);
+}
+
+// out[k] = lane k's x, in every lane of its 16-lane row (unused entries are
+// dropped by the compiler)
+__device__ __forceinline__ void row_bcast_all(float x, float (&out)[16])
+{
+    out[0] = row_bcast<0>(x);
+    out[1] = row_bcast<1>(x);
+    out[2] = row_bcast<2>(x);
+    out[3] = row_bcast<3>(x);
+    out[4] = row_bcast<4>(x);
+    out[5] = row_bcast<5>(x);
+    out[6] = row_bcast<6>(x);
+    out[7] = row_bcast<7>(x);
+    out[8] = row_bcast<8>(x);
+    out[9] = row_bcast<9>(x);
+    out[10] = row_bcast<10>(x);
+    out[11] = row_bcast<11>(x);
+    out[12] = row_bcast<12>(x);
+    out[13] = row_bcast<13>(x);
+    out[14] = row_bcast<14>(x);
+    out[15] = row_bcast<15>(x);
+}
+
 // Sum over the L consecutive lanes of a row; every lane of the row ends with
 // the same bits (each step adds the same two operands on both partners).
 template <int L>
 __device__ __forceinline__ float row_sum(float x)
 {
     static_assert(L == 8 || L == 16 || L == 32, "row width");
-    x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
-    x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
-    x += dpp<0x141>(x);   // row_half_mirror: lane ^ 7 inside 8
-    if constexpr (L >= 16) x += dpp<0x140>(x);   // row_mirror: lane ^ 15 inside 16
+    x += dpp<kQuadXor1>(x);
+    x += dpp<kQuadXor2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    if constexpr (L >= 16) x += dpp<kRowMirror>(x);
     if constexpr (L == 32) x += __shfl_xor(x, 16);
     return x;
+}
+
+// Lane li of each 16-lane row holds x[0..15]; returns sum over the row's
+// lanes of x[li].  Four halving steps; in each, the lane keeps the half of
+// its values whose index bit matches its own lane bit and adds the partner's
+// copy of that half (partners: lane ^ 8, lane ^ 7, lane ^ 2, lane ^ 1, which
+// together span all 16 lanes).
+__device__ __forceinline__ float reduce_scatter16(const float (&x)[16], int li)
+{
+    const bool b3 = li & 8, b2 = li & 4, b1 = li & 2, b0 = li & 1;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float send = b3 ? x[k] : x[k + 8];
+        const float keep = b3 ? x[k + 8] : x[k];
+        y[k] = keep + dpp<kRowRor8>(send);
+    }
+    float z[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float send = b2 ? y[k] : y[k + 4];
+        const float keep = b2 ? y[k + 4] : y[k];
+        z[k] = keep + dpp<kRowHalfMirror>(send);
+    }
+    float w[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float send = b1 ? z[k] : z[k + 2];
+        const float keep = b1 ? z[k + 2] : z[k];
+        w[k] = keep + dpp<kQuadXor2>(send);
+    }
+    const float send = b0 ? w[0] : w[1];
+    const float keep = b0 ? w[1] : w[0];
+    return keep + dpp<kQuadXor1>(send);
 }
 
 template <typename T>
@@ -117,8 +222,324 @@ __device__ __forceinline__ float elem(const Row16 &v, int e)
     else return v.f[e];
 }
 
-template <typename T, int D, int G, int J>
-__global__ void __launch_bounds__(kThreads) partial_kernel(PartialArgs a)
+// Shared-memory image of the epilogue.
+template <int G, int D>
+struct EpilogueSmem {
+    float acc[kWaves][G][D];
+    float m[kWaves][G];
+    float l[kWaves][G];
+    int last;
+};
+
+// Combine the per-row states of the workgroup and store.  On entry every lane
+// holds, for each head h of the group, the running max m[h] and denominator
+// l[h] of its row (the same in all lanes of the row) and its VEC dims of the
+// row's accumulator acc[h].
+template <int G, int D, int L, bool FUSED>
+__device__ __forceinline__ void epilogue(const PartialArgs &a, EpilogueSmem<G, D> &sm, float (&m)[G],
+                                         float (&l)[G], float (&acc)[G][D / L], int n, int kvh,
+                                         int r, int t, int npages)
+{
+    constexpr int VEC = D / L;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int row = lane / L;
+    const int li = lane % L;
+#pragma unroll
+    for (int off = L; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(m[h], off);
+            const float lo = __shfl_xor(l[h], off);
+            const float mx = fmaxf(m[h], mo);
+            const float a1 = fast_exp2(m[h] - mx);
+            const float a2 = fast_exp2(mo - mx);
+            l[h] = l[h] * a1 + lo * a2;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float ao = __shfl_xor(acc[h][e], off);
+                acc[h][e] = acc[h][e] * a1 + ao * a2;
+            }
+            m[h] = mx;
+        }
+    }
+    if (row == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sm.acc[wave][h][li * VEC + e] = acc[h][e];
+            if (li == 0) {
+                sm.m[wave][h] = m[h];
+                sm.l[wave][h] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+
+    const int hq = a.num_qo_heads;
+    const int64_t head0 = int64_t(kvh) * G;
+    int ntiles = 1;
+    if constexpr (FUSED) {
+        const int c = a.pages_per_chunk;
+        ntiles = npages > 0 ? (npages + c - 1) / c : 1;
+    }
+    // single-chunk requests in fused mode go straight to the output
+    const bool direct = FUSED && ntiles == 1;
+    float *vdst = direct ? a.o_final + (int64_t(r) * hq + head0) * D
+                         : a.v_out + (int64_t(n) * hq + head0) * D;
+    float *ldst = direct ? a.lse_final + int64_t(r) * hq + head0 : a.lse_out + int64_t(n) * hq + head0;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D;
+        const int d = idx - h * D;
+        float mx = sm.m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][h]);
+        float lsum = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = fast_exp2(sm.m[w][h] - mx);
+            lsum = fmaf(sm.l[w][h], sc, lsum);
+            o = fmaf(sm.acc[w][h][d], sc, o);
+        }
+        vdst[int64_t(h) * D + d] = lsum > 0.f ? o / lsum : 0.f;
+        if (d == 0) ldst[h] = lsum > 0.f ? mx + fast_log2(lsum) : -INFINITY;
+    }
+    if constexpr (FUSED) {
+        if (direct) return;
+        // publish this chunk's row, then count it; the last chunk of the
+        // request merges all of them (rows n - t .. n - t + ntiles - 1)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvh;
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            sm.last = prev == ntiles - 1;
+        }
+        __syncthreads();
+        if (!sm.last) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int64_t first = n - t;
+        for (int idx = tid; idx < G * D; idx += kThreads) {
+            const int h = idx / D;
+            const int d = idx - h * D;
+            const float *lrow = a.lse_out + first * hq + head0 + h;
+            const float *vrow = a.v_out + (first * hq + head0 + h) * D + d;
+            float mx = -INFINITY;
+            for (int i = 0; i < ntiles; ++i) mx = fmaxf(mx, lrow[int64_t(i) * hq]);
+            float wsum = 0.f, o = 0.f;
+            if (mx != -INFINITY) {
+                constexpr int U = 4;
+                for (int i0 = 0; i0 < ntiles; i0 += U) {
+                    float x[U], vv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int i = min(i0 + u, ntiles - 1);
+                        x[u] = lrow[int64_t(i) * hq];
+                        vv[u] = vrow[int64_t(i) * hq * D];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const bool live = i0 + u < ntiles && x[u] != -INFINITY;
+                        const float w = live ? fast_exp2(x[u] - mx) : 0.f;
+                        wsum += w;
+                        o = live ? fmaf(w, vv[u], o) : o;
+                    }
+                }
+            }
+            a.o_final[(int64_t(r) * hq + head0 + h) * D + d] = wsum > 0.f ? o / wsum : 0.f;
+            if (d == 0)
+                a.lse_final[int64_t(r) * hq + head0 + h] = wsum > 0.f ? mx + fast_log2(wsum) : -INFINITY;
+        }
+        if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------- page kernel
+template <typename T, int G, bool FUSED>
+__global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
+{
+    constexpr int VEC = Vec<T>::N;
+    constexpr int L = 16;             // lanes per 256-byte row
+    constexpr int R = 4;              // rows per wave
+    constexpr int D = L * VEC;
+    constexpr int J = 16 / G;         // token rows per lane per step
+    constexpr int SPS = R * J;        // slots per step
+    static_assert(J * G == 16 && J >= 1, "group");
+
+    __shared__ int32_t s_pid[kPageWindow];
+    __shared__ EpilogueSmem<G, D> sm;
+
+    const int wg = blockIdx.x;
+    const int n = wg / a.num_kv_heads;
+    const int kvh = wg - n * a.num_kv_heads;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+    const int lane = tid & 63;
+    const int row = lane >> 4;
+    const int li = lane & 15;
+
+    const int r = a.req_idx[n];
+    const int t = a.tile_idx[n];
+    const int pbeg = a.indptr[r];
+    const int npages = a.indptr[r + 1] - pbeg;
+    const int fpo = a.fpo[r];
+    const int lpl = a.lpl[r];
+    const int ps = a.page_size;
+    const int cp0 = t * a.pages_per_chunk;
+    const int cp1 = min(npages, cp0 + a.pages_per_chunk);
+    const int spp_log2 = a.spp_log2;
+
+    const T *qp = static_cast<const T *>(a.q) +
+                  (int64_t(r) * a.num_qo_heads + int64_t(kvh) * G) * D + li * VEC;
+    Row16 qv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) qv[h].u = *reinterpret_cast<const uint4 *>(qp + h * D);
+
+    constexpr int ESZ = sizeof(T);
+    const char *kb = static_cast<const char *>(a.k) + int64_t(kvh) * a.head_stride * ESZ;
+    const char *vb = static_cast<const char *>(a.v) + int64_t(kvh) * a.head_stride * ESZ;
+    const int64_t page_bytes = a.page_stride * ESZ;
+    const uint32_t step_bytes = uint32_t(a.token_stride * ESZ * SPS);
+    // bytes of one page that this KV head's rows span: loads are buffer loads
+    // bounded by it (an offset past it would read 0, never another page)
+    const int32_t page_span = int32_t(int64_t(ps - 1) * a.token_stride * ESZ + D * ESZ);
+    int32_t lane_off[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        lane_off[j] = int32_t((j * R + row) * a.token_stride * ESZ) + li * 16;
+
+    float m_run = kNoMax;             // running max of head (li % G) of this row
+    float l_part = 0.f;               // denominator share of this lane's (token, head)
+    float acc[G][VEC];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+
+    const int j_own = li / G;         // the token row this lane scores
+
+    for (int wp0 = cp0; wp0 < cp1; wp0 += kPageWindow) {
+        const int wp1 = min(cp1, wp0 + kPageWindow);
+        __syncthreads();
+        for (int i = tid; i < wp1 - wp0; i += kThreads) s_pid[i] = a.indices[pbeg + wp0 + i];
+        __syncthreads();
+        const int nsteps = (wp1 - wp0) << spp_log2;
+
+        auto load = [&](int s, Row16 (&kr)[J], Row16 (&vr)[J]) {
+            const int p = s >> spp_log2;
+            const int sub = s & ((1 << spp_log2) - 1);
+            const int pid = __builtin_amdgcn_readfirstlane(s_pid[p]);
+            const int64_t base = int64_t(pid) * page_bytes;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(kb + base), 0, page_span, kBufferWord3);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(vb + base), 0, page_span, kBufferWord3);
+            const int soff = int(sub * step_bytes);
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                kr[j].u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off[j], soff, kLoadNT));
+                vr[j].u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off[j], soff, kLoadNT));
+            }
+        };
+
+        auto compute = [&](int s, const Row16 (&kr)[J], Row16 (&vr)[J]) {
+            const int p = wp0 + (s >> spp_log2);          // request-relative page
+            const int sub = s & ((1 << spp_log2) - 1);
+            float x[16];
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+#pragma unroll
+                for (int h = 0; h < G; ++h) x[j * G + h] = dot_row<T>(qv[h], kr[j]);
+            float sc = reduce_scatter16(x, li) * a.scale_log2;
+            // slots outside the visible range: first page before fpo, last
+            // page from lpl on
+            const bool edge = (p == 0 && fpo > 0) || (p == npages - 1 && lpl < ps);
+            if (edge) {
+                const int lo = p == 0 ? fpo : 0;
+                const int hi = p == npages - 1 ? lpl : ps;
+                const int slot_own = sub * SPS + j_own * R + row;
+                sc = (slot_own >= lo && slot_own < hi) ? sc : -INFINITY;
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int slot = sub * SPS + j * R + row;
+                    const bool ok = slot >= lo && slot < hi;
+                    vr[j].u.x = ok ? vr[j].u.x : 0u;
+                    vr[j].u.y = ok ? vr[j].u.y : 0u;
+                    vr[j].u.z = ok ? vr[j].u.z : 0u;
+                    vr[j].u.w = ok ? vr[j].u.w : 0u;
+                }
+            }
+            // block max over the J lanes that hold the same head
+            float mb = sc;
+            if constexpr (J >= 2) mb = fmaxf(mb, dpp<G == 8 ? kRowRor8 : kRowRor4>(mb));
+            if constexpr (J == 4) mb = fmaxf(mb, dpp<kRowRor8>(mb));
+            const bool need = mb > m_run + kLazyMargin;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float m_new = need ? mb : m_run;
+                const float alpha = fast_exp2(m_run - m_new);
+                l_part *= alpha;
+                m_run = m_new;
+                float ab[16];            // lane h of the row holds head h
+                row_bcast_all(alpha, ab);
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[h][e] *= ab[h];
+            }
+            const float pl = fast_exp2(sc - m_run);
+            l_part += pl;
+            float pb[16];                // p of (token j, head h) is in lane j*G + h
+            row_bcast_all(pl, pb);
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float y = acc[h][e];
+#pragma unroll
+                    for (int j = 0; j < J; ++j) y = fmaf(pb[j * G + h], elem<T>(vr[j], e), y);
+                    acc[h][e] = y;
+                }
+        };
+
+        Row16 k0[J], v0[J], k1[J], v1[J];
+        int s = wave;
+        if (s < nsteps) load(s, k0, v0);
+        while (s < nsteps) {
+            const int s1 = s + kWaves;
+            if (s1 < nsteps) load(s1, k1, v1);
+            compute(s, k0, v0);
+            if (s1 >= nsteps) break;
+            const int s2 = s1 + kWaves;
+            if (s2 < nsteps) load(s2, k0, v0);
+            compute(s1, k1, v1);
+            s = s2;
+        }
+    }
+
+    // per-row state for every head: head h lives in lanes li = h (mod G); the
+    // J lanes of a head share m_run and split l
+    float lsum = l_part;
+    if constexpr (J >= 2) lsum += dpp<G == 8 ? kRowRor8 : kRowRor4>(lsum);
+    if constexpr (J == 4) lsum += dpp<kRowRor8>(lsum);
+    float m[G], l[G];
+    {
+        float tm[16], tl[16];
+        row_bcast_all(m_run, tm);
+        row_bcast_all(lsum, tl);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            m[h] = tm[h];
+            l[h] = tl[h];
+        }
+    }
+    epilogue<G, D, L, FUSED>(a, sm, m, l, acc, n, kvh, r, t, npages);
+}
+
+// --------------------------------------------------------------- token kernel
+template <typename T, int D, int G, int J, bool FUSED>
+__global__ void __launch_bounds__(kThreads) partial_token_kernel(PartialArgs a)
 {
     constexpr int VEC = Vec<T>::N;
     constexpr int L = D / VEC;        // lanes per token row
@@ -127,9 +548,7 @@ __global__ void __launch_bounds__(kThreads) partial_kernel(PartialArgs a)
     static_assert(L * VEC == D && R * L == 64, "shape");
 
     __shared__ int32_t s_pid[kPageWindow];
-    __shared__ float s_acc[kWaves][G][D];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
+    __shared__ EpilogueSmem<G, D> sm;
 
     const int wg = blockIdx.x;
     const int n = wg / a.num_kv_heads;
@@ -165,7 +584,7 @@ __global__ void __launch_bounds__(kThreads) partial_kernel(PartialArgs a)
     float m[G], l[G], acc[G][VEC];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
+        m[h] = kNoMax;
         l[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
@@ -191,8 +610,8 @@ __global__ void __launch_bounds__(kThreads) partial_kernel(PartialArgs a)
                 const uint32_t e = slot - pi * uint32_t(ps);
                 const int64_t pid = s_pid[int(pi) - wp0];
                 const int64_t off = pid * a.page_stride + int64_t(e) * a.token_stride;
-                kr[j].u = *reinterpret_cast<const uint4 *>(kbase + off);
-                vr[j].u = *reinterpret_cast<const uint4 *>(vbase + off);
+                kr[j].u = load_nt(kbase + off);
+                vr[j].u = load_nt(vbase + off);
             }
         };
 
@@ -212,13 +631,12 @@ __global__ void __launch_bounds__(kThreads) partial_kernel(PartialArgs a)
                 float mx = m[h];
 #pragma unroll
                 for (int j = 0; j < J; ++j) mx = fmaxf(mx, sc[j][h]);
-                const float ms = mx == -INFINITY ? 0.f : mx;
-                const float alpha = fast_exp2(m[h] - ms);
+                const float alpha = fast_exp2(m[h] - mx);
                 float p[J];
                 float psum = 0.f;
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    p[j] = fast_exp2(sc[j][h] - ms);
+                    p[j] = fast_exp2(sc[j][h] - mx);
                     psum += p[j];
                 }
                 l[h] = fmaf(l[h], alpha, psum);
@@ -247,94 +665,151 @@ __global__ void __launch_bounds__(kThreads) partial_kernel(PartialArgs a)
             s = s2;
         }
     }
-
-    // combine the R rows of each wave (lanes li, li + L, ... hold the same dims)
-#pragma unroll
-    for (int off = L; off < 64; off <<= 1) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mo = __shfl_xor(m[h], off);
-            const float lo = __shfl_xor(l[h], off);
-            const float mx = fmaxf(m[h], mo);
-            const float ms = mx == -INFINITY ? 0.f : mx;
-            const float a1 = fast_exp2(m[h] - ms);
-            const float a2 = fast_exp2(mo - ms);
-            l[h] = l[h] * a1 + lo * a2;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float ao = __shfl_xor(acc[h][e], off);
-                acc[h][e] = acc[h][e] * a1 + ao * a2;
-            }
-            m[h] = mx;
-        }
-    }
-    if (row == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) s_acc[wave][h][li * VEC + e] = acc[h][e];
-            if (li == 0) {
-                s_m[wave][h] = m[h];
-                s_l[wave][h] = l[h];
-            }
-        }
-    }
-    __syncthreads();
-    const int64_t out_head0 = int64_t(n) * a.num_qo_heads + int64_t(kvh) * G;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D;
-        const int d = idx - h * D;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, s_m[w][h]);
-        const float ms = mx == -INFINITY ? 0.f : mx;
-        float lsum = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float sc = fast_exp2(s_m[w][h] - ms);
-            lsum = fmaf(s_l[w][h], sc, lsum);
-            o = fmaf(s_acc[w][h][d], sc, o);
-        }
-        a.v_out[(out_head0 + h) * D + d] = lsum > 0.f ? o / lsum : 0.f;
-        if (d == 0) a.lse_out[out_head0 + h] = mx == -INFINITY ? -INFINITY : mx + fast_log2(lsum);
-    }
+    epilogue<G, D, L, FUSED>(a, sm, m, l, acc, n, kvh, r, t, npages);
 }
 
-template <typename T, int D, int G>
-constexpr int tokens_per_row_step()
+// ------------------------------------------------------------------- dispatch
+using KernelFn = void (*)(PartialArgs);
+
+template <int G>
+constexpr int token_rows_per_step()
 {
     return G <= 4 ? 4 : (G <= 8 ? 2 : 1);
 }
 
-using KernelFn = void (*)(PartialArgs);
-
-template <typename T, int D>
-KernelFn pick_g(int g)
+template <typename T, int D, bool FUSED>
+KernelFn pick_token(int g)
 {
     switch (g) {
-    case 1: return partial_kernel<T, D, 1, tokens_per_row_step<T, D, 1>()>;
-    case 2: return partial_kernel<T, D, 2, tokens_per_row_step<T, D, 2>()>;
-    case 4: return partial_kernel<T, D, 4, tokens_per_row_step<T, D, 4>()>;
-    case 8: return partial_kernel<T, D, 8, tokens_per_row_step<T, D, 8>()>;
-    case 12: return partial_kernel<T, D, 12, tokens_per_row_step<T, D, 12>()>;
-    case 16: return partial_kernel<T, D, 16, tokens_per_row_step<T, D, 16>()>;
+    case 1: return partial_token_kernel<T, D, 1, token_rows_per_step<1>(), FUSED>;
+    case 2: return partial_token_kernel<T, D, 2, token_rows_per_step<2>(), FUSED>;
+    case 4: return partial_token_kernel<T, D, 4, token_rows_per_step<4>(), FUSED>;
+    case 8: return partial_token_kernel<T, D, 8, token_rows_per_step<8>(), FUSED>;
+    case 12: return partial_token_kernel<T, D, 12, token_rows_per_step<12>(), FUSED>;
+    case 16: return partial_token_kernel<T, D, 16, token_rows_per_step<16>(), FUSED>;
     default: return nullptr;
     }
 }
 
-KernelFn pick_kernel(int dtype, int d, int g)
+template <typename T, bool FUSED>
+KernelFn pick_page(int g)
 {
-    if (dtype == PD_DTYPE_FP16) {
-        if (d == 64) return pick_g<_Float16, 64>(g);
-        if (d == 128) return pick_g<_Float16, 128>(g);
-    } else if (dtype == PD_DTYPE_FP32) {
-        if (d == 64) return pick_g<float, 64>(g);
-        if (d == 128) return pick_g<float, 128>(g);
+    switch (g) {
+    case 4: return partial_page_kernel<T, 4, FUSED>;
+    case 8: return partial_page_kernel<T, 8, FUSED>;
+    case 16: return partial_page_kernel<T, 16, FUSED>;
+    default: return nullptr;
     }
-    return nullptr;
+}
+
+struct Choice {
+    KernelFn fn;
+    int spp_log2;
+};
+
+// The page kernel serves 256-byte rows, G in {4, 8, 16}, and page sizes that
+// are a power-of-two multiple of its 64/G slots per step with 32-bit lane
+// offsets; every other shape takes the token kernel.
+Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
+            bool allow_page = true)
+{
+    Choice c{nullptr, 0};
+    const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
+    const bool row256 = (dtype == PD_DTYPE_FP16 && d == 128) || (dtype == PD_DTYPE_FP32 && d == 64);
+    if (allow_page && row256 && (g == 4 || g == 8 || g == 16)) {
+        const int sps = 64 / g;
+        if (page_size % sps == 0) {
+            const int spp = page_size / sps;
+            if ((spp & (spp - 1)) == 0 && token_stride * esz * page_size < (int64_t(1) << 31)) {
+                int lg = 0;
+                while ((1 << lg) < spp) ++lg;
+                c.spp_log2 = lg;
+                if (dtype == PD_DTYPE_FP16) c.fn = fused ? pick_page<_Float16, true>(g) : pick_page<_Float16, false>(g);
+                else c.fn = fused ? pick_page<float, true>(g) : pick_page<float, false>(g);
+                return c;
+            }
+        }
+    }
+    if (dtype == PD_DTYPE_FP16) {
+        if (d == 64) c.fn = fused ? pick_token<_Float16, 64, true>(g) : pick_token<_Float16, 64, false>(g);
+        if (d == 128) c.fn = fused ? pick_token<_Float16, 128, true>(g) : pick_token<_Float16, 128, false>(g);
+    } else if (dtype == PD_DTYPE_FP32) {
+        if (d == 64) c.fn = fused ? pick_token<float, 64, true>(g) : pick_token<float, 64, false>(g);
+        if (d == 128) c.fn = fused ? pick_token<float, 128, true>(g) : pick_token<float, 128, false>(g);
+    }
+    return c;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_and_fill(PartialArgs &a, const void *q, const void *k_pool, const void *v_pool,
+                   int64_t page_stride, int64_t token_stride, int64_t head_stride, int32_t dtype,
+                   const int32_t *indices, const int32_t *indptr, const int32_t *last_page_len,
+                   const int32_t *first_page_offset, const int32_t *request_indices,
+                   const int32_t *kv_tile_indices, int32_t num_chunks, int32_t pages_per_chunk,
+                   int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t page_size, float sm_scale, float *v_partial, float *lse_partial,
+                   const char *who)
+{
+    if (!q || !k_pool || !v_pool || !indices || !indptr || !last_page_len ||
+        !first_page_offset || !request_indices || !kv_tile_indices || !v_partial ||
+        !lse_partial)
+        return fail(PD_E_NULL, std::string(who) + ": null pointer");
+    if (num_chunks < 0 || batch < 1 || pages_per_chunk < 1 || page_size < 1 ||
+        num_kv_heads < 1 || num_qo_heads < 1 || num_qo_heads % num_kv_heads != 0 ||
+        page_stride < 0 || token_stride < 0 || head_stride < 0 || !std::isfinite(sm_scale))
+        return fail(PD_E_ARG, std::string(who) + ": bad sizes or strides");
+    if (int64_t(num_chunks) > PD_MAX_CHUNKS)
+        return fail(PD_E_ARG, std::string(who) + ": more chunks than the launch bound");
+    if (dtype != PD_DTYPE_FP16 && dtype != PD_DTYPE_FP32)
+        return fail(PD_E_UNSUPPORTED, std::string(who) + ": dtype");
+    const int64_t esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (page_stride * esz) % 16 || (token_stride * esz) % 16 || (head_stride * esz) % 16)
+        return fail(PD_E_UNSUPPORTED, std::string(who) + ": q/pools need 16-byte alignment");
+    if (!aligned16(v_partial))
+        return fail(PD_E_UNSUPPORTED, std::string(who) + ": v_partial needs 16-byte alignment");
+    a.q = q;
+    a.k = k_pool;
+    a.v = v_pool;
+    a.page_stride = page_stride;
+    a.token_stride = token_stride;
+    a.head_stride = head_stride;
+    a.indices = indices;
+    a.indptr = indptr;
+    a.lpl = last_page_len;
+    a.fpo = first_page_offset;
+    a.req_idx = request_indices;
+    a.tile_idx = kv_tile_indices;
+    a.num_kv_heads = num_kv_heads;
+    a.num_qo_heads = num_qo_heads;
+    a.page_size = page_size;
+    a.pages_per_chunk = pages_per_chunk;
+    a.spp_log2 = 0;
+    a.fd = make_fastdiv(uint32_t(page_size));
+    a.scale_log2 = float(double(sm_scale) * 1.4426950408889634074);   // log2(e)
+    a.v_out = v_partial;
+    a.lse_out = lse_partial;
+    a.o_final = nullptr;
+    a.lse_final = nullptr;
+    a.counters = nullptr;
+    return PD_OK;
+}
+
+int launch(const Choice &c, const PartialArgs &a, int32_t num_chunks, void *stream,
+           const char *who)
+{
+    PartialArgs b = a;
+    b.spp_log2 = c.spp_log2;
+    const dim3 grid(uint32_t(int64_t(num_chunks) * a.num_kv_heads));
+    hipLaunchKernelGGL(c.fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), b);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PD_E_HIP, std::string(who) + ": launch failed: " + hipGetErrorString(err));
+    return PD_OK;
+}
+
+int g_force_token_kernel = 0;   // testing hook: route every shape to the token kernel
 
 }  // namespace
 }  // namespace pd
@@ -354,77 +829,88 @@ extern "C" int paged_decode_partial(const void *q, const void *k_pool, const voi
                                     int32_t head_dim, int32_t page_size, float sm_scale,
                                     float *v_partial, float *lse_partial, void *stream)
 {
-    if (!q || !k_pool || !v_pool || !indices || !indptr || !last_page_len ||
-        !first_page_offset || !request_indices || !kv_tile_indices || !v_partial ||
-        !lse_partial)
-        return fail(PD_E_NULL, "paged_decode_partial: null pointer");
-    if (num_chunks < 0 || batch < 1 || pages_per_chunk < 1 || page_size < 1 ||
-        num_kv_heads < 1 || num_qo_heads < 1 || num_qo_heads % num_kv_heads != 0 ||
-        page_stride < 0 || token_stride < 0 || head_stride < 0 || !std::isfinite(sm_scale))
-        return fail(PD_E_ARG, "paged_decode_partial: bad sizes or strides");
-    if (int64_t(num_chunks) > PD_MAX_CHUNKS)
-        return fail(PD_E_ARG, "paged_decode_partial: more chunks than the launch bound");
-    const int g = num_qo_heads / num_kv_heads;
-    KernelFn fn = pick_kernel(dtype, head_dim, g);
-    if (!fn)
-        return fail(PD_E_UNSUPPORTED, "paged_decode_partial: no kernel for this (dtype, D, group)");
-    const int64_t esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        (page_stride * esz) % 16 || (token_stride * esz) % 16 || (head_stride * esz) % 16)
-        return fail(PD_E_UNSUPPORTED, "paged_decode_partial: q/pools need 16-byte alignment");
-    if (!aligned16(v_partial))
-        return fail(PD_E_UNSUPPORTED, "paged_decode_partial: v_partial needs 16-byte alignment");
-    if (num_chunks == 0) return PD_OK;
-
     PartialArgs a;
-    a.q = q;
-    a.k = k_pool;
-    a.v = v_pool;
-    a.page_stride = page_stride;
-    a.token_stride = token_stride;
-    a.head_stride = head_stride;
-    a.indices = indices;
-    a.indptr = indptr;
-    a.lpl = last_page_len;
-    a.fpo = first_page_offset;
-    a.req_idx = request_indices;
-    a.tile_idx = kv_tile_indices;
-    a.num_kv_heads = num_kv_heads;
-    a.num_qo_heads = num_qo_heads;
-    a.page_size = page_size;
-    a.pages_per_chunk = pages_per_chunk;
-    a.fd = make_fastdiv(uint32_t(page_size));
-    a.scale_log2 = float(double(sm_scale) * 1.4426950408889634074);   // log2(e)
-    a.v_out = v_partial;
-    a.lse_out = lse_partial;
+    const char *who = "paged_decode_partial";
+    int rc = check_and_fill(a, q, k_pool, v_pool, page_stride, token_stride, head_stride, dtype,
+                            indices, indptr, last_page_len, first_page_offset, request_indices,
+                            kv_tile_indices, num_chunks, pages_per_chunk, batch, num_qo_heads,
+                            num_kv_heads, head_dim, page_size, sm_scale, v_partial, lse_partial,
+                            who);
+    if (rc) return rc;
+    const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
+                          false, !g_force_token_kernel);
+    if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_partial: no kernel for this (dtype, D, group)");
+    if (num_chunks == 0) return PD_OK;
+    return launch(c, a, num_chunks, stream, who);
+}
 
-    const dim3 grid(uint32_t(int64_t(num_chunks) * num_kv_heads));
-    hipLaunchKernelGGL(fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
-        return fail(PD_E_HIP, std::string("paged_decode_partial: launch failed: ") +
-                                  hipGetErrorString(err));
+extern "C" int paged_decode_fused(const void *q, const void *k_pool, const void *v_pool,
+                                  int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                                  int32_t dtype, const int32_t *indices, const int32_t *indptr,
+                                  const int32_t *last_page_len, const int32_t *first_page_offset,
+                                  const int32_t *request_indices, const int32_t *kv_tile_indices,
+                                  int32_t num_chunks, int32_t pages_per_chunk, int32_t batch,
+                                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t page_size, float sm_scale, float *v_partial,
+                                  float *lse_partial, int32_t *counters, float *out,
+                                  float *lse_out, void *stream)
+{
+    PartialArgs a;
+    const char *who = "paged_decode_fused";
+    int rc = check_and_fill(a, q, k_pool, v_pool, page_stride, token_stride, head_stride, dtype,
+                            indices, indptr, last_page_len, first_page_offset, request_indices,
+                            kv_tile_indices, num_chunks, pages_per_chunk, batch, num_qo_heads,
+                            num_kv_heads, head_dim, page_size, sm_scale, v_partial, lse_partial,
+                            who);
+    if (rc) return rc;
+    if (!counters || !out || !lse_out) return fail(PD_E_NULL, "paged_decode_fused: null pointer");
+    if (num_chunks < batch)
+        return fail(PD_E_ARG, "paged_decode_fused: fewer chunks than requests");
+    const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
+                          true, !g_force_token_kernel);
+    if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_fused: no kernel for this (dtype, D, group)");
+    a.o_final = out;
+    a.lse_final = lse_out;
+    a.counters = counters;
+    return launch(c, a, num_chunks, stream, who);
+}
+
+extern "C" int paged_decode_set_kernel_choice(int32_t force_token_kernel)
+{
+    g_force_token_kernel = force_token_kernel != 0;
     return PD_OK;
+}
+
+extern "C" int paged_decode_kernel_kind(int32_t dtype, int32_t head_dim, int32_t group_size,
+                                        int32_t page_size, int64_t token_stride)
+{
+    const Choice c = pick(dtype, head_dim, group_size, page_size, token_stride, false,
+                          !g_force_token_kernel);
+    if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_kernel_kind: unsupported shape");
+    const Choice t = pick(dtype, head_dim, group_size, page_size, token_stride, false, false);
+    return c.fn == t.fn ? 0 : 1;   // 0 token kernel, 1 page kernel
 }
 
 extern "C" int paged_decode_default_target_wgs(int32_t device, int32_t group_size,
                                                int32_t head_dim, int32_t dtype)
 {
-    KernelFn fn = pick_kernel(dtype, head_dim, group_size);
-    if (!fn) return fail(PD_E_UNSUPPORTED, "paged_decode_default_target_wgs: unsupported shape");
+    const Choice c = pick(dtype, head_dim, group_size, 16, head_dim, false, !g_force_token_kernel);
+    if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_default_target_wgs: unsupported shape");
     int dev = device;
     if (dev < 0 && hipGetDevice(&dev) != hipSuccess)
         return fail(PD_E_HIP, "paged_decode_default_target_wgs: no current device");
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return fail(PD_E_HIP, "paged_decode_default_target_wgs: cannot query CU count");
-    int per_cu = 0;
     int prev = -1;
-    hipGetDevice(&prev);
-    hipSetDevice(dev);
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess)
+        return fail(PD_E_HIP, "paged_decode_default_target_wgs: cannot select device");
+    int per_cu = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void *>(fn), kThreads, 0);
-    if (prev >= 0) hipSetDevice(prev);
+        &per_cu, reinterpret_cast<const void *>(c.fn), kThreads, 0);
+    if (prev >= 0 && prev != dev && hipSetDevice(prev) != hipSuccess)
+        return fail(PD_E_HIP, "paged_decode_default_target_wgs: cannot restore device");
     if (e != hipSuccess || per_cu < 1)
         return fail(PD_E_HIP, "paged_decode_default_target_wgs: occupancy query failed");
     return cus * per_cu;

@@ -43,7 +43,7 @@ class PagedDecode:
 
     def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
                  num_kv_heads: int, head_dim: int, target_wgs: int = 0,
-                 fixed_pages_per_chunk: int = 0, device="cuda"):
+                 fixed_pages_per_chunk: int = 0, fused: bool = False, device="cuda"):
         indptr = np.asarray(csr["indptr"], np.int32)
         self.batch = indptr.size - 1
         self.page_size = page_size
@@ -66,13 +66,18 @@ class PagedDecode:
         self.v_partial = torch.empty((n, num_qo_heads, head_dim), dtype=torch.float32,
                                      device=self.device)
         self.lse_partial = torch.empty((n, num_qo_heads), dtype=torch.float32, device=self.device)
-        if info.needs_merge:
+        self.fused = fused
+        if info.needs_merge or fused:
             self.out = torch.empty((self.batch, num_qo_heads, head_dim), dtype=torch.float32,
                                    device=self.device)
             self.lse = torch.empty((self.batch, num_qo_heads), dtype=torch.float32,
                                    device=self.device)
         else:   # write-O-directly: the partial, in request order, is the answer
             self.out, self.lse = self.v_partial, self.lse_partial
+        # per-(request, KV head) arrival counters of the fused launch; every
+        # completed launch leaves them at zero
+        self.counters = (torch.zeros(self.batch * num_kv_heads, dtype=torch.int32,
+                                     device=self.device) if fused else None)
 
     def plan_summary(self) -> dict:
         i = self.info
@@ -94,6 +99,15 @@ class PagedDecode:
             B.paged_merge_states(self.v_partial, self.lse_partial, self.d_oindptr, self.batch,
                                  self.num_qo_heads, self.head_dim, self.out, self.lse, stream)
 
+    def fused_step(self, q, k_pool, v_pool, sm_scale, stream=None):
+        ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
+        B.paged_decode_fused(q, k_pool, v_pool, ps_, ts_, hs_, _pd_dtype(q), self.d_indices,
+                             self.d_indptr, self.d_lpl, self.d_fpo, self.d_req, self.d_tile,
+                             self.info.num_chunks, self.info.pages_per_chunk, self.batch,
+                             self.num_qo_heads, self.num_kv_heads, self.head_dim,
+                             self.page_size, sm_scale, self.v_partial, self.lse_partial,
+                             self.counters, self.out, self.lse, stream)
+
     def run(self, q, k_pool, v_pool, sm_scale, stream=None):
         """One decode step: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32,
         log2 units); the tensors are this object's buffers."""
@@ -101,8 +115,11 @@ class PagedDecode:
             raise ValueError("q must be a contiguous [B, Hq, D] tensor")
         if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
             raise TypeError("q and pools must share a dtype")
-        self.partial(q, k_pool, v_pool, sm_scale, stream)
-        self.merge(stream)
+        if self.fused:
+            self.fused_step(q, k_pool, v_pool, sm_scale, stream)
+        else:
+            self.partial(q, k_pool, v_pool, sm_scale, stream)
+            self.merge(stream)
         return self.out, self.lse
 
 

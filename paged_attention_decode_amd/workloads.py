@@ -83,6 +83,22 @@ def _pool(rng, num_pages, page_size, hkv, d, dtype, poison_unused, used_pages):
     return k, v
 
 
+def poison_invisible(w: "Workload") -> "Workload":
+    """Set every pool entry that is not a visible token of some request to
+    NaN: unused pages, entries before a window's first token in its first
+    page, entries past the last written token in a last page.  A decode that
+    reads any of them (outside the masked slots) produces NaN."""
+    ps = w.page_size
+    visible = np.zeros(w.k_pool.shape[:2], dtype=bool)
+    for t, s, e in zip(w.block_tables, w.logical_start, w.written_len):
+        pos = np.arange(int(s), int(e))
+        if pos.size:
+            visible[t[pos // ps], pos % ps] = True
+    w.k_pool[~visible] = np.nan
+    w.v_pool[~visible] = np.nan
+    return w
+
+
 def _tables_from_lengths(rng, lengths_start_end, page_size, pool_pages):
     """Draw distinct physical pages for every logical block a request still
     holds (blocks wholly before the logical start are released = -1)."""
@@ -129,12 +145,13 @@ def generic(name, *, seed, dtype, page_size, num_qo_heads, num_kv_heads, head_di
     q = _normal(rng, (len(ls), num_qo_heads, head_dim), dtype)
     k, v = _pool(rng, pool_pages, page_size, num_kv_heads, head_dim, dtype,
                  poison_unused, used)
-    return Workload(name=name, dtype=dtype, page_size=page_size,
-                    num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
-                    head_dim=head_dim,
-                    sm_scale=float(sm_scale if sm_scale is not None else 1.0 / np.sqrt(head_dim)),
-                    q=q, k_pool=k, v_pool=v, block_tables=tables,
-                    logical_start=ls, written_len=wl, target_wgs=target_wgs)
+    w = Workload(name=name, dtype=dtype, page_size=page_size,
+                 num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+                 head_dim=head_dim,
+                 sm_scale=float(sm_scale if sm_scale is not None else 1.0 / np.sqrt(head_dim)),
+                 q=q, k_pool=k, v_pool=v, block_tables=tables,
+                 logical_start=ls, written_len=wl, target_wgs=target_wgs)
+    return poison_invisible(w) if poison_unused else w
 
 
 def tiny_fp32(seed=1, poison_unused=False):
@@ -147,11 +164,12 @@ def tiny_fp32(seed=1, poison_unused=False):
     table = perm[:32].copy()
     q = _normal(rng, (1, hq, d), FP32)
     k, v = _pool(rng, 64, ps, hkv, d, FP32, poison_unused, table)
-    return Workload(name="tiny_fp32", dtype=FP32, page_size=ps, num_qo_heads=hq,
-                    num_kv_heads=hkv, head_dim=d, sm_scale=1.0 / np.sqrt(d),
-                    q=q, k_pool=k, v_pool=v, block_tables=[table],
-                    logical_start=np.zeros(1, np.int32),
-                    written_len=np.array([n], np.int32), target_wgs=8)
+    w = Workload(name="tiny_fp32", dtype=FP32, page_size=ps, num_qo_heads=hq,
+                 num_kv_heads=hkv, head_dim=d, sm_scale=1.0 / np.sqrt(d),
+                 q=q, k_pool=k, v_pool=v, block_tables=[table],
+                 logical_start=np.zeros(1, np.int32),
+                 written_len=np.array([n], np.int32), target_wgs=8)
+    return poison_invisible(w) if poison_unused else w
 
 
 def batched_fp16(seed=2, poison_unused=False):
@@ -166,10 +184,11 @@ def batched_fp16(seed=2, poison_unused=False):
     tables, used = _tables_from_lengths(rng, [(0, int(x)) for x in lens], ps, 2048)
     q = _normal(rng, (b, hq, d), FP16)
     k, v = _pool(rng, 2048, ps, hkv, d, FP16, poison_unused, used)
-    return Workload(name="batched_fp16", dtype=FP16, page_size=ps, num_qo_heads=hq,
-                    num_kv_heads=hkv, head_dim=d, sm_scale=1.0 / np.sqrt(d),
-                    q=q, k_pool=k, v_pool=v, block_tables=tables,
-                    logical_start=np.zeros(b, np.int32), written_len=lens)
+    w = Workload(name="batched_fp16", dtype=FP16, page_size=ps, num_qo_heads=hq,
+                 num_kv_heads=hkv, head_dim=d, sm_scale=1.0 / np.sqrt(d),
+                 q=q, k_pool=k, v_pool=v, block_tables=tables,
+                 logical_start=np.zeros(b, np.int32), written_len=lens)
+    return poison_invisible(w) if poison_unused else w
 
 
 def long_context_fp16(seed=3, poison_unused=False):
@@ -189,10 +208,11 @@ def long_context_fp16(seed=3, poison_unused=False):
                                         pool_pages)
     q = _normal(rng, (4, hq, d), FP16)
     k, v = _pool(rng, pool_pages, ps, hkv, d, FP16, poison_unused, used)
-    return Workload(name="long_context_fp16", dtype=FP16, page_size=ps,
-                    num_qo_heads=hq, num_kv_heads=hkv, head_dim=d,
-                    sm_scale=1.0 / np.sqrt(d), q=q, k_pool=k, v_pool=v,
-                    block_tables=tables, logical_start=ls, written_len=wl)
+    w = Workload(name="long_context_fp16", dtype=FP16, page_size=ps,
+                 num_qo_heads=hq, num_kv_heads=hkv, head_dim=d,
+                 sm_scale=1.0 / np.sqrt(d), q=q, k_pool=k, v_pool=v,
+                 block_tables=tables, logical_start=ls, written_len=wl)
+    return poison_invisible(w) if poison_unused else w
 
 
 @dataclasses.dataclass
@@ -243,11 +263,12 @@ def cascade_fp16(seed=5, members=4, prefix_tokens=8192, suffix_lo=256, suffix_hi
     q = _normal(rng, (members, hq, d), FP16)
     k, v = _pool(rng, pool_pages, ps, hkv, d, FP16, poison_unused, used)
     wl = (prefix_tokens + suffix).astype(np.int32)
-    return Workload(name="cascade_fp16", dtype=FP16, page_size=ps, num_qo_heads=hq,
-                    num_kv_heads=hkv, head_dim=d, sm_scale=1.0 / np.sqrt(d),
-                    q=q, k_pool=k, v_pool=v, block_tables=tables,
-                    logical_start=np.zeros(members, np.int32), written_len=wl,
-                    extra={"shared_pages": pre_pages, "suffix_tokens": suffix})
+    w = Workload(name="cascade_fp16", dtype=FP16, page_size=ps, num_qo_heads=hq,
+                 num_kv_heads=hkv, head_dim=d, sm_scale=1.0 / np.sqrt(d),
+                 q=q, k_pool=k, v_pool=v, block_tables=tables,
+                 logical_start=np.zeros(members, np.int32), written_len=wl,
+                 extra={"shared_pages": pre_pages, "suffix_tokens": suffix})
+    return poison_invisible(w) if poison_unused else w
 
 
 def random_geometry(seed, *, batch, page_size, max_len, dtype=FP16, num_qo_heads=8,

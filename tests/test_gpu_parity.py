@@ -61,11 +61,35 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None):
+_WORKLOADS = {}
+
+
+def cached(name, **kw):
+    """Large workloads are generated once per session (tests only read them)."""
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _WORKLOADS:
+        _WORKLOADS[key] = getattr(workloads, name)(**kw)
+    return _WORKLOADS[key]
+
+
+MODES = [("auto", False), ("auto", True), ("token", False), ("token", True)]
+MODE_IDS = ["page-2launch", "page-fused", "token-2launch", "token-fused"]
+
+
+@pytest.fixture(params=MODES, ids=MODE_IDS)
+def mode(request):
+    kernel, fused = request.param
+    B.paged_decode_set_kernel_choice(kernel == "token")
+    yield dict(fused=fused, kernel=kernel)
+    B.paged_decode_set_kernel_choice(False)
+
+
+def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None, fused=False,
+             repeat=1):
     """HIP flat decode of workload w vs the oracle; returns the decoder."""
-    say("case %s dtype=%s B=%d Hq=%d Hkv=%d D=%d ps=%d target=%d fixed=%d" % (
+    say("case %s dtype=%s B=%d Hq=%d Hkv=%d D=%d ps=%d target=%d fixed=%d fused=%s" % (
         w.name, w.dtype, w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
-        target, fixed))
+        target, fixed, fused))
     pool_pages = w.k_pool.shape[0]
     csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
                             pool_pages)
@@ -75,9 +99,14 @@ def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None):
         assert np.array_equal(csr[k], ocsr[k]), k
     dec = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
                          num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
-                         head_dim=w.head_dim, target_wgs=target, fixed_pages_per_chunk=fixed)
+                         head_dim=w.head_dim, target_wgs=target, fixed_pages_per_chunk=fixed,
+                         fused=fused)
     info = dec.info
-    say("  plan", dec.plan_summary())
+    kind = B.paged_decode_kernel_kind(B.PD_DTYPE_FP16 if w.dtype == workloads.FP16 else
+                                      B.PD_DTYPE_FP32, w.head_dim,
+                                      w.num_qo_heads // w.num_kv_heads, w.page_size,
+                                      w.k_pool.shape[2] * w.head_dim)
+    say("  plan", dec.plan_summary(), "kernel", "page" if kind else "token")
     oplan = orc.plan(ocsr["indptr"], w.num_kv_heads, info.target_wgs,
                      fixed_pages_per_chunk=fixed)
     assert oplan["pages_per_chunk"] == info.pages_per_chunk
@@ -85,17 +114,21 @@ def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None):
     assert np.array_equal(oplan["kv_tile_indices"], dec.kv_tile_indices)
     assert np.array_equal(oplan["o_indptr"], dec.o_indptr)
     q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
-    if stream is not None:
-        with torch.cuda.stream(stream):
-            out, lse = dec.run(q, k, v, w.sm_scale)
-        stream.synchronize()
-    else:
-        out, lse = dec.run(q, k, v, w.sm_scale)
-    torch.cuda.synchronize()
     ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
                                  nthreads=NTHREADS)
-    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "final")
-    if check_partials:
+    for it in range(repeat):
+        if stream is not None:
+            with torch.cuda.stream(stream):
+                out, lse = dec.run(q, k, v, w.sm_scale)
+            stream.synchronize()
+        else:
+            out, lse = dec.run(q, k, v, w.sm_scale)
+        torch.cuda.synchronize()
+        check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype,
+                    "final (call %d)" % it)
+        if fused:
+            assert int(dec.counters.abs().sum()) == 0, "fused launch left a counter non-zero"
+    if check_partials and not fused:
         pv, pl = orc.partial(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
                              oplan["request_indices"], oplan["kv_tile_indices"],
                              oplan["pages_per_chunk"], nthreads=NTHREADS)
@@ -113,31 +146,36 @@ def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None):
 
 # ---------------------------------------------------------------- configs
 
-def test_tiny_fp32_single_merge_of_four(orc):
+def test_tiny_fp32_single_merge_of_four(orc, mode):
     w = workloads.tiny_fp32()
-    dec = run_flat(orc, w, target=8)
+    dec = run_flat(orc, w, target=8, fused=mode["fused"])
     assert dec.info.pages_per_chunk == 10 and dec.info.num_chunks == 4
     assert list(dec.o_indptr) == [0, 4] and dec.info.needs_merge
-    dec = run_flat(orc, w, target=8, fixed=8)
+    dec = run_flat(orc, w, target=8, fixed=8, fused=mode["fused"])
     assert dec.info.num_chunks == 4
 
 
-def test_tiny_fp32_poisoned_pool(orc):
-    run_flat(orc, workloads.tiny_fp32(poison_unused=True), target=8)
+def test_tiny_fp32_poisoned_pool(orc, mode):
+    run_flat(orc, workloads.tiny_fp32(poison_unused=True), target=8, fused=mode["fused"],
+             repeat=2)
 
 
 @pytest.mark.parametrize("target", [0, 64, 1024])
-def test_batched_fp16(orc, target):
-    w = workloads.batched_fp16(poison_unused=True)
+def test_batched_fp16(orc, target, mode):
+    w = cached("batched_fp16", poison_unused=True)
     assert w.written_len[0] % w.page_size == 0          # an exactly-full last page
-    run_flat(orc, w, target=target)
+    run_flat(orc, w, target=target, fused=mode["fused"], repeat=2)
 
 
-@pytest.mark.parametrize("target", [0, 1024])
-def test_long_context_fp16_full_size(orc, target):
-    w = workloads.long_context_fp16(poison_unused=True)
-    dec = run_flat(orc, w, target=target)
-    assert dec.info.needs_merge
+@pytest.mark.parametrize("target", [0, 1024, 1])
+def test_long_context_fp16_full_size(orc, target, mode):
+    """Full size; target 1 gives 2048-page chunks (several LDS page-id rounds)."""
+    w = cached("long_context_fp16", poison_unused=True)
+    dec = run_flat(orc, w, target=target, fused=mode["fused"], repeat=2)
+    if target == 1:       # one 2048-page chunk per request: written directly
+        assert dec.info.pages_per_chunk == 2048 and not dec.info.needs_merge
+    else:
+        assert dec.info.needs_merge
 
 
 def test_token_sparse_page_size_one(orc):
@@ -224,18 +262,41 @@ def test_cascade_member_major_stacking_is_wrong(orc):
 # ------------------------------------------------------- invariance / edges
 
 @pytest.mark.parametrize("fixed", [1, 2, 4, 8, 0])
-def test_chunk_size_invariance(orc, fixed):
+def test_chunk_size_invariance(orc, fixed, mode):
     w = workloads.random_geometry(40, batch=5, page_size=16, max_len=3000, num_qo_heads=16,
                                   num_kv_heads=4)
-    run_flat(orc, w, target=256, fixed=fixed)
+    run_flat(orc, w, target=256, fixed=fixed, fused=mode["fused"])
 
 
-@pytest.mark.parametrize("seed,ps", [(50, 1), (51, 3), (52, 16), (53, 64), (54, 7)])
-def test_ragged_force_merge(orc, seed, ps):
+@pytest.mark.parametrize("seed,ps", [(50, 1), (51, 3), (52, 16), (53, 64), (54, 7), (55, 32),
+                                     (56, 4)])
+def test_ragged_force_merge(orc, seed, ps, mode):
     """pages_per_chunk = 1: every request through the merge, maximally ragged."""
     w = workloads.random_geometry(seed, batch=7, page_size=ps, max_len=700, num_qo_heads=8,
                                   num_kv_heads=2, p_empty=0.2, p_trim=0.5)
-    run_flat(orc, w, fixed=1)
+    run_flat(orc, w, fixed=1, fused=mode["fused"], repeat=2)
+
+
+@pytest.mark.parametrize("g", [4, 8, 16])
+@pytest.mark.parametrize("ps", [4, 16, 64])
+def test_page_kernel_shapes_ragged(orc, g, ps, mode):
+    """Ragged windows over the page kernel's group sizes and page sizes."""
+    w = workloads.random_geometry(100 + g + ps, batch=5, page_size=ps, max_len=1500,
+                                  num_qo_heads=2 * g, num_kv_heads=2, p_empty=0.15,
+                                  p_trim=0.5)
+    run_flat(orc, w, target=48, fused=mode["fused"])
+
+
+def test_kernel_choice():
+    kk = B.paged_decode_kernel_kind
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1024) == 1
+    assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 1
+    assert kk(B.PD_DTYPE_FP16, 128, 16, 16, 1024) == 1
+    assert kk(B.PD_DTYPE_FP32, 64, 4, 16, 128) == 1
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 8, 1024) == 0     # page smaller than a step
+    assert kk(B.PD_DTYPE_FP16, 128, 12, 1, 128) == 0     # token-sparse page_size 1
+    assert kk(B.PD_DTYPE_FP16, 64, 4, 16, 512) == 0      # 128-byte rows
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 48, 1024) == 0    # 3 steps per page
 
 
 def test_empty_requests_do_not_poison_neighbours(orc):
