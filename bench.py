@@ -8,11 +8,13 @@ K/V pools, page table, plan arrays, workspace) are resident in HBM before
 timing; the plan is built outside the timed region, as the pages' microbench
 does (PR #984, commit adding the three-way microbench).
 
-Before each timed step the L2 and the 256 MB last-level cache are flushed by
-reading a 1 GiB buffer, so every step streams its KV bytes from HBM; the step
-time is taken with HIP events on the launch stream around partial + merge
-(flush excluded).  `value` = algorithmic KV bytes / mean step time.  A warm
-(unflushed) figure is reported beside it.
+The timed region is K back-to-back decode steps, bracketed by device
+synchronization and HIP events on the launch stream.  Consecutive steps read
+different copies of the K/V pools (3 by default, each larger than the 256 MB
+last-level cache), so every step streams its KV bytes from HBM.  `value` =
+algorithmic KV bytes / (region time / K).  The partial kernel alone is timed
+the same way for the roofline entry, and an isolated step after a 1 GiB
+cache flush, bracketed by its own event pair, is reported for reference.
 
 The GPU result is checked against the f64 oracle on the same inputs before
 anything is reported (`parity`); the oracle's own time on the host cores is
@@ -73,6 +75,8 @@ def parse():
     p.add_argument("--mode", default="two-launch", choices=["fused", "two-launch"],
                    help="fused: one launch, the last chunk of each request merges; "
                         "two-launch: partial kernel then merge kernel")
+    p.add_argument("--pool-copies", type=int, default=3,
+                   help="independent K/V pool copies used in turn by consecutive steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="approximate CPU work budget of the oracle baseline")
@@ -119,20 +123,28 @@ def main():
                                 num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                                 head_dim=w.head_dim, target_wgs=args.target_wgs,
                                 fixed_pages_per_chunk=args.fixed_pages_per_chunk,
-                                fused=args.mode == "fused", device=dev)
+                                fused=args.mode == "fused",
+                                dtype=torch.float32 if w.dtype == "fp32" else torch.float16,
+                                device=dev)
         plan = runner.plan_summary()
         plan["mode"] = args.mode
         partial_only = runner
         kv_bytes = w.kv_bytes()
     q = torch.from_numpy(w.q).to(dev)
-    k = torch.from_numpy(w.k_pool).to(dev)
-    v = torch.from_numpy(w.v_pool).to(dev)
+    # independent copies of the K/V pools, used in turn by consecutive steps,
+    # so that no step finds the previous step's KV in the 256 MB last-level
+    # cache (each copy is larger than that cache)
+    kv = [(torch.from_numpy(w.k_pool).to(dev), torch.from_numpy(w.v_pool).to(dev))]
+    for _ in range(args.pool_copies - 1):
+        kv.append((kv[0][0].clone(), kv[0][1].clone()))
+    k, v = kv[0]
     flush = torch.empty(1 << 29, dtype=torch.float16, device=dev).normal_()   # 1 GiB
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    def step():
-        return runner.run(q, k, v, w.sm_scale)
+    def step(i=0):
+        kk, vv = kv[i % len(kv)]
+        return runner.run(q, kk, vv, w.sm_scale)
 
     # parity gate before timing (the pages' bench refuses to time arms that disagree)
     out, lse = step()
@@ -158,40 +170,49 @@ def main():
         sys.exit(1)
 
     stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
 
-    def timed(n, do_flush):
-        tot, part = [], []
-        for _ in range(n):
-            if do_flush:
-                flush.max()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e2 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            if partial_only is not None and not partial_only.fused:
-                partial_only.partial(q, k, v, w.sm_scale)
-                e1.record(stream)
-                partial_only.merge()
-            else:
-                step()
-                e1.record(stream)
-            e2.record(stream)
-            tot.append((e0, e2))
-            part.append((e0, e1))
+    def run_steps(n, fn):
+        """n back-to-back calls of fn(i), timed as one region (events on the
+        launch stream and the wall clock, synchronized on both sides)."""
         torch.cuda.synchronize()
-        return ([a.elapsed_time(b) * 1e-3 for a, b in tot],
-                [a.elapsed_time(b) * 1e-3 for a, b in part])
+        e0, e1 = ev(), ev()
+        w0 = time.time()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n, (time.time() - w0) / n
 
-    timed(args.warmup, True)
-    torch.cuda.synchronize()
-    wall0 = time.time()
-    step_s, part_s = timed(args.steps, True)
-    torch.cuda.synchronize()
-    wall_s = time.time() - wall0
-    warm_step_s, warm_part_s = timed(args.steps, False)
+    # warmup, then the timed steps (the metric)
+    run_steps(args.warmup, step)
+    step_s, wall_step_s = run_steps(args.steps, step)
 
-    mean_step = float(np.mean(step_s))
-    value = kv_bytes / mean_step / 1e9
+    # the dominant kernel alone, back to back over the same pool copies
+    part_s = None
+    if partial_only is not None:
+        if partial_only.fused:
+            part_s = step_s
+        else:
+            kk = lambda i: kv[i % len(kv)]   # noqa: E731
+            run_steps(args.warmup, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
+            part_s, _ = run_steps(args.steps, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
+
+    # reference: one isolated step after a cache flush, bracketed by its own
+    # events (includes the fixed cost of an event pair around a launch)
+    iso = []
+    for i in range(args.steps):
+        flush.max()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        iso.append((e0, e1))
+    torch.cuda.synchronize()
+    iso_s = np.array([a.elapsed_time(b) * 1e-3 for a, b in iso])
+
+    value = kv_bytes / step_s / 1e9
     total_tokens = int(w.visible_tokens.sum())
     res = {
         "metric": METRIC,
@@ -200,7 +221,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(mean_step * 1e3, 5),
+        "ms_per_step": round(step_s * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -211,27 +232,29 @@ def main():
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
             "visible_tokens": [int(x) for x in w.visible_tokens],
             "kv_bytes_per_step": int(kv_bytes), "accumulate": "fp32",
-            "cache": "L2 + LLC flushed (1 GiB read) before every timed step",
+            "timing": "%d back-to-back decode steps (partial + merge), step i reads K/V pool "
+                      "copy i mod %d (%d x %.0f MB); events on the launch stream"
+                      % (args.steps, len(kv), len(kv),
+                         2 * w.k_pool.nbytes / 1e6),
             "plan": plan,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "kv_tokens_per_s": round(total_tokens / mean_step, 1),
-        "step_us": {"mean": round(mean_step * 1e6, 2),
-                    "p10": round(float(np.percentile(step_s, 10)) * 1e6, 2),
-                    "p50": round(float(np.median(step_s)) * 1e6, 2),
-                    "p90": round(float(np.percentile(step_s, 90)) * 1e6, 2)},
-        "warm": {"step_us_mean": round(float(np.mean(warm_step_s)) * 1e6, 2),
-                 "kv_gbs": round(kv_bytes / float(np.mean(warm_step_s)) / 1e9, 2)},
-        "wall_s_timed_region_incl_flush": round(wall_s, 4),
+        "kv_tokens_per_s": round(total_tokens / step_s, 1),
+        "step_us": round(step_s * 1e6, 2),
+        "wall_step_us": round(wall_step_s * 1e6, 2),
+        "isolated_flushed_step_us": {"mean": round(float(iso_s.mean()) * 1e6, 2),
+                                     "p10": round(float(np.percentile(iso_s, 10)) * 1e6, 2),
+                                     "p50": round(float(np.median(iso_s)) * 1e6, 2),
+                                     "p90": round(float(np.percentile(iso_s, 90)) * 1e6, 2),
+                                     "kv_gbs": round(kv_bytes / float(iso_s.mean()) / 1e9, 2)},
         "setup_s": round(setup_s, 1),
         "parity": {"max_abs_v": dv, "max_abs_lse2": dl, "tol_v": tv, "tol_lse2": tl,
                    "ok": bool(parity_ok)},
     }
-    if partial_only is not None:
-        mean_part = float(np.mean(part_s))
-        achieved = kv_bytes / mean_part / 1e9
-        res["partial_us_mean"] = round(mean_part * 1e6, 2)
-        res["merge_and_gap_us_mean"] = round((mean_step - mean_part) * 1e6, 2)
+    if part_s is not None:
+        achieved = kv_bytes / part_s / 1e9
+        res["partial_us"] = round(part_s * 1e6, 2)
+        res["merge_and_gap_us"] = round((step_s - part_s) * 1e6, 2)
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),

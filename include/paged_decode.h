@@ -114,8 +114,13 @@ int paged_csr_build(int32_t batch, int32_t page_size, int32_t num_pool_pages,
  * plan takes the largest c in that range whose workgroup count reaches
  * target_wgs (binary search: chunks(c) is non-increasing), or c_min when
  * none does.  fixed_pages_per_chunk > 0 pins c instead (e.g. 1 to force every
- * request through the merge).  target_wgs <= 0 uses
- * paged_decode_default_target_wgs() of the current device.
+ * request through the merge).  The count is in (chunk, KV head) units, the
+ * pages' CTAs: a workgroup of the token kernel is one unit, a wave of the
+ * page kernel is one unit.  target_wgs <= 0 fits the device: with S =
+ * paged_decode_default_target_wgs() units resident at once on the current
+ * device, the target is the largest t <= S whose plan has at most S units
+ * (reported in info->target_wgs); `dtype` (PD_DTYPE_*) selects the kernel
+ * whose occupancy defines S and is otherwise unused.
  *
  * Outputs (HOST): request_indices[n] / kv_tile_indices[n] for n < N, in
  * request order (chunk t of request r covers its pages [t*c, (t+1)*c));
@@ -129,7 +134,7 @@ int paged_csr_build(int32_t batch, int32_t page_size, int32_t num_pool_pages,
 typedef struct {
     int32_t pages_per_chunk;
     int32_t num_chunks;
-    int32_t num_wgs;          /* num_chunks * num_kv_heads * q_groups */
+    int32_t num_wgs;          /* (chunk, KV head) units: num_chunks * num_kv_heads * q_groups */
     int32_t q_groups;         /* 1: a workgroup owns every query head of its KV head */
     int32_t needs_merge;
     int32_t target_wgs;       /* the target actually used */
@@ -138,7 +143,7 @@ typedef struct {
 
 int paged_decode_plan(int32_t batch, const int32_t *indptr,
                       int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t target_wgs, int32_t fixed_pages_per_chunk,
+                      int32_t dtype, int32_t target_wgs, int32_t fixed_pages_per_chunk,
                       int32_t capacity, int32_t *request_indices,
                       int32_t *kv_tile_indices, int32_t *o_indptr,
                       paged_decode_plan_info *info);
@@ -265,11 +270,12 @@ int paged_cascade_gather_states(const float *v0, const float *lse0, int32_t n0,
  * G: one workgroup per KV head), or a negative code if unsupported. */
 int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dtype);
 
-/* Device target for the plan: compute units x resident partial-kernel
- * workgroups per CU (HIP occupancy query) for the given shape on `device`.
+/* (chunk, KV head) units the device holds resident at once for this shape:
+ * compute units x resident partial-kernel workgroups per CU (HIP occupancy
+ * query) x units per workgroup, on `device` (-1: the current device).
  * Returns the count, or a negative code. */
 int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t head_dim,
-                                    int32_t dtype);
+                                    int32_t dtype, int32_t num_kv_heads);
 
 /* Which partial kernel serves a shape: 1 = page kernel (256-byte K/V rows,
  * group 4, 8 or 16, page_size a power-of-two multiple of 64/group slots),

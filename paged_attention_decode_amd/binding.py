@@ -15,7 +15,7 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpaged_decode.so")
+LIB_PATH = os.environ.get("PAGED_DECODE_LIB", os.path.join(HERE, "libpaged_decode.so"))
 
 PD_DTYPE_FP16 = 0
 PD_DTYPE_FP32 = 1
@@ -61,8 +61,8 @@ _SIGS = {
     "csr_validate": (i32, [i32, i32, i32, i32p, i32p, i32p, i32p, i32p, i32p]),
     "paged_csr_build": (i32, [i32, i32, i32, i32p, i32p, i32p, i32p, i32, i32p, i32p, i32p,
                               i32p, i32p, i32p]),
-    "paged_decode_plan": (i32, [i32, i32p, i32, i32, i32, i32, i32, i32, i32p, i32p, i32p,
-                                ctypes.POINTER(PlanInfo)]),
+    "paged_decode_plan": (i32, [i32, i32p, i32, i32, i32, i32, i32, i32, i32, i32p, i32p,
+                                i32p, ctypes.POINTER(PlanInfo)]),
     "paged_decode_partial": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
                                    i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]),
     "paged_decode_fused": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
@@ -75,7 +75,7 @@ _SIGS = {
     "paged_cascade_gather_states": (i32, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, vp,
                                           vp, vp]),
     "paged_decode_q_heads_per_wg": (i32, [i32, i32, i32]),
-    "paged_decode_default_target_wgs": (i32, [i32, i32, i32, i32]),
+    "paged_decode_default_target_wgs": (i32, [i32, i32, i32, i32, i32]),
     "paged_fastdiv_eval": (i32, [i32, u32p, i64, u32p, u32p]),
 }
 
@@ -176,24 +176,24 @@ def paged_csr_build(block_tables, logical_start, written_len, page_size, num_poo
 
 
 def paged_decode_plan(indptr, num_qo_heads, num_kv_heads, head_dim, target_wgs=0,
-                      fixed_pages_per_chunk=0, sizes_only=False):
+                      fixed_pages_per_chunk=0, sizes_only=False, dtype=PD_DTYPE_FP16):
     """Returns (info: PlanInfo, request_indices, kv_tile_indices, o_indptr)."""
     lib = load()
     ip = _host_i32(indptr)
     b = ip.size - 1
     info = PlanInfo()
     oi = np.zeros(b + 1, np.int32)
-    _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, target_wgs,
-                                 fixed_pages_per_chunk, 0, None, None, _hp(oi),
+    _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, dtype,
+                                 target_wgs, fixed_pages_per_chunk, 0, None, None, _hp(oi),
                                  ctypes.byref(info)))
     if sizes_only:
         return info, None, None, oi
     cap = max(1, info.num_chunks)
     ri = np.zeros(cap, np.int32)
     ti = np.zeros(cap, np.int32)
-    _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, target_wgs,
-                                 fixed_pages_per_chunk, cap, _hp(ri), _hp(ti), _hp(oi),
-                                 ctypes.byref(info)))
+    _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, dtype,
+                                 target_wgs, fixed_pages_per_chunk, cap, _hp(ri), _hp(ti),
+                                 _hp(oi), ctypes.byref(info)))
     return info, ri[:info.num_chunks], ti[:info.num_chunks], oi
 
 
@@ -260,9 +260,9 @@ def paged_decode_q_heads_per_wg(group_size, head_dim, dtype):
     return _check_nonneg(load().paged_decode_q_heads_per_wg(group_size, head_dim, dtype))
 
 
-def paged_decode_default_target_wgs(device, group_size, head_dim, dtype):
+def paged_decode_default_target_wgs(device, group_size, head_dim, dtype, num_kv_heads=1):
     return _check_nonneg(load().paged_decode_default_target_wgs(device, group_size, head_dim,
-                                                                dtype))
+                                                                dtype, num_kv_heads))
 
 
 def _check_nonneg(v):

@@ -37,28 +37,30 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, build_dir: str, extra_flags) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [hipcc()] + COMMON + DEVICE + ["-c", path, "-o", obj]
+        cmd = [hipcc()] + COMMON + list(extra_flags) + DEVICE + ["-c", path, "-o", obj]
     else:
-        cmd = [hipcc()] + COMMON + ["-x", "c++", "-c", path, "-o", obj]
+        cmd = [hipcc()] + COMMON + list(extra_flags) + ["-x", "c++", "-c", path, "-o", obj]
     subprocess.check_call(cmd)
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = OUT, extra_flags=(), build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link the shared library at `out`
+    (`extra_flags` are added to each compile, e.g. -D tuning knobs)."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra_flags), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp]
                           + objs)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 def dump_isa(src: str = "pd_partial.hip", out_dir: str = BUILD_DIR) -> str:

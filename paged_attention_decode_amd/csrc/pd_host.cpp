@@ -175,6 +175,53 @@ int64_t chunks_at(int32_t batch, const int32_t *indptr, int64_t c)
     return total;
 }
 
+// the plan rule: largest c in [c_min, c_max] with chunks(c) * wg_per_chunk >=
+// target, else c_min
+int64_t plan_c(int32_t batch, const int32_t *indptr, int64_t wg_per_chunk, int64_t target,
+               int64_t cmin, int64_t cmax)
+{
+    if (chunks_at(batch, indptr, cmin) * wg_per_chunk < target) return cmin;
+    int64_t lo = cmin, hi = cmax;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (chunks_at(batch, indptr, mid) * wg_per_chunk >= target) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+int64_t cmin_of(int32_t batch, const int32_t *indptr, int64_t cmax)
+{
+    int64_t lo = 1, hi = cmax;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (chunks_at(batch, indptr, mid) <= PD_MAX_CHUNKS) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
+// Largest target t <= slots whose plan uses at most `slots` units (units(t)
+// is non-decreasing in t); `slots` itself when even t = 1 overflows.
+int64_t fit_target(int32_t batch, const int32_t *indptr, int64_t wg_per_chunk, int64_t slots)
+{
+    int64_t cmax = 1;
+    for (int32_t r = 0; r < batch; ++r) cmax = std::max<int64_t>(cmax, int64_t(indptr[r + 1]) - indptr[r]);
+    const int64_t cmin = cmin_of(batch, indptr, cmax);
+    auto units = [&](int64_t t) {
+        return chunks_at(batch, indptr, plan_c(batch, indptr, wg_per_chunk, t, cmin, cmax)) *
+               wg_per_chunk;
+    };
+    if (units(1) > slots) return slots;
+    int64_t lo = 1, hi = slots;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (units(mid) <= slots) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 }  // namespace
 
 extern "C" int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dtype)
@@ -192,7 +239,7 @@ extern "C" int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim,
 
 extern "C" int paged_decode_plan(int32_t batch, const int32_t *indptr,
                                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t target_wgs, int32_t fixed_pages_per_chunk,
+                                 int32_t dtype, int32_t target_wgs, int32_t fixed_pages_per_chunk,
                                  int32_t capacity, int32_t *request_indices,
                                  int32_t *kv_tile_indices, int32_t *o_indptr,
                                  paged_decode_plan_info *info)
@@ -218,14 +265,17 @@ extern "C" int paged_decode_plan(int32_t batch, const int32_t *indptr,
                     fmt("paged_decode_plan: %lld requests exceed the %lld-chunk launch bound",
                         batch, PD_MAX_CHUNKS));
     int64_t target = target_wgs;
-    if (target <= 0) {
-        int dev = 0;
-        const int g = paged_decode_default_target_wgs(-1, num_qo_heads / num_kv_heads, head_dim,
-                                                      PD_DTYPE_FP16);
-        (void)dev;
-        if (g <= 0) return g < 0 ? g : fail(PD_E_ARG, "paged_decode_plan: no device target");
-        target = g;
+    if (target <= 0 && fixed_pages_per_chunk <= 0) {
+        // device default: the units the device holds resident at once, and
+        // within that the largest target whose plan still fits one round
+        // (the plan rule rounds the count up past its target, which would
+        // leave a few workgroups for a second, nearly empty round)
+        const int slots = paged_decode_default_target_wgs(-1, num_qo_heads / num_kv_heads,
+                                                          head_dim, dtype, num_kv_heads);
+        if (slots <= 0) return slots < 0 ? slots : fail(PD_E_ARG, "paged_decode_plan: no device target");
+        target = fit_target(batch, indptr, wg_per_chunk, slots);
     }
+    if (target <= 0) target = 1;
     int64_t c;
     if (fixed_pages_per_chunk > 0) {
         c = fixed_pages_per_chunk;
@@ -234,27 +284,7 @@ extern "C" int paged_decode_plan(int32_t batch, const int32_t *indptr,
                         fmt("paged_decode_plan: %lld pages per chunk gives more than %lld chunks",
                             c, PD_MAX_CHUNKS));
     } else {
-        // c_min: smallest launchable size (chunks(c) is non-increasing in c)
-        int64_t lo = 1, hi = cmax;
-        while (lo < hi) {
-            const int64_t mid = lo + (hi - lo) / 2;
-            if (chunks_at(batch, indptr, mid) <= PD_MAX_CHUNKS) hi = mid;
-            else lo = mid + 1;
-        }
-        const int64_t cmin = lo;
-        if (chunks_at(batch, indptr, cmin) * wg_per_chunk < target) {
-            c = cmin;  // nothing reaches the target: the most parallel launchable plan
-        } else {
-            // largest c in [cmin, cmax] whose workgroup count still reaches the target
-            lo = cmin;
-            hi = cmax;
-            while (lo < hi) {
-                const int64_t mid = lo + (hi - lo + 1) / 2;
-                if (chunks_at(batch, indptr, mid) * wg_per_chunk >= target) lo = mid;
-                else hi = mid - 1;
-            }
-            c = lo;
-        }
+        c = plan_c(batch, indptr, wg_per_chunk, target, cmin_of(batch, indptr, cmax), cmax);
     }
     const int64_t n = chunks_at(batch, indptr, c);
     info->pages_per_chunk = int32_t(c);

@@ -133,6 +133,100 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
     if (dv == 0) lse_out[oh] = m + __builtin_amdgcn_logf(wsum);
 }
 
+// One workgroup per (output row, head): its 256 threads are `split` row
+// lanes x D/4 dim lanes.  Row lane k merges rows k, k + split, ... of the
+// group into a partial state (max, weight sum, weighted V) with the loads of
+// up to kUnroll rows in flight, and the split partial states are combined
+// through LDS.  Long groups (many chunks per request) thus finish in a few
+// load round trips instead of one per row.
+template <int W>
+__global__ void __launch_bounds__(256) merge_split_kernel(const float *__restrict__ v_in,
+                                                          const float *__restrict__ lse_in,
+                                                          const int32_t *__restrict__ o_indptr,
+                                                          int32_t num_heads, int32_t head_dim,
+                                                          float *__restrict__ v_out,
+                                                          float *__restrict__ lse_out)
+{
+    using V = typename VecF<W>::type;
+    __shared__ float s_m[256];
+    __shared__ float s_w[256];
+    __shared__ V s_acc[256];
+    const int per_head = head_dim / W;           // <= 256, checked by the launcher
+    const int split = 256 / per_head;
+    const int tid = threadIdx.x;
+    const int k = tid / per_head;                // row lane
+    const int dv = tid - k * per_head;
+    const int64_t oh = blockIdx.x;               // o * num_heads + h
+    const int h = int(oh % num_heads);
+    const int64_t o = oh / num_heads;
+    const int b = o_indptr[o];
+    const int e = o_indptr[o + 1];
+    const bool active = k < split;
+
+    float m = -INFINITY;
+    bool nan_seen = false;
+    if (active) {
+        for (int i0 = b + k; i0 < e; i0 += split * kUnroll) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = min(i0 + u * split, e - 1);
+                const float x = lse_in[int64_t(i) * num_heads + h];
+                nan_seen |= x != x;
+                m = fmaxf(m, x);
+            }
+        }
+    }
+    float wsum = 0.f;
+    V acc = filled<V>(0.f);
+    if (active && m != -INFINITY) {
+        for (int i0 = b + k; i0 < e; i0 += split * kUnroll) {
+            float x[kUnroll];
+            V vi[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = min(i0 + u * split, e - 1);
+                x[u] = lse_in[int64_t(i) * num_heads + h];
+                vi[u] = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const bool live = i0 + u * split < e && x[u] != -INFINITY;
+                const float w = live ? __builtin_amdgcn_exp2f(x[u] - m) : 0.f;
+                wsum += w;
+                fma_live(acc, live, w, vi[u]);
+            }
+        }
+    }
+    s_m[tid] = nan_seen ? NAN : m;
+    s_w[tid] = wsum;
+    s_acc[tid] = acc;
+    __syncthreads();
+    if (k != 0) return;
+    float mx = -INFINITY;
+    bool any_nan = false;
+    for (int j = 0; j < split; ++j) {
+        const float mj = s_m[j * per_head + dv];
+        any_nan |= mj != mj;
+        mx = fmaxf(mx, mj);
+    }
+    V *dst = reinterpret_cast<V *>(v_out + oh * head_dim) + dv;
+    if (any_nan || mx == -INFINITY) {
+        *dst = filled<V>(any_nan ? NAN : 0.f);
+        if (dv == 0) lse_out[oh] = any_nan ? NAN : -INFINITY;
+        return;
+    }
+    float wt = 0.f;
+    V o_acc = filled<V>(0.f);
+    for (int j = 0; j < split; ++j) {
+        const float mj = s_m[j * per_head + dv];
+        const float sc = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - mx);
+        wt = fmaf(s_w[j * per_head + dv], sc, wt);
+        fma_into(o_acc, sc, s_acc[j * per_head + dv]);
+    }
+    *dst = scaled(o_acc, 1.f / wt);
+    if (dv == 0) lse_out[oh] = mx + __builtin_amdgcn_logf(wt);
+}
+
 }  // namespace
 }  // namespace pd
 
@@ -156,7 +250,17 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (vec4)
+    if (head_dim / w <= 256) {
+        // one workgroup per (output row, head), rows split across lanes
+        const int64_t nblk = int64_t(num_out_rows) * num_heads;
+        if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
+        if (vec4)
+            hipLaunchKernelGGL(merge_split_kernel<4>, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
+                               lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
+        else
+            hipLaunchKernelGGL(merge_split_kernel<1>, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
+                               lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
+    } else if (vec4)
         hipLaunchKernelGGL(merge_kernel<4>, dim3(uint32_t(blocks)), dim3(256), 0, s, v_in, lse_in,
                            o_indptr, num_out_rows, num_heads, head_dim, v_out, lse_out);
     else

@@ -54,6 +54,10 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPageWindow = 1024;     // page ids staged in LDS per round
+#ifndef PD_PIPELINE_DEPTH
+#define PD_PIPELINE_DEPTH 2
+#endif
+constexpr int kDepth = PD_PIPELINE_DEPTH;   // page kernel: steps per wave in the load pipeline
 constexpr float kLazyMargin = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr float kNoMax = -1e30f;      // finite "no score yet" running max
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer descriptor dword 3 (32-bit data)
@@ -284,8 +288,11 @@ __device__ __forceinline__ void epilogue(const PartialArgs &a, EpilogueSmem<G, D
         const int c = a.pages_per_chunk;
         ntiles = npages > 0 ? (npages + c - 1) / c : 1;
     }
-    // single-chunk requests in fused mode go straight to the output
+    // single-chunk requests in fused mode go straight to the output; a chunk
+    // whose row another workgroup will merge is published with agent-scope
+    // (cross-XCD coherent, "sc1") stores
     const bool direct = FUSED && ntiles == 1;
+    const bool publish = FUSED && !direct;
     float *vdst = direct ? a.o_final + (int64_t(r) * hq + head0) * D
                          : a.v_out + (int64_t(n) * hq + head0) * D;
     float *ldst = direct ? a.lse_final + int64_t(r) * hq + head0 : a.lse_out + int64_t(n) * hq + head0;
@@ -302,42 +309,60 @@ __device__ __forceinline__ void epilogue(const PartialArgs &a, EpilogueSmem<G, D
             lsum = fmaf(sm.l[w][h], sc, lsum);
             o = fmaf(sm.acc[w][h][d], sc, o);
         }
-        vdst[int64_t(h) * D + d] = lsum > 0.f ? o / lsum : 0.f;
-        if (d == 0) ldst[h] = lsum > 0.f ? mx + fast_log2(lsum) : -INFINITY;
+        const float ov = lsum > 0.f ? o / lsum : 0.f;
+        const float lv = lsum > 0.f ? mx + fast_log2(lsum) : -INFINITY;
+        if (publish) {
+            __hip_atomic_store(vdst + int64_t(h) * D + d, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) __hip_atomic_store(ldst + h, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            vdst[int64_t(h) * D + d] = ov;
+            if (d == 0) ldst[h] = lv;
+        }
     }
     if constexpr (FUSED) {
         if (direct) return;
-        // publish this chunk's row, then count it; the last chunk of the
-        // request merges all of them (rows n - t .. n - t + ntiles - 1)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // Every wave waits for its coherent stores to complete (a workgroup
+        // fence is a plain vmcnt wait here, not a cache writeback), then one
+        // thread counts the chunk.  The workgroup that brings the count to
+        // ntiles merges rows n - t .. n - t + ntiles - 1, reading them with
+        // coherent loads, and resets the counter for the next launch.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvh;
         if (tid == 0) {
-            const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL,
+            const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
             sm.last = prev == ntiles - 1;
         }
         __syncthreads();
         if (!sm.last) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const int64_t first = n - t;
         for (int idx = tid; idx < G * D; idx += kThreads) {
             const int h = idx / D;
             const int d = idx - h * D;
             const float *lrow = a.lse_out + first * hq + head0 + h;
             const float *vrow = a.v_out + (first * hq + head0 + h) * D + d;
+            constexpr int U = 16;
             float mx = -INFINITY;
-            for (int i = 0; i < ntiles; ++i) mx = fmaxf(mx, lrow[int64_t(i) * hq]);
+            for (int i0 = 0; i0 < ntiles; i0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = min(i0 + u, ntiles - 1);
+                    mx = fmaxf(mx, __hip_atomic_load(lrow + int64_t(i) * hq, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+                }
+            }
             float wsum = 0.f, o = 0.f;
             if (mx != -INFINITY) {
-                constexpr int U = 4;
                 for (int i0 = 0; i0 < ntiles; i0 += U) {
                     float x[U], vv[U];
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int i = min(i0 + u, ntiles - 1);
-                        x[u] = lrow[int64_t(i) * hq];
-                        vv[u] = vrow[int64_t(i) * hq * D];
+                        x[u] = __hip_atomic_load(lrow + int64_t(i) * hq, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                        vv[u] = __hip_atomic_load(vrow + int64_t(i) * hq * D, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
@@ -357,9 +382,25 @@ __device__ __forceinline__ void epilogue(const PartialArgs &a, EpilogueSmem<G, D
 }
 
 // ---------------------------------------------------------------- page kernel
-template <typename T, int G, bool FUSED>
-__global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
+// A workgroup holds HPW KV heads of one chunk with WPH waves per head (wave =
+// hi * WPH + wp).  With HPW = 8, WPH = 1 the eight waves of a workgroup walk
+// the same pages at the same time, each reading its head's rows, so every
+// page of K and V is fetched as one 32 KB burst on one CU (DRAM rows are
+// opened once per page instead of once per head).  Each wave is one (chunk,
+// KV head) unit in the sense of the plan.
+template <int G, int D, int HPW, int WPH>
+struct PageSmem {
+    float acc[WPH > 1 ? HPW * WPH : 1][G][WPH > 1 ? D : 1];
+    float m[HPW * WPH][G];
+    float l[HPW * WPH][G];
+    int last;
+};
+
+template <typename T, int G, int HPW, int WPH, bool FUSED>
+__global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArgs a)
 {
+    constexpr int NW = HPW * WPH;     // waves per workgroup
+    constexpr int NT = 64 * NW;
     constexpr int VEC = Vec<T>::N;
     constexpr int L = 16;             // lanes per 256-byte row
     constexpr int R = 4;              // rows per wave
@@ -369,13 +410,17 @@ __global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
     static_assert(J * G == 16 && J >= 1, "group");
 
     __shared__ int32_t s_pid[kPageWindow];
-    __shared__ EpilogueSmem<G, D> sm;
+    __shared__ PageSmem<G, D, HPW, WPH> sm;
 
+    const int groups = a.num_kv_heads / HPW;
     const int wg = blockIdx.x;
-    const int n = wg / a.num_kv_heads;
-    const int kvh = wg - n * a.num_kv_heads;
+    const int n = wg / groups;
+    const int kvg = wg - n * groups;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+    const int hi = wave / WPH;
+    const int wp = wave - hi * WPH;
+    const int kvh = kvg * HPW + hi;
     const int lane = tid & 63;
     const int row = lane >> 4;
     const int li = lane & 15;
@@ -423,19 +468,26 @@ __global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
     for (int wp0 = cp0; wp0 < cp1; wp0 += kPageWindow) {
         const int wp1 = min(cp1, wp0 + kPageWindow);
         __syncthreads();
-        for (int i = tid; i < wp1 - wp0; i += kThreads) s_pid[i] = a.indices[pbeg + wp0 + i];
+        for (int i = tid; i < wp1 - wp0; i += NT) s_pid[i] = a.indices[pbeg + wp0 + i];
         __syncthreads();
         const int nsteps = (wp1 - wp0) << spp_log2;
 
+        // Loads are issued unconditionally so that the wait before each
+        // step's compute only covers that step's loads (a load under a
+        // branch makes the wait count conservative, i.e. wait for all).  A
+        // step past the end gets a zero-size buffer: its loads return zeros
+        // and touch no memory.
         auto load = [&](int s, Row16 (&kr)[J], Row16 (&vr)[J]) {
-            const int p = s >> spp_log2;
+            const bool live = s < nsteps;
+            const int p = min(s >> spp_log2, wp1 - wp0 - 1);
             const int sub = s & ((1 << spp_log2) - 1);
             const int pid = __builtin_amdgcn_readfirstlane(s_pid[p]);
             const int64_t base = int64_t(pid) * page_bytes;
+            const int32_t span = live ? page_span : 0;
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<char *>(kb + base), 0, page_span, kBufferWord3);
+                const_cast<char *>(kb + base), 0, span, kBufferWord3);
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<char *>(vb + base), 0, page_span, kBufferWord3);
+                const_cast<char *>(vb + base), 0, span, kBufferWord3);
             const int soff = int(sub * step_bytes);
 #pragma unroll
             for (int j = 0; j < J; ++j) {
@@ -458,13 +510,13 @@ __global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
             const bool edge = (p == 0 && fpo > 0) || (p == npages - 1 && lpl < ps);
             if (edge) {
                 const int lo = p == 0 ? fpo : 0;
-                const int hi = p == npages - 1 ? lpl : ps;
+                const int hi_slot = p == npages - 1 ? lpl : ps;
                 const int slot_own = sub * SPS + j_own * R + row;
-                sc = (slot_own >= lo && slot_own < hi) ? sc : -INFINITY;
+                sc = (slot_own >= lo && slot_own < hi_slot) ? sc : -INFINITY;
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
                     const int slot = sub * SPS + j * R + row;
-                    const bool ok = slot >= lo && slot < hi;
+                    const bool ok = slot >= lo && slot < hi_slot;
                     vr[j].u.x = ok ? vr[j].u.x : 0u;
                     vr[j].u.y = ok ? vr[j].u.y : 0u;
                     vr[j].u.z = ok ? vr[j].u.z : 0u;
@@ -503,18 +555,22 @@ __global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
                 }
         };
 
-        Row16 k0[J], v0[J], k1[J], v1[J];
-        int s = wave;
-        if (s < nsteps) load(s, k0, v0);
+        // software pipeline: the loads of this wave's next kDepth-1 steps
+        // are in flight while a step computes
+        Row16 kbuf[kDepth][J], vbuf[kDepth][J];
+        int s = wp;
+        if (s < nsteps) {
+#pragma unroll
+            for (int d = 0; d < kDepth - 1; ++d) load(s + d * WPH, kbuf[d], vbuf[d]);
+        }
         while (s < nsteps) {
-            const int s1 = s + kWaves;
-            if (s1 < nsteps) load(s1, k1, v1);
-            compute(s, k0, v0);
-            if (s1 >= nsteps) break;
-            const int s2 = s1 + kWaves;
-            if (s2 < nsteps) load(s2, k0, v0);
-            compute(s1, k1, v1);
-            s = s2;
+#pragma unroll
+            for (int u = 0; u < kDepth; ++u) {
+                load(s + (kDepth - 1) * WPH, kbuf[(u + kDepth - 1) % kDepth],
+                     vbuf[(u + kDepth - 1) % kDepth]);
+                if (s < nsteps) compute(s, kbuf[u], vbuf[u]);
+                s += WPH;
+            }
         }
     }
 
@@ -534,7 +590,153 @@ __global__ void __launch_bounds__(kThreads) partial_page_kernel(PartialArgs a)
             l[h] = tl[h];
         }
     }
-    epilogue<G, D, L, FUSED>(a, sm, m, l, acc, n, kvh, r, t, npages);
+    // combine the four rows of the wave (same head, same dims in lanes li,
+    // li + 16, li + 32, li + 48)
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(m[h], off);
+            const float lo = __shfl_xor(l[h], off);
+            const float mx = fmaxf(m[h], mo);
+            const float a1 = fast_exp2(m[h] - mx);
+            const float a2 = fast_exp2(mo - mx);
+            l[h] = l[h] * a1 + lo * a2;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float ao = __shfl_xor(acc[h][e], off);
+                acc[h][e] = acc[h][e] * a1 + ao * a2;
+            }
+            m[h] = mx;
+        }
+    }
+
+    const int hq = a.num_qo_heads;
+    int ntiles = 1;
+    if constexpr (FUSED) {
+        const int c = a.pages_per_chunk;
+        ntiles = npages > 0 ? (npages + c - 1) / c : 1;
+    }
+    const bool direct = FUSED && ntiles == 1;
+    const bool publish = FUSED && !direct;
+    const int64_t head_lo = int64_t(kvg) * HPW * G;      // first query head of the workgroup
+    float *vrow = direct ? a.o_final + int64_t(r) * hq * D : a.v_out + int64_t(n) * hq * D;
+    float *lrow = direct ? a.lse_final + int64_t(r) * hq : a.lse_out + int64_t(n) * hq;
+    auto put = [&](int64_t qh, int d, float ov, bool with_lse, float lv) {
+        if (publish) {
+            __hip_atomic_store(vrow + qh * D + d, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (with_lse) __hip_atomic_store(lrow + qh, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            vrow[qh * D + d] = ov;
+            if (with_lse) lrow[qh] = lv;
+        }
+    };
+
+    if constexpr (WPH == 1) {
+        // each wave owns its head: row 0 writes it
+        if (row == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+                const float lv = l[h] > 0.f ? m[h] + fast_log2(l[h]) : -INFINITY;
+                const int64_t qh = int64_t(kvh) * G + h;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) put(qh, li * VEC + e, acc[h][e] * inv, e == 0 && li == 0, lv);
+            }
+        }
+    } else {
+        if (row == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) sm.acc[wave][h][li * VEC + e] = acc[h][e];
+                if (li == 0) {
+                    sm.m[wave][h] = m[h];
+                    sm.l[wave][h] = l[h];
+                }
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < HPW * G * D; idx += NT) {
+            const int hh = idx / D;               // hi * G + h
+            const int d = idx - hh * D;
+            const int hw = hh / G;
+            const int h = hh - hw * G;
+            float mx = sm.m[hw * WPH][h];
+#pragma unroll
+            for (int w = 1; w < WPH; ++w) mx = fmaxf(mx, sm.m[hw * WPH + w][h]);
+            float lsum2 = 0.f, o = 0.f;
+#pragma unroll
+            for (int w = 0; w < WPH; ++w) {
+                const float sc = fast_exp2(sm.m[hw * WPH + w][h] - mx);
+                lsum2 = fmaf(sm.l[hw * WPH + w][h], sc, lsum2);
+                o = fmaf(sm.acc[hw * WPH + w][h][d], sc, o);
+            }
+            put(head_lo + hh, d, lsum2 > 0.f ? o / lsum2 : 0.f, d == 0,
+                lsum2 > 0.f ? mx + fast_log2(lsum2) : -INFINITY);
+        }
+    }
+
+    if constexpr (FUSED) {
+        if (direct) return;
+        // Every wave waits for its coherent stores to complete (a workgroup
+        // fence is a plain vmcnt wait here, not a cache writeback), then one
+        // thread counts the chunk.  The workgroup that brings the count to
+        // ntiles merges rows n - t .. n - t + ntiles - 1 for its heads,
+        // reading them with coherent loads, and resets the counter.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvg;
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            sm.last = prev == ntiles - 1;
+        }
+        __syncthreads();
+        if (!sm.last) return;
+        const int64_t first = n - t;
+        for (int idx = tid; idx < HPW * G * D; idx += NT) {
+            const int64_t qh = head_lo + idx / D;
+            const int d = idx % D;
+            const float *lr = a.lse_out + first * hq + qh;
+            const float *vr = a.v_out + (first * hq + qh) * D + d;
+            constexpr int U = 16;
+            float mx = -INFINITY;
+            for (int i0 = 0; i0 < ntiles; i0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = min(i0 + u, ntiles - 1);
+                    mx = fmaxf(mx, __hip_atomic_load(lr + int64_t(i) * hq, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+                }
+            }
+            float wsum = 0.f, o = 0.f;
+            if (mx != -INFINITY) {
+                for (int i0 = 0; i0 < ntiles; i0 += U) {
+                    float x[U], vv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int i = min(i0 + u, ntiles - 1);
+                        x[u] = __hip_atomic_load(lr + int64_t(i) * hq, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                        vv[u] = __hip_atomic_load(vr + int64_t(i) * hq * D, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const bool live = i0 + u < ntiles && x[u] != -INFINITY;
+                        const float w = live ? fast_exp2(x[u] - mx) : 0.f;
+                        wsum += w;
+                        o = live ? fmaf(w, vv[u], o) : o;
+                    }
+                }
+            }
+            a.o_final[(int64_t(r) * hq + qh) * D + d] = wsum > 0.f ? o / wsum : 0.f;
+            if (d == 0)
+                a.lse_final[int64_t(r) * hq + qh] = wsum > 0.f ? mx + fast_log2(wsum) : -INFINITY;
+        }
+        if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // --------------------------------------------------------------- token kernel
@@ -651,16 +853,18 @@ __global__ void __launch_bounds__(kThreads) partial_token_kernel(PartialArgs a)
             }
         };
 
+        // loads issued unconditionally (rows past the end are clamped to the
+        // last token) so that each wait covers only the step it feeds
         Row16 k0[J], v0[J], k1[J], v1[J];
         int s = wave;
         if (s < nsteps) load(s, k0, v0);
         while (s < nsteps) {
             const int s1 = s + kWaves;
-            if (s1 < nsteps) load(s1, k1, v1);
+            load(s1, k1, v1);
             compute(s, k0, v0);
             if (s1 >= nsteps) break;
             const int s2 = s1 + kWaves;
-            if (s2 < nsteps) load(s2, k0, v0);
+            load(s2, k0, v0);
             compute(s1, k1, v1);
             s = s2;
         }
@@ -691,13 +895,43 @@ KernelFn pick_token(int g)
     }
 }
 
+// KV heads per workgroup of the page kernel: every head of the chunk (up to
+// 8), one wave each; a group of fewer heads gets more waves per head so the
+// workgroup still has 4 to 8 waves.
+#ifndef PD_PAGE_HPW_MAX
+#define PD_PAGE_HPW_MAX 8
+#endif
+int page_heads_per_wg(int hkv, int g)
+{
+    // G = 16 needs more than 256 VGPRs per lane: at most 4 waves per group
+    const int cap = g >= 16 ? (PD_PAGE_HPW_MAX < 4 ? PD_PAGE_HPW_MAX : 4) : PD_PAGE_HPW_MAX;
+    for (int h = cap; h > 1; h >>= 1)
+        if (hkv % h == 0) return h;
+    return 1;
+}
+
+template <typename T, int G, bool FUSED>
+KernelFn pick_page_shape(int hpw)
+{
+    switch (hpw) {
+    case 8:
+        if constexpr (G < 16) return partial_page_kernel<T, G, 8, 1, FUSED>;
+        else return nullptr;
+    case 4: return partial_page_kernel<T, G, 4, 1, FUSED>;
+    case 2: return partial_page_kernel<T, G, 2, 2, FUSED>;
+    default: return partial_page_kernel<T, G, 1, 4, FUSED>;
+    }
+}
+
+int page_threads(int hpw) { return hpw >= 4 ? 64 * hpw : 256; }
+
 template <typename T, bool FUSED>
-KernelFn pick_page(int g)
+KernelFn pick_page(int g, int hpw)
 {
     switch (g) {
-    case 4: return partial_page_kernel<T, 4, FUSED>;
-    case 8: return partial_page_kernel<T, 8, FUSED>;
-    case 16: return partial_page_kernel<T, 16, FUSED>;
+    case 4: return pick_page_shape<T, 4, FUSED>(hpw);
+    case 8: return pick_page_shape<T, 8, FUSED>(hpw);
+    case 16: return pick_page_shape<T, 16, FUSED>(hpw);
     default: return nullptr;
     }
 }
@@ -705,15 +939,17 @@ KernelFn pick_page(int g)
 struct Choice {
     KernelFn fn;
     int spp_log2;
+    int heads_per_wg;   // KV heads one workgroup covers
+    int threads;
 };
 
 // The page kernel serves 256-byte rows, G in {4, 8, 16}, and page sizes that
 // are a power-of-two multiple of its 64/G slots per step with 32-bit lane
 // offsets; every other shape takes the token kernel.
 Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
-            bool allow_page = true)
+            bool allow_page = true, int hkv = 1)
 {
-    Choice c{nullptr, 0};
+    Choice c{nullptr, 0, 1, kThreads};
     const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
     const bool row256 = (dtype == PD_DTYPE_FP16 && d == 128) || (dtype == PD_DTYPE_FP32 && d == 64);
     if (allow_page && row256 && (g == 4 || g == 8 || g == 16)) {
@@ -724,8 +960,11 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
                 int lg = 0;
                 while ((1 << lg) < spp) ++lg;
                 c.spp_log2 = lg;
-                if (dtype == PD_DTYPE_FP16) c.fn = fused ? pick_page<_Float16, true>(g) : pick_page<_Float16, false>(g);
-                else c.fn = fused ? pick_page<float, true>(g) : pick_page<float, false>(g);
+                const int hpw = page_heads_per_wg(hkv, g);
+                c.heads_per_wg = hpw;
+                c.threads = page_threads(hpw);
+                if (dtype == PD_DTYPE_FP16) c.fn = fused ? pick_page<_Float16, true>(g, hpw) : pick_page<_Float16, false>(g, hpw);
+                else c.fn = fused ? pick_page<float, true>(g, hpw) : pick_page<float, false>(g, hpw);
                 return c;
             }
         }
@@ -801,8 +1040,8 @@ int launch(const Choice &c, const PartialArgs &a, int32_t num_chunks, void *stre
 {
     PartialArgs b = a;
     b.spp_log2 = c.spp_log2;
-    const dim3 grid(uint32_t(int64_t(num_chunks) * a.num_kv_heads));
-    hipLaunchKernelGGL(c.fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), b);
+    const dim3 grid(uint32_t(int64_t(num_chunks) * (a.num_kv_heads / c.heads_per_wg)));
+    hipLaunchKernelGGL(c.fn, grid, dim3(c.threads), 0, static_cast<hipStream_t>(stream), b);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return fail(PD_E_HIP, std::string(who) + ": launch failed: " + hipGetErrorString(err));
@@ -838,7 +1077,7 @@ extern "C" int paged_decode_partial(const void *q, const void *k_pool, const voi
                             who);
     if (rc) return rc;
     const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
-                          false, !g_force_token_kernel);
+                          false, !g_force_token_kernel, num_kv_heads);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_partial: no kernel for this (dtype, D, group)");
     if (num_chunks == 0) return PD_OK;
     return launch(c, a, num_chunks, stream, who);
@@ -867,7 +1106,7 @@ extern "C" int paged_decode_fused(const void *q, const void *k_pool, const void 
     if (num_chunks < batch)
         return fail(PD_E_ARG, "paged_decode_fused: fewer chunks than requests");
     const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
-                          true, !g_force_token_kernel);
+                          true, !g_force_token_kernel, num_kv_heads);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_fused: no kernel for this (dtype, D, group)");
     a.o_final = out;
     a.lse_final = lse_out;
@@ -892,9 +1131,13 @@ extern "C" int paged_decode_kernel_kind(int32_t dtype, int32_t head_dim, int32_t
 }
 
 extern "C" int paged_decode_default_target_wgs(int32_t device, int32_t group_size,
-                                               int32_t head_dim, int32_t dtype)
+                                               int32_t head_dim, int32_t dtype,
+                                               int32_t num_kv_heads)
 {
-    const Choice c = pick(dtype, head_dim, group_size, 16, head_dim, false, !g_force_token_kernel);
+    if (num_kv_heads < 1)
+        return fail(PD_E_ARG, "paged_decode_default_target_wgs: num_kv_heads must be >= 1");
+    const Choice c = pick(dtype, head_dim, group_size, 16, int64_t(num_kv_heads) * head_dim,
+                          false, !g_force_token_kernel, num_kv_heads);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_default_target_wgs: unsupported shape");
     int dev = device;
     if (dev < 0 && hipGetDevice(&dev) != hipSuccess)
@@ -908,10 +1151,12 @@ extern "C" int paged_decode_default_target_wgs(int32_t device, int32_t group_siz
         return fail(PD_E_HIP, "paged_decode_default_target_wgs: cannot select device");
     int per_cu = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void *>(c.fn), kThreads, 0);
+        &per_cu, reinterpret_cast<const void *>(c.fn), c.threads, 0);
     if (prev >= 0 && prev != dev && hipSetDevice(prev) != hipSuccess)
         return fail(PD_E_HIP, "paged_decode_default_target_wgs: cannot restore device");
     if (e != hipSuccess || per_cu < 1)
         return fail(PD_E_HIP, "paged_decode_default_target_wgs: occupancy query failed");
-    return cus * per_cu;
+    // resident (chunk, KV head) units: a workgroup of the page kernel holds
+    // heads_per_wg of them
+    return cus * per_cu * c.heads_per_wg;
 }

@@ -43,15 +43,18 @@ class PagedDecode:
 
     def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
                  num_kv_heads: int, head_dim: int, target_wgs: int = 0,
-                 fixed_pages_per_chunk: int = 0, fused: bool = False, device="cuda"):
+                 fixed_pages_per_chunk: int = 0, fused: bool = False, dtype=torch.float16,
+                 device="cuda"):
         indptr = np.asarray(csr["indptr"], np.int32)
         self.batch = indptr.size - 1
         self.page_size = page_size
         self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
         B.csr_validate(self.batch, page_size, num_pool_pages, indptr, csr["indices"],
                        csr["last_page_len"], csr["first_page_offset"], csr.get("seq_lens"))
+        pd_dtype = B.PD_DTYPE_FP32 if dtype == torch.float32 else B.PD_DTYPE_FP16
         info, ri, ti, oi = B.paged_decode_plan(indptr, num_qo_heads, num_kv_heads, head_dim,
-                                               target_wgs, fixed_pages_per_chunk)
+                                               target_wgs, fixed_pages_per_chunk,
+                                               dtype=pd_dtype)
         self.info, self.request_indices, self.kv_tile_indices, self.o_indptr = info, ri, ti, oi
         self.device = torch.device(device)
         idx = np.asarray(csr["indices"], np.int32)

@@ -100,7 +100,8 @@ def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None, fused=
     dec = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
                          num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
                          head_dim=w.head_dim, target_wgs=target, fixed_pages_per_chunk=fixed,
-                         fused=fused)
+                         fused=fused,
+                         dtype=torch.float32 if w.dtype == workloads.FP32 else torch.float16)
     info = dec.info
     kind = B.paged_decode_kernel_kind(B.PD_DTYPE_FP16 if w.dtype == workloads.FP16 else
                                       B.PD_DTYPE_FP32, w.head_dim,
@@ -424,6 +425,25 @@ def test_merge_kernel_nan_propagates(orc):
 
 
 def test_default_target_is_cu_multiple():
-    t = B.paged_decode_default_target_wgs(0, 4, 128, B.PD_DTYPE_FP16)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert t >= cus and t % cus == 0
+    for g, hkv in ((4, 8), (4, 2), (8, 8), (16, 8), (12, 1)):
+        t = B.paged_decode_default_target_wgs(0, g, 128, B.PD_DTYPE_FP16, hkv)
+        assert t >= cus and t % cus == 0, (g, hkv, t)
+
+
+@pytest.mark.parametrize("name", ["long_context_fp16", "batched_fp16", "tiny_fp32"])
+def test_default_target_fits_one_round(orc, name):
+    """Default plan: the largest target whose unit count fits the resident
+    capacity S, checked against the oracle's exhaustive plans."""
+    w = cached(name)
+    csr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                    w.page_size)
+    g = w.num_qo_heads // w.num_kv_heads
+    dt = B.PD_DTYPE_FP16 if w.dtype == workloads.FP16 else B.PD_DTYPE_FP32
+    slots = B.paged_decode_default_target_wgs(0, g, w.head_dim, dt, w.num_kv_heads)
+    info, _, _, _ = B.paged_decode_plan(csr["indptr"], w.num_qo_heads, w.num_kv_heads,
+                                        w.head_dim, 0, 0, sizes_only=True, dtype=dt)
+    units = lambda t: orc.plan(csr["indptr"], w.num_kv_heads, t)["num_chunks"] * w.num_kv_heads
+    best = max([t for t in range(1, slots + 1) if units(t) <= slots] or [slots])
+    assert info.target_wgs == best
+    assert info.num_wgs <= slots or units(1) > slots
