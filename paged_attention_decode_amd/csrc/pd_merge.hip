@@ -163,22 +163,14 @@ __global__ void __launch_bounds__(256) merge_split_kernel(const float *__restric
     const int e = o_indptr[o + 1];
     const bool active = k < split;
 
+    // one pass: each batch of kUnroll rows is loaded at once (LSE and V
+    // together), and the running state is rescaled when a batch raises the
+    // max
     float m = -INFINITY;
     bool nan_seen = false;
-    if (active) {
-        for (int i0 = b + k; i0 < e; i0 += split * kUnroll) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int i = min(i0 + u * split, e - 1);
-                const float x = lse_in[int64_t(i) * num_heads + h];
-                nan_seen |= x != x;
-                m = fmaxf(m, x);
-            }
-        }
-    }
     float wsum = 0.f;
     V acc = filled<V>(0.f);
-    if (active && m != -INFINITY) {
+    if (active) {
         for (int i0 = b + k; i0 < e; i0 += split * kUnroll) {
             float x[kUnroll];
             V vi[kUnroll];
@@ -188,8 +180,21 @@ __global__ void __launch_bounds__(256) merge_split_kernel(const float *__restric
                 x[u] = lse_in[int64_t(i) * num_heads + h];
                 vi[u] = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
             }
+            float mb = m;
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
+                nan_seen |= x[u] != x[u];
+                mb = fmaxf(mb, x[u]);
+            }
+            if (mb == -INFINITY) continue;              // nothing finite yet
+            const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mb);
+            wsum *= sc;
+            acc = scaled(acc, sc);
+            m = mb;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                // a row past the group end or with lse = -inf (empty chunk) has
+                // no weight, and its V (possibly not finite) is never multiplied in
                 const bool live = i0 + u * split < e && x[u] != -INFINITY;
                 const float w = live ? __builtin_amdgcn_exp2f(x[u] - m) : 0.f;
                 wsum += w;
