@@ -58,6 +58,10 @@ constexpr int kPageWindow = 1024;     // page ids staged in LDS per round
 #define PD_PIPELINE_DEPTH 2
 #endif
 constexpr int kDepth = PD_PIPELINE_DEPTH;   // page kernel: steps per wave in the load pipeline
+#ifndef PD_LOCKSTEP_ROUNDS
+#define PD_LOCKSTEP_ROUNDS 1
+#endif
+constexpr int kLockstep = PD_LOCKSTEP_ROUNDS;   // page kernel: rounds between wave barriers (0: none)
 constexpr float kLazyMargin = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr float kNoMax = -1e30f;      // finite "no score yet" running max
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer descriptor dword 3 (32-bit data)
@@ -142,6 +146,61 @@ __device__ __forceinline__ void row_bcast_all(float x, float (&out)[16])
     out[13] = row_bcast<13>(x);
     out[14] = row_bcast<14>(x);
     out[15] = row_bcast<15>(x);
+}
+
+// Read-only plan data (page table, request and chunk arrays) through the
+// scalar cache: the address is wave-uniform, and an address-space-4 (constant)
+// pointer lets the compiler use a scalar load instead of a vector load plus
+// readfirstlane.  Nothing in the kernel writes these arrays.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t *p)
+{
+    typedef const __attribute__((address_space(4))) int32_t constant_i32;
+    return *(constant_i32 *)p;   // generic -> constant address space
+}
+
+// gfx950 permlane swaps.  After swap32(a, b) the lanes of the lower half
+// hold (a of lane l, a of lane l + 32) and those of the upper half hold (b of
+// lane l - 32, b of lane l): each half gets the (lower, upper) pair of one of
+// the two values.  swap16 does the same for each pair of 16-lane rows (even
+// row: the pair of a, odd row: the pair of b).  They are issued as inline
+// assembly because the compiler's builtins for them hand back the first
+// result in place of the second; the nop covers the wait states a permlane
+// needs after a VALU write of its operands.
+__device__ __forceinline__ void swap32(float &a, float &b)
+{
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float &a, float &b)
+{
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// One level of the reduce-scatter combine of softmax states: the lane keeps
+// state a (lower half / even row) or state b (upper half / odd row), merged
+// with the same state of its partner lane.  Partners compute from the same
+// (lower, upper) pair, so a state's two copies stay bit-identical.
+template <bool HALVES, int VEC>
+__device__ __forceinline__ void merge_level(float ma, float mb, float la, float lb,
+                                            const float (&xa)[VEC], const float (&xb)[VEC],
+                                            float &m, float &l, float (&x)[VEC])
+{
+    auto swap = [](float &u, float &v) {
+        if constexpr (HALVES) swap32(u, v);
+        else swap16(u, v);
+    };
+    swap(ma, mb);
+    swap(la, lb);
+    const float mx = fmaxf(ma, mb);
+    const float s0 = fast_exp2(ma - mx);
+    const float s1 = fast_exp2(mb - mx);
+    m = mx;
+    l = la * s0 + lb * s1;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        float u = xa[e], v = xb[e];
+        swap(u, v);
+        x[e] = u * s0 + v * s1;
+    }
 }
 
 // Sum over the L consecutive lanes of a row; every lane of the row ends with
@@ -409,7 +468,6 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
     constexpr int SPS = R * J;        // slots per step
     static_assert(J * G == 16 && J >= 1, "group");
 
-    __shared__ int32_t s_pid[kPageWindow];
     __shared__ PageSmem<G, D, HPW, WPH> sm;
 
     const int groups = a.num_kv_heads / HPW;
@@ -425,12 +483,12 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
     const int row = lane >> 4;
     const int li = lane & 15;
 
-    const int r = a.req_idx[n];
-    const int t = a.tile_idx[n];
-    const int pbeg = a.indptr[r];
-    const int npages = a.indptr[r + 1] - pbeg;
-    const int fpo = a.fpo[r];
-    const int lpl = a.lpl[r];
+    const int r = ld_uniform(a.req_idx + n);
+    const int t = ld_uniform(a.tile_idx + n);
+    const int pbeg = ld_uniform(a.indptr + r);
+    const int npages = ld_uniform(a.indptr + r + 1) - pbeg;
+    const int fpo = ld_uniform(a.fpo + r);
+    const int lpl = ld_uniform(a.lpl + r);
     const int ps = a.page_size;
     const int cp0 = t * a.pages_per_chunk;
     const int cp1 = min(npages, cp0 + a.pages_per_chunk);
@@ -465,12 +523,13 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
 
     const int j_own = li / G;         // the token row this lane scores
 
-    for (int wp0 = cp0; wp0 < cp1; wp0 += kPageWindow) {
-        const int wp1 = min(cp1, wp0 + kPageWindow);
-        __syncthreads();
-        for (int i = tid; i < wp1 - wp0; i += NT) s_pid[i] = a.indices[pbeg + wp0 + i];
-        __syncthreads();
-        const int nsteps = (wp1 - wp0) << spp_log2;
+    // The page ids of the chunk are taken 64 at a time, one per lane of a
+    // vector register (a single load per wave; no LDS staging and no
+    // barrier), and read out per step with readlane.
+    for (int wp0 = cp0; wp0 < cp1; wp0 += 64) {
+        const int wcount = min(cp1 - wp0, 64);
+        const int32_t idv = a.indices[pbeg + wp0 + min(lane, wcount - 1)];
+        const int nsteps = wcount << spp_log2;
 
         // Loads are issued unconditionally so that the wait before each
         // step's compute only covers that step's loads (a load under a
@@ -479,9 +538,9 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
         // and touch no memory.
         auto load = [&](int s, Row16 (&kr)[J], Row16 (&vr)[J]) {
             const bool live = s < nsteps;
-            const int p = min(s >> spp_log2, wp1 - wp0 - 1);
+            const int p = min(s >> spp_log2, wcount - 1);
             const int sub = s & ((1 << spp_log2) - 1);
-            const int pid = __builtin_amdgcn_readfirstlane(s_pid[p]);
+            const int pid = __builtin_amdgcn_readlane(idv, p);
             const int64_t base = int64_t(pid) * page_bytes;
             const int32_t span = live ? page_span : 0;
             const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -559,17 +618,26 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
         // are in flight while a step computes
         Row16 kbuf[kDepth][J], vbuf[kDepth][J];
         int s = wp;
-        if (s < nsteps) {
 #pragma unroll
-            for (int d = 0; d < kDepth - 1; ++d) load(s + d * WPH, kbuf[d], vbuf[d]);
-        }
-        while (s < nsteps) {
+        for (int d = 0; d < kDepth - 1; ++d) load(s + d * WPH, kbuf[d], vbuf[d]);
+        // Every wave runs the same number of rounds (the step count is
+        // uniform over the workgroup), so the waves can be held in lockstep
+        // by a barrier every kLockstep rounds.  Without it the SIMD issues
+        // the older of its two waves first: waves 0..3 end their pages long
+        // before waves 4..7, and for the rest of the chunk the CU streams
+        // with half its waves.  The barrier orders no memory, so it is the
+        // bare instruction: the loads in flight stay in flight across it.
+        const int rounds = (nsteps + WPH * kDepth - 1) / (WPH * kDepth);
+        for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
             for (int u = 0; u < kDepth; ++u) {
                 load(s + (kDepth - 1) * WPH, kbuf[(u + kDepth - 1) % kDepth],
                      vbuf[(u + kDepth - 1) % kDepth]);
                 if (s < nsteps) compute(s, kbuf[u], vbuf[u]);
                 s += WPH;
+            }
+            if constexpr (kLockstep > 0 && NW > 1) {
+                if (rd % kLockstep == kLockstep - 1) __builtin_amdgcn_s_barrier();
             }
         }
     }
@@ -590,26 +658,21 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
             l[h] = tl[h];
         }
     }
-    // combine the four rows of the wave (same head, same dims in lanes li,
-    // li + 16, li + 32, li + 48)
+    // Combine the four rows of the wave (same head, same dims in lanes li,
+    // li + 16, li + 32, li + 48) as a reduce-scatter: the halves split the G
+    // heads in two, then the row pairs split each half again, so row rho
+    // ends with the combined state of heads rho * G/4 .. rho * G/4 + G/4 - 1.
+    constexpr int G2 = G / 2, G4 = G / 4;
+    float m1[G2], l1[G2], acc1[G2][VEC];
 #pragma unroll
-    for (int off = 16; off < 64; off <<= 1) {
+    for (int k = 0; k < G2; ++k)
+        merge_level<true>(m[k], m[k + G2], l[k], l[k + G2], acc[k], acc[k + G2], m1[k], l1[k], acc1[k]);
+    float m2[G4], l2[G4], acc2[G4][VEC];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mo = __shfl_xor(m[h], off);
-            const float lo = __shfl_xor(l[h], off);
-            const float mx = fmaxf(m[h], mo);
-            const float a1 = fast_exp2(m[h] - mx);
-            const float a2 = fast_exp2(mo - mx);
-            l[h] = l[h] * a1 + lo * a2;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float ao = __shfl_xor(acc[h][e], off);
-                acc[h][e] = acc[h][e] * a1 + ao * a2;
-            }
-            m[h] = mx;
-        }
-    }
+    for (int k = 0; k < G4; ++k)
+        merge_level<false>(m1[k], m1[k + G4], l1[k], l1[k + G4], acc1[k], acc1[k + G4], m2[k], l2[k],
+                           acc2[k]);
+    const int h_row = row * G4;       // first head of this row
 
     const int hq = a.num_qo_heads;
     int ntiles = 1;
@@ -633,27 +696,23 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
     };
 
     if constexpr (WPH == 1) {
-        // each wave owns its head: row 0 writes it
-        if (row == 0) {
+        // each wave owns its KV head; every row writes the heads it holds
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
-                const float lv = l[h] > 0.f ? m[h] + fast_log2(l[h]) : -INFINITY;
-                const int64_t qh = int64_t(kvh) * G + h;
+        for (int k = 0; k < G4; ++k) {
+            const float inv = l2[k] > 0.f ? 1.f / l2[k] : 0.f;
+            const float lv = l2[k] > 0.f ? m2[k] + fast_log2(l2[k]) : -INFINITY;
+            const int64_t qh = int64_t(kvh) * G + h_row + k;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) put(qh, li * VEC + e, acc[h][e] * inv, e == 0 && li == 0, lv);
-            }
+            for (int e = 0; e < VEC; ++e) put(qh, li * VEC + e, acc2[k][e] * inv, e == 0 && li == 0, lv);
         }
     } else {
-        if (row == 0) {
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
+        for (int k = 0; k < G4; ++k) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) sm.acc[wave][h][li * VEC + e] = acc[h][e];
-                if (li == 0) {
-                    sm.m[wave][h] = m[h];
-                    sm.l[wave][h] = l[h];
-                }
+            for (int e = 0; e < VEC; ++e) sm.acc[wave][h_row + k][li * VEC + e] = acc2[k][e];
+            if (li == 0) {
+                sm.m[wave][h_row + k] = m2[k];
+                sm.l[wave][h_row + k] = l2[k];
             }
         }
         __syncthreads();
