@@ -9,7 +9,9 @@ timing; the plan is built outside the timed region, as the pages' microbench
 does (PR #984, commit adding the three-way microbench).
 
 The timed region is K back-to-back decode steps, bracketed by device
-synchronization and HIP events on the launch stream.  Consecutive steps read
+synchronization and HIP events on the launch stream, after --settle-ms of
+untimed steps and W warmup steps (a GPU coming out of idle runs the first few
+milliseconds of work about 5% slower).  Consecutive steps read
 different copies of the K/V pools (3 by default, each larger than the 256 MB
 last-level cache), so every step streams its KV bytes from HBM.  `value` =
 algorithmic KV bytes / (region time / K).  The partial kernel alone is timed
@@ -66,8 +68,11 @@ def counter_traffic():
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--settle-ms", type=float, default=50.0,
+                   help="untimed steps run for this long before the warmup steps of each "
+                        "timed region (the GPU takes a few ms to leave its idle state)")
     p.add_argument("--workload", default="long_context_fp16",
                    choices=["long_context_fp16", "batched_fp16", "tiny_fp32", "cascade_fp16"])
     p.add_argument("--target-wgs", type=int, default=0, help="plan target (0: device default)")
@@ -185,7 +190,19 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / n, (time.time() - w0) / n
 
-    # warmup, then the timed steps (the metric)
+    def settle(fn):
+        """Run fn back to back for --settle-ms of wall time (untimed): the
+        first few ms of work after an idle period run measurably slower."""
+        t_end = time.time() + args.settle_ms * 1e-3
+        i = 0
+        while time.time() < t_end:
+            for _ in range(20):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+
+    # settle and warmup, then the timed steps (the metric)
+    settle(step)
     run_steps(args.warmup, step)
     step_s, wall_step_s = run_steps(args.steps, step)
 
@@ -196,6 +213,7 @@ def main():
             part_s = step_s
         else:
             kk = lambda i: kv[i % len(kv)]   # noqa: E731
+            settle(lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
             run_steps(args.warmup, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
             part_s, _ = run_steps(args.steps, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
 
@@ -232,9 +250,10 @@ def main():
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
             "visible_tokens": [int(x) for x in w.visible_tokens],
             "kv_bytes_per_step": int(kv_bytes), "accumulate": "fp32",
-            "timing": "%d back-to-back decode steps (partial + merge), step i reads K/V pool "
+            "timing": "%d back-to-back decode steps (partial + merge) after %.0f ms of "
+                      "untimed settle steps and %d warmup steps; step i reads K/V pool "
                       "copy i mod %d (%d x %.0f MB); events on the launch stream"
-                      % (args.steps, len(kv), len(kv),
+                      % (args.steps, args.settle_ms, args.warmup, len(kv), len(kv),
                          2 * w.k_pool.nbytes / 1e6),
             "plan": plan,
         },

@@ -17,9 +17,10 @@
 //  * page kernel (rows of 256 B, i.e. L = 16: fp16 D = 128 or fp32 D = 64;
 //    G in {4, 8, 16}; page_size a multiple of the 64/G slots of one step).
 //    A wave step covers 64/G consecutive slots of ONE page, so the page id is
-//    wave-uniform: it comes from LDS into an SGPR and the load address is a
-//    scalar page base plus a per-lane offset fixed for the whole kernel (no
-//    per-token division or 64-bit multiply).  Each lane loads J = 16/G token
+//    wave-uniform: it is read with readlane from a register holding the next
+//    64 page ids of the chunk, and the load address is a scalar page base
+//    plus a per-lane offset fixed for the whole kernel (no per-token division
+//    or 64-bit multiply).  Each lane loads J = 16/G token
 //    rows; the J*G = 16 partial dot products of a 16-lane row are
 //    reduce-scattered with DPP so that lane i ends up owning the score of one
 //    (token, head) pair; the softmax then runs once per score instead of on
@@ -34,12 +35,14 @@
 //    resolves its own token through a fast divide by page_size and the page
 //    ids staged in LDS; partial dots are all-reduced inside the row with DPP.
 //
-// Epilogue: the R rows of a wave are combined with lane shuffles, the four
-// waves through LDS, and the result is either written as the chunk's partial
-// row, or -- in the fused mode -- written straight to the output when the
-// request has one chunk, else written as a partial after which the last
-// workgroup of the request (found with an agent-scope atomic counter that it
-// resets to zero) merges the request's partial rows into the output.
+// Epilogue: the R rows of a wave are combined (page kernel: a permlane
+// reduce-scatter, after which each row holds a quarter of the heads; token
+// kernel: lane shuffles), the waves that share a head through LDS, and the
+// result is either written as the chunk's partial row, or -- in the fused
+// mode -- written straight to the output when the request has one chunk, else
+// written as a partial after which the last workgroup of the request (found
+// with an agent-scope atomic counter that it resets to zero) merges the
+// request's partial rows into the output.
 
 #include <hip/hip_runtime.h>
 
@@ -53,7 +56,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPageWindow = 1024;     // page ids staged in LDS per round
+constexpr int kPageWindow = 1024;     // token kernel: page ids staged in LDS per round
 #ifndef PD_PIPELINE_DEPTH
 #define PD_PIPELINE_DEPTH 2
 #endif
@@ -637,7 +640,8 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
                 s += WPH;
             }
             if constexpr (kLockstep > 0 && NW > 1) {
-                if (rd % kLockstep == kLockstep - 1) __builtin_amdgcn_s_barrier();
+                constexpr int every = kLockstep > 0 ? kLockstep : 1;
+                if (rd % every == every - 1) __builtin_amdgcn_s_barrier();
             }
         }
     }
