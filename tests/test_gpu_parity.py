@@ -170,7 +170,7 @@ def test_batched_fp16(orc, target, mode):
 
 @pytest.mark.parametrize("target", [0, 1024, 1])
 def test_long_context_fp16_full_size(orc, target, mode):
-    """Full size; target 1 gives 2048-page chunks (several LDS page-id rounds)."""
+    """Full size; target 1 gives 2048-page chunks (32 windows of 64 page ids in the page kernel)."""
     w = cached("long_context_fp16", poison_unused=True)
     dec = run_flat(orc, w, target=target, fused=mode["fused"], repeat=2)
     if target == 1:       # one 2048-page chunk per request: written directly
