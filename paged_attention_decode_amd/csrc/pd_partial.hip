@@ -497,6 +497,23 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
     const int cp1 = min(npages, cp0 + a.pages_per_chunk);
     const int spp_log2 = a.spp_log2;
 
+    // The page ids of the chunk are taken 64 at a time, one per lane of a
+    // vector register (one load per wave; no LDS staging and no barrier), and
+    // read out per step with readlane.  The load is bounded by a buffer
+    // descriptor of the window's size: lanes past the window, and windows past
+    // the chunk, read 0 and touch no memory, so the load is unconditional.
+    auto load_ids = [&](int w0) -> int32_t {
+        // (readfirstlane keeps the clamp scalar: as a VALU med3 the descriptor
+        // would land in vector registers)
+        const int cnt = __builtin_amdgcn_readfirstlane(max(0, min(cp1 - w0, 64)));
+        const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(a.indices) + pbeg + w0, 0, cnt * 4, kBufferWord3);
+        return int32_t(__builtin_amdgcn_raw_buffer_load_b32(ri, lane * 4, 0, 0));
+    };
+    // issued before the query rows: loads complete in order, so the first K/V
+    // loads then wait for the page ids alone
+    int32_t idv = load_ids(cp0);
+
     const T *qp = static_cast<const T *>(a.q) +
                   (int64_t(r) * a.num_qo_heads + int64_t(kvh) * G) * D + li * VEC;
     Row16 qv[G];
@@ -526,12 +543,9 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
 
     const int j_own = li / G;         // the token row this lane scores
 
-    // The page ids of the chunk are taken 64 at a time, one per lane of a
-    // vector register (a single load per wave; no LDS staging and no
-    // barrier), and read out per step with readlane.
     for (int wp0 = cp0; wp0 < cp1; wp0 += 64) {
         const int wcount = min(cp1 - wp0, 64);
-        const int32_t idv = a.indices[pbeg + wp0 + min(lane, wcount - 1)];
+        const int32_t idn = load_ids(wp0 + 64);    // the next window's ids, one window ahead
         const int nsteps = wcount << spp_log2;
 
         // Loads are issued unconditionally so that the wait before each
@@ -644,6 +658,7 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
                 if (rd % every == every - 1) __builtin_amdgcn_s_barrier();
             }
         }
+        idv = idn;
     }
 
     // per-row state for every head: head h lives in lanes li = h (mod G); the
