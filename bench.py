@@ -82,6 +82,10 @@ def parse():
                         "two-launch: partial kernel then merge kernel")
     p.add_argument("--pool-copies", type=int, default=3,
                    help="independent K/V pool copies used in turn by consecutive steps")
+    p.add_argument("--cascade-members", type=int, default=4,
+                   help="cascade workload: requests sharing the prefix")
+    p.add_argument("--cascade-prefix", type=int, default=8192,
+                   help="cascade workload: shared prefix tokens")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="approximate CPU work budget of the oracle baseline")
@@ -109,20 +113,30 @@ def main():
     B.load()
     dev = torch.device("cuda:0")
     t0 = time.time()
-    w = getattr(workloads, args.workload)()
+    if args.workload == "cascade_fp16":
+        w = workloads.cascade_fp16(members=args.cascade_members, prefix_tokens=args.cascade_prefix)
+    else:
+        w = getattr(workloads, args.workload)()
     pool_pages = w.k_pool.shape[0]
     csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
                             pool_pages)
+    flat_runner = None
     if args.workload == "cascade_fp16":
-        runner = PD.CascadeDecode(w.block_tables, w.written_len,
-                                  shared_pages=w.extra["shared_pages"], page_size=w.page_size,
-                                  num_pool_pages=pool_pages, num_qo_heads=w.num_qo_heads,
-                                  num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-                                  target_wgs=args.target_wgs, device=dev)
-        plan = dict(level0=runner.level0.plan_summary(), level1=runner.level1.plan_summary())
+        # detection over the page table picks the members and the shared span
+        runner = PD.CascadeDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
+                                  num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                                  head_dim=w.head_dim, target_wgs=args.target_wgs, device=dev)
+        plan = runner.plan_summary()
         partial_only = None
-        kv_bytes = (w.extra["shared_pages"] * w.page_size + int(w.extra["suffix_tokens"].sum())) \
-            * w.num_kv_heads * w.head_dim * 2 * 2
+        row_bytes = w.num_kv_heads * w.head_dim * 2 * 2
+        span_tokens = runner.shared_pages * w.page_size if runner.active else 0
+        reads = (len(runner.subgroups) if runner.active else 0) * span_tokens + \
+            int(w.visible_tokens.sum()) - runner.member_req.size * span_tokens
+        kv_bytes = reads * row_bytes
+        # the flat decode of the same batch, timed the same way beside it
+        flat_runner = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
+                                     num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                                     head_dim=w.head_dim, target_wgs=args.target_wgs, device=dev)
     else:
         runner = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
                                 num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
@@ -217,6 +231,13 @@ def main():
             run_steps(args.warmup, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
             part_s, _ = run_steps(args.steps, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
 
+    flat_s = None
+    if flat_runner is not None:
+        fstep = lambda i: flat_runner.run(q, *kv[i % len(kv)], w.sm_scale)   # noqa: E731
+        settle(fstep)
+        run_steps(args.warmup, fstep)
+        flat_s, _ = run_steps(args.steps, fstep)
+
     # reference: one isolated step after a cache flush, bracketed by its own
     # events (includes the fixed cost of an event pair around a launch)
     iso = []
@@ -270,6 +291,14 @@ def main():
         "parity": {"max_abs_v": dv, "max_abs_lse2": dl, "tol_v": tv, "tol_lse2": tl,
                    "ok": bool(parity_ok)},
     }
+    if flat_s is not None:
+        flat_bytes = w.kv_bytes()
+        res["cascade_vs_flat"] = {
+            "cascade_step_us": round(step_s * 1e6, 2), "flat_step_us": round(flat_s * 1e6, 2),
+            "speedup": round(flat_s / step_s, 3), "cascade_kv_bytes": int(kv_bytes),
+            "flat_kv_bytes": int(flat_bytes),
+            "flat_kv_gbs": round(flat_bytes / flat_s / 1e9, 2),
+            "flat_plan": flat_runner.plan_summary()}
     if part_s is not None:
         achieved = kv_bytes / part_s / 1e9
         res["partial_us"] = round(part_s * 1e6, 2)

@@ -233,32 +233,82 @@ int paged_merge_states(const float *v_in, const float *lse_in, const int32_t *o_
                        float *v_out, float *lse_out, void *stream);
 
 /* ------------------------------------------------------------------------
- * Cascade head stacking -- cascade-attention doc, "head stacking".
+ * Cascade decode -- mlxcel cascade-attention doc.
  *
- * Level 0 attends a page span shared by `members` requests once, as one
- * request with members*G query heads per KV head.  Stacked head h0 =
- * kv*(members*G) + m*G + g holds query head kv*G + g of member m, so the
- * kernel's head-to-KV-head rule h0 / (members*G) reads KV head kv.
+ * A page span shared by several requests is attended once (level 0) instead
+ * of once per request; every request's own pages are attended per request
+ * (level 1); one merge finishes the step.
  *
- * paged_cascade_stack_q: q [members, Hq, D] (DEVICE, dtype as above) ->
- *   q0 [1, members*Hq, D] in stacked order.
- * paged_cascade_gather_states: builds the input of the cascade's single
- *   merge.  Member m's merge group starts at row m*n0 + o1[m] (o1 = the
- *   level-1 plan's o_indptr) and holds first the n0 level-0 partial rows of
- *   v0 [n0, members*Hq, D] / lse0 [n0, members*Hq] un-stacked to [Hq, D],
- *   then the member's level-1 rows from v1 [n1, Hq, D] / lse1 [n1, Hq]
- *   (level-1 chunk n, of member req1[n], goes to row (req1[n]+1)*n0 + n).
- *   v_dst [members*n0 + n1, Hq, D], lse_dst [members*n0 + n1, Hq] (fp32,
- *   DEVICE); req1 is the level-1 plan's request_indices (DEVICE).
+ * paged_cascade_detect (HOST arrays; the doc's detection section): page i
+ *   of two requests is shared when both hold the same pool row there
+ *   (positional comparison of `indices`).  Candidates are the requests with
+ *   at least one page and first_page_offset 0, grouped by their first page.
+ *   A group's span is the number of leading positions on which all members
+ *   agree, capped at (pages - 1) of every member (the last page may be
+ *   partial, level 0's pages are full).  Groups with fewer than min_members
+ *   members or a span below min_shared_pages are dropped; of the rest, the
+ *   one with the largest span * (members - 1) wins (ties: the group whose
+ *   first member comes first).  Out: member_req[0 .. *num_members) the
+ *   members in ascending request order (room for `batch`), *shared_pages the
+ *   span; *num_members = *shared_pages = 0 when nothing qualifies.
+ *   min_shared_pages >= 1 and min_members >= 2 (the doc's defaults: 16, 2).
+ *
+ * paged_cascade_split (HOST): the two levels' page tables.  Level 0 is one
+ *   request of `shared_pages` full pages: indices0 [shared_pages] (its
+ *   indptr is {0, shared_pages}, last_page_len {page_size},
+ *   first_page_offset {0}).  Level 1 keeps every request: a member keeps the
+ *   pages after the span (first_page_offset 0), a non-member its whole list;
+ *   indptr1 [batch+1], indices1 [indptr[batch] - num_members*shared_pages],
+ *   last_page_len1 / first_page_offset1 [batch].  PD_E_ARG if member_req is
+ *   not ascending, or a member starts mid-page, holds no page after the
+ *   span, or does not hold the span.
+ *
+ * paged_cascade_layout (HOST): the merge input's row layout.  Request r's
+ *   group is [o_indptr[r], o_indptr[r+1]): first its level0_rows level-0
+ *   rows when it is a member, then its level-1 rows (o_indptr1 = the level-1
+ *   plan's o_indptr).  Out: dst0 [num_members] (first row of member m's
+ *   level-0 rows), dst1 [o_indptr1[batch]] (row of level-1 chunk n),
+ *   o_indptr [batch+1].
+ *
+ * paged_cascade_stack_q (DEVICE): q [B, Hq, D] -> q0 [1, members*Hq, D];
+ *   stacked head h0 = kv*(members*G) + m*G + g holds query head kv*G + g of
+ *   request member_req[m] (member_req: DEVICE [members], or NULL for
+ *   members 0..members-1), so the kernel's head-to-KV-head rule
+ *   h0 / (members*G) reads KV head kv (the doc's head stacking; stacking
+ *   member-major instead reads the wrong KV heads).
+ *
+ * paged_cascade_gather_states (DEVICE): the merge input.  Level-0 row i
+ *   (v0 [n0, members*Hq, D], lse0 [n0, members*Hq]) is un-stacked into row
+ *   dst0[m] + i for every member m; level-1 row n (v1 [n1, Hq, D], lse1
+ *   [n1, Hq]) goes to row dst1[n].  v_dst / lse_dst [rows, Hq, D] / [rows,
+ *   Hq] fp32 with rows = o_indptr[batch] of the layout.  dst0, dst1: DEVICE
+ *   copies of the layout's arrays.  head_dim % 4 == 0 and 16-byte aligned buffers
+ *   (PD_E_UNSUPPORTED otherwise).
  * ---------------------------------------------------------------------- */
-int paged_cascade_stack_q(const void *q, int32_t dtype, int32_t members,
-                          int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                          void *q0, void *stream);
+int paged_cascade_detect(int32_t batch, const int32_t *indptr, const int32_t *indices,
+                         const int32_t *first_page_offset, int32_t min_shared_pages,
+                         int32_t min_members, int32_t *member_req, int32_t *num_members,
+                         int32_t *shared_pages);
+
+int paged_cascade_split(int32_t batch, int32_t page_size, const int32_t *indptr,
+                        const int32_t *indices, const int32_t *last_page_len,
+                        const int32_t *first_page_offset, const int32_t *member_req,
+                        int32_t num_members, int32_t shared_pages, int32_t *indices0,
+                        int32_t *indptr1, int32_t *indices1, int32_t *last_page_len1,
+                        int32_t *first_page_offset1);
+
+int paged_cascade_layout(int32_t batch, const int32_t *member_req, int32_t num_members,
+                         int32_t level0_rows, const int32_t *o_indptr1, int32_t *dst0,
+                         int32_t *dst1, int32_t *o_indptr);
+
+int paged_cascade_stack_q(const void *q, int32_t dtype, const int32_t *member_req,
+                          int32_t members, int32_t num_qo_heads, int32_t num_kv_heads,
+                          int32_t head_dim, void *q0, void *stream);
 
 int paged_cascade_gather_states(const float *v0, const float *lse0, int32_t n0,
-                                const float *v1, const float *lse1, int32_t n1,
-                                const int32_t *req1, int32_t members, int32_t num_qo_heads,
-                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t members, const int32_t *dst0, const float *v1,
+                                const float *lse1, int32_t n1, const int32_t *dst1,
+                                int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                                 float *v_dst, float *lse_dst, void *stream);
 
 /* ------------------------------------------------------------------------

@@ -24,6 +24,11 @@ Functions and the passages of the mlxcel pages they follow:
 - ``plan``: exhaustive scan over pages-per-chunk (PR #984 body item 4, the
   commit "plan + launch": largest chunk size whose workgroup count reaches the
   target, 65535-chunk launch bound, >= 1 chunk per request, request order).
+- ``cascade_detect``: brute-force search for the shared page span that
+  cascade decode attends once (cascade-attention doc, detection section:
+  positional comparison of page ids, groups by first page, span capped one
+  page short of every member's last page, requests starting mid-page left
+  out, minimum span and member count, largest span * (members - 1) wins).
 
 Every function is pinned by CPU tests in ``tests/test_oracle_*.py`` against
 closed forms, library special cases and hand-worked fixtures.
@@ -226,6 +231,25 @@ def plan(indptr, num_kv_heads: int, target: int, q_groups: int = 1,
     return dict(pages_per_chunk=c.value, num_chunks=n.value,
                 request_indices=ri[:n.value].copy(), kv_tile_indices=ti[:n.value].copy(),
                 o_indptr=oi)
+
+
+def cascade_detect(indptr, indices, first_page_offset, min_shared_pages=16, min_members=2):
+    """Brute-force cascade detection: returns (members int32 array in request
+    order, shared_pages); empty and 0 when nothing qualifies."""
+    lib = _load()
+    indptr = _i32(indptr)
+    b = indptr.size - 1
+    idx = _i32(indices) if np.asarray(indices).size else np.zeros(1, np.int32)
+    fpo = _i32(first_page_offset)
+    out = np.zeros(max(1, b), np.int32)
+    nm = ctypes.c_int32(0)
+    sp = ctypes.c_int32(0)
+    rc = lib.orc_cascade_detect(ctypes.c_int32(b), _p(indptr), _p(idx), _p(fpo),
+                                ctypes.c_int32(min_shared_pages), ctypes.c_int32(min_members),
+                                _p(out), ctypes.byref(nm), ctypes.byref(sp))
+    if rc != 0:
+        raise ValueError("oracle cascade detection failed (rc=%d)" % rc)
+    return out[:nm.value].copy(), sp.value
 
 
 def attention_dense_f64(q_rows, k_rows, v_rows, sm_scale):

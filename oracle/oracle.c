@@ -390,3 +390,70 @@ int orc_plan(int32_t batch, const int32_t *indptr, int64_t wg_per_chunk, int64_t
     *num_chunks = k;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* Cascade detection (cascade-attention doc, the detection section),   */
+/* by brute force.  Candidates: requests with at least one page whose   */
+/* window starts on a page boundary.  For every candidate a that is the */
+/* first candidate (lowest request index) holding its first page, the   */
+/* group is every candidate holding that same first page; its span is   */
+/* the number of leading positions s for which every member still has  */
+/* a page after position s (s < pages - 1) and holds at position s the  */
+/* same pool row as a.  Groups below min_members members or below       */
+/* min_shared pages are dropped; the largest span * (members - 1) wins, */
+/* the earlier leader on ties.  Nothing qualifying: 0 members, 0 span.  */
+/* ------------------------------------------------------------------ */
+static int cascade_candidate(const int32_t *indptr, const int32_t *fpo, int32_t r)
+{
+    return indptr[r + 1] - indptr[r] >= 1 && fpo[r] == 0;
+}
+
+int orc_cascade_detect(int32_t batch, const int32_t *indptr, const int32_t *indices,
+                       const int32_t *first_page_offset, int32_t min_shared_pages,
+                       int32_t min_members, int32_t *member_req, int32_t *num_members,
+                       int32_t *shared_pages)
+{
+    int64_t best_score = -1;
+    int32_t best_leader = -1, best_span = 0;
+    *num_members = 0;
+    *shared_pages = 0;
+    for (int32_t a = 0; a < batch; ++a) {
+        if (!cascade_candidate(indptr, first_page_offset, a)) continue;
+        const int32_t first = indices[indptr[a]];
+        int leads = 1;
+        for (int32_t b = 0; b < a; ++b)
+            if (cascade_candidate(indptr, first_page_offset, b) && indices[indptr[b]] == first)
+                leads = 0;
+        if (!leads) continue;
+        int32_t count = 0;
+        for (int32_t b = a; b < batch; ++b)
+            if (cascade_candidate(indptr, first_page_offset, b) && indices[indptr[b]] == first)
+                ++count;
+        int32_t span = 0;
+        for (;;) {
+            int all = 1;
+            for (int32_t b = a; b < batch && all; ++b) {
+                if (!cascade_candidate(indptr, first_page_offset, b) || indices[indptr[b]] != first)
+                    continue;
+                if (span >= indptr[b + 1] - indptr[b] - 1) all = 0;
+                else if (indices[indptr[b] + span] != indices[indptr[a] + span]) all = 0;
+            }
+            if (!all) break;
+            ++span;
+        }
+        if (count < min_members || span < min_shared_pages) continue;
+        const int64_t score = (int64_t)span * (count - 1);
+        if (score > best_score) {
+            best_score = score;
+            best_leader = a;
+            best_span = span;
+        }
+    }
+    if (best_leader < 0) return ORC_OK;
+    const int32_t first = indices[indptr[best_leader]];
+    for (int32_t b = best_leader; b < batch; ++b)
+        if (cascade_candidate(indptr, first_page_offset, b) && indices[indptr[b]] == first)
+            member_req[(*num_members)++] = b;
+    *shared_pages = best_span;
+    return ORC_OK;
+}

@@ -31,6 +31,7 @@ CODES = {v: k for k, v in ERRORS.items()}
 EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_decode_plan", "paged_decode_partial", "paged_decode_fused",
             "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
+            "paged_cascade_detect", "paged_cascade_split", "paged_cascade_layout",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
             "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
             "paged_fastdiv_eval"]
@@ -71,9 +72,13 @@ _SIGS = {
     "paged_merge_states": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
     "paged_decode_kernel_kind": (i32, [i32, i32, i32, i32, i64]),
     "paged_decode_set_kernel_choice": (i32, [i32]),
-    "paged_cascade_stack_q": (i32, [vp, i32, i32, i32, i32, i32, vp, vp]),
-    "paged_cascade_gather_states": (i32, [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, vp,
-                                          vp, vp]),
+    "paged_cascade_detect": (i32, [i32, i32p, i32p, i32p, i32, i32, i32p, i32p, i32p]),
+    "paged_cascade_split": (i32, [i32, i32, i32p, i32p, i32p, i32p, i32p, i32, i32, i32p, i32p,
+                                  i32p, i32p, i32p]),
+    "paged_cascade_layout": (i32, [i32, i32p, i32, i32, i32p, i32p, i32p, i32p]),
+    "paged_cascade_stack_q": (i32, [vp, i32, vp, i32, i32, i32, i32, vp, vp]),
+    "paged_cascade_gather_states": (i32, [vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, i32, i32,
+                                          vp, vp, vp]),
     "paged_decode_q_heads_per_wg": (i32, [i32, i32, i32]),
     "paged_decode_default_target_wgs": (i32, [i32, i32, i32, i32, i32]),
     "paged_fastdiv_eval": (i32, [i32, u32p, i64, u32p, u32p]),
@@ -242,18 +247,69 @@ def paged_merge_states(v_in, lse_in, o_indptr, num_out_rows, num_heads, head_dim
                                   _stream(stream)))
 
 
-def paged_cascade_stack_q(q, dtype, members, num_qo_heads, num_kv_heads, head_dim, q0,
-                          stream=None):
-    _check(load().paged_cascade_stack_q(_dev(q), dtype, members, num_qo_heads, num_kv_heads,
-                                        head_dim, _dev(q0), _stream(stream)))
+def paged_cascade_detect(indptr, indices, first_page_offset, min_shared_pages=16,
+                         min_members=2):
+    """Returns (member_req int32 array, shared_pages); empty / 0 if nothing
+    qualifies."""
+    indptr = _host_i32(indptr)
+    batch = indptr.size - 1
+    indices = _host_i32(indices if np.asarray(indices).size else np.zeros(1, np.int32))
+    fpo = _host_i32(first_page_offset)
+    members = np.zeros(max(1, batch), np.int32)
+    nm, sp = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().paged_cascade_detect(batch, _hp(indptr), _hp(indices), _hp(fpo),
+                                       min_shared_pages, min_members, _hp(members),
+                                       ctypes.byref(nm), ctypes.byref(sp)))
+    return members[:nm.value].copy(), sp.value
 
 
-def paged_cascade_gather_states(v0, lse0, n0, v1, lse1, n1, req1, members, num_qo_heads,
+def paged_cascade_split(page_size, indptr, indices, last_page_len, first_page_offset,
+                        member_req, shared_pages):
+    """Returns (indices0, csr1) with csr1 a dict of the level-1 page table."""
+    indptr = _host_i32(indptr)
+    batch = indptr.size - 1
+    indices = _host_i32(indices)
+    member_req = _host_i32(member_req)
+    nnz1 = int(indptr[-1]) - member_req.size * shared_pages
+    indices0 = np.zeros(max(1, shared_pages), np.int32)
+    indptr1 = np.zeros(batch + 1, np.int32)
+    indices1 = np.zeros(max(1, nnz1), np.int32)
+    lpl1 = np.zeros(batch, np.int32)
+    fpo1 = np.zeros(batch, np.int32)
+    _check(load().paged_cascade_split(batch, page_size, _hp(indptr), _hp(indices),
+                                      _hp(_host_i32(last_page_len)),
+                                      _hp(_host_i32(first_page_offset)), _hp(member_req),
+                                      member_req.size, shared_pages, _hp(indices0), _hp(indptr1),
+                                      _hp(indices1), _hp(lpl1), _hp(fpo1)))
+    return indices0[:shared_pages].copy(), dict(indptr=indptr1, indices=indices1[:max(0, nnz1)],
+                                                last_page_len=lpl1, first_page_offset=fpo1)
+
+
+def paged_cascade_layout(member_req, level0_rows, o_indptr1):
+    """Returns (dst0, dst1, o_indptr) of the cascade merge input."""
+    member_req = _host_i32(member_req)
+    o1 = _host_i32(o_indptr1)
+    batch = o1.size - 1
+    dst0 = np.zeros(max(1, member_req.size), np.int32)
+    dst1 = np.zeros(max(1, int(o1[-1])), np.int32)
+    oi = np.zeros(batch + 1, np.int32)
+    _check(load().paged_cascade_layout(batch, _hp(member_req), member_req.size, level0_rows,
+                                       _hp(o1), _hp(dst0), _hp(dst1), _hp(oi)))
+    return dst0[:member_req.size].copy(), dst1[:int(o1[-1])].copy(), oi
+
+
+def paged_cascade_stack_q(q, dtype, member_req, members, num_qo_heads, num_kv_heads, head_dim,
+                          q0, stream=None):
+    _check(load().paged_cascade_stack_q(_dev(q), dtype, _dev(member_req), members, num_qo_heads,
+                                        num_kv_heads, head_dim, _dev(q0), _stream(stream)))
+
+
+def paged_cascade_gather_states(v0, lse0, n0, members, dst0, v1, lse1, n1, dst1, num_qo_heads,
                                 num_kv_heads, head_dim, v_dst, lse_dst, stream=None):
-    _check(load().paged_cascade_gather_states(_dev(v0), _dev(lse0), n0, _dev(v1), _dev(lse1), n1,
-                                              _dev(req1), members, num_qo_heads, num_kv_heads,
-                                              head_dim, _dev(v_dst), _dev(lse_dst),
-                                              _stream(stream)))
+    _check(load().paged_cascade_gather_states(_dev(v0), _dev(lse0), n0, members, _dev(dst0),
+                                              _dev(v1), _dev(lse1), n1, _dev(dst1),
+                                              num_qo_heads, num_kv_heads, head_dim, _dev(v_dst),
+                                              _dev(lse_dst), _stream(stream)))
 
 
 def paged_decode_q_heads_per_wg(group_size, head_dim, dtype):

@@ -127,63 +127,120 @@ class PagedDecode:
 
 
 class CascadeDecode:
-    """Cascade decode for `members` requests that share their first
-    `shared_pages` pages (cascade-attention doc): level 0 attends the shared
-    span once with stacked heads, level 1 attends each member's suffix, and
-    one merge pairs every member's level-0 and level-1 states."""
+    """Cascade decode of one batch (cascade-attention doc).
 
-    def __init__(self, block_tables, written_len, *, shared_pages: int, page_size: int,
-                 num_pool_pages: int, num_qo_heads: int, num_kv_heads: int, head_dim: int,
-                 target_wgs: int = 0, target_wgs_level0: int = 0, device="cuda"):
-        m = len(block_tables)
-        self.members = m
+    Detection over the page table (``paged_cascade_detect``) picks the
+    requests that share leading pages and the shared span, unless members and
+    shared_pages are given.  Level 0 attends the span once per subgroup of
+    members with their query heads stacked (a launch stacks at most 16 query
+    heads per KV head, so M*G > 16 splits the members into subgroups that each
+    read the span); level 1 attends every request's own pages -- the members'
+    pages after the span and the other requests' whole lists; one merge over
+    the host-computed layout finishes every request.  With no qualifying span
+    the step is the flat decode.
+    """
+
+    def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
+                 num_kv_heads: int, head_dim: int, members=None, shared_pages: int = 0,
+                 min_shared_pages: int = 16, min_members: int = 2, target_wgs: int = 0,
+                 target_wgs_level0: int = 0, dtype=torch.float16, device="cuda"):
+        indptr = np.asarray(csr["indptr"], np.int32)
+        indices = np.asarray(csr["indices"], np.int32)
+        lpl = np.asarray(csr["last_page_len"], np.int32)
+        fpo = np.asarray(csr["first_page_offset"], np.int32)
+        self.batch = indptr.size - 1
         self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
-        prefix = np.asarray(block_tables[0][:shared_pages], np.int32)
-        for t in block_tables:
-            if not np.array_equal(np.asarray(t[:shared_pages]), prefix):
-                raise ValueError("members do not share the span")
-        wl = np.asarray(written_len, np.int64)
-        if np.any(wl < shared_pages * page_size):
-            raise ValueError("every member must hold the whole shared span")
-        csr0 = B.paged_csr_build([prefix], [0], [shared_pages * page_size], page_size,
-                                 num_pool_pages)
-        suffix = [np.asarray(t[shared_pages:], np.int32) for t in block_tables]
-        csr1 = B.paged_csr_build(suffix, [0] * m, (wl - shared_pages * page_size).astype(np.int32),
-                                 page_size, num_pool_pages)
-        self.level0 = PagedDecode(csr0, page_size=page_size, num_pool_pages=num_pool_pages,
-                                  num_qo_heads=m * num_qo_heads, num_kv_heads=num_kv_heads,
-                                  head_dim=head_dim,
-                                  target_wgs=target_wgs_level0 or target_wgs, device=device)
-        self.level1 = PagedDecode(csr1, page_size=page_size, num_pool_pages=num_pool_pages,
-                                  num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
-                                  head_dim=head_dim, target_wgs=target_wgs, device=device)
-        n0 = self.level0.info.num_chunks
-        n1 = self.level1.info.num_chunks
-        o1 = self.level1.o_indptr
-        oi = np.array([k * n0 + o1[k] for k in range(m + 1)], np.int32)
-        self.n0, self.n1 = n0, n1
-        dev = self.level0.device
-        self.d_oindptr = _dev_i32(oi, dev)
-        self.q0 = None
-        self.v_cat = torch.empty((m * n0 + n1, num_qo_heads, head_dim), dtype=torch.float32,
-                                 device=dev)
-        self.lse_cat = torch.empty((m * n0 + n1, num_qo_heads), dtype=torch.float32, device=dev)
-        self.out = torch.empty((m, num_qo_heads, head_dim), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((m, num_qo_heads), dtype=torch.float32, device=dev)
+        B.csr_validate(self.batch, page_size, num_pool_pages, indptr, indices, lpl, fpo,
+                       csr.get("seq_lens"))
+        if members is None:
+            members, shared_pages = B.paged_cascade_detect(indptr, indices, fpo,
+                                                           min_shared_pages, min_members)
+        self.member_req = np.asarray(members, np.int32)
+        self.shared_pages = int(shared_pages)
+        self.device = torch.device(device)
+        kw = dict(page_size=page_size, num_pool_pages=num_pool_pages, num_kv_heads=num_kv_heads,
+                  head_dim=head_dim, dtype=dtype, device=device)
+        self.flat = None
+        if self.member_req.size == 0 or self.shared_pages == 0:
+            self.flat = PagedDecode(csr, num_qo_heads=num_qo_heads, target_wgs=target_wgs, **kw)
+            self.out, self.lse = self.flat.out, self.flat.lse
+            return
+        idx0, csr1 = B.paged_cascade_split(page_size, indptr, indices, lpl, fpo, self.member_req,
+                                           self.shared_pages)
+        csr0 = dict(indptr=np.array([0, self.shared_pages], np.int32), indices=idx0,
+                    last_page_len=np.array([page_size], np.int32),
+                    first_page_offset=np.array([0], np.int32))
+        # subgroups of members whose stacked group size a launch supports
+        g = num_qo_heads // num_kv_heads
+        pd_dtype = B.PD_DTYPE_FP32 if dtype == torch.float32 else B.PD_DTYPE_FP16
+        per = 1
+        for k in range(1, self.member_req.size + 1):
+            if k * g <= 16 and B.load().paged_decode_q_heads_per_wg(k * g, head_dim, pd_dtype) > 0:
+                per = k
+        self.subgroups = [self.member_req[i:i + per] for i in range(0, self.member_req.size, per)]
+        self.level0 = []
+        fixed = 0
+        for sub in self.subgroups:
+            lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads,
+                             target_wgs=target_wgs_level0 or target_wgs,
+                             fixed_pages_per_chunk=fixed, **kw)
+            fixed = fixed or lv.info.pages_per_chunk      # one level-0 chunking for all
+            self.level0.append(lv)
+        self.level1 = PagedDecode(csr1, num_qo_heads=num_qo_heads, target_wgs=target_wgs, **kw)
+        self.n0 = self.level0[0].info.num_chunks
+        self.n1 = self.level1.info.num_chunks
+        dst0, dst1, oi = B.paged_cascade_layout(self.member_req, self.n0, self.level1.o_indptr)
+        self.o_indptr = oi
+        self.d_oindptr = _dev_i32(oi, self.device)
+        self.d_dst1 = _dev_i32(dst1 if dst1.size else np.zeros(1, np.int32), self.device)
+        self.d_members, self.d_dst0 = [], []
+        pos = 0
+        for sub in self.subgroups:
+            self.d_members.append(_dev_i32(sub, self.device))
+            self.d_dst0.append(_dev_i32(dst0[pos:pos + sub.size], self.device))
+            pos += sub.size
+        rows = int(oi[-1])
+        self.q0 = [None] * len(self.subgroups)
+        self.v_cat = torch.empty((rows, num_qo_heads, head_dim), dtype=torch.float32,
+                                 device=self.device)
+        self.lse_cat = torch.empty((rows, num_qo_heads), dtype=torch.float32, device=self.device)
+        self.out = torch.empty((self.batch, num_qo_heads, head_dim), dtype=torch.float32,
+                               device=self.device)
+        self.lse = torch.empty((self.batch, num_qo_heads), dtype=torch.float32,
+                               device=self.device)
+
+    @property
+    def active(self) -> bool:
+        return self.flat is None
+
+    def plan_summary(self) -> dict:
+        if self.flat is not None:
+            return dict(cascade=False, flat=self.flat.plan_summary())
+        return dict(cascade=True, members=[int(x) for x in self.member_req],
+                    shared_pages=self.shared_pages, subgroups=len(self.subgroups),
+                    level0=self.level0[0].plan_summary(), level1=self.level1.plan_summary())
 
     def run(self, q, k_pool, v_pool, sm_scale, stream=None):
-        m, hq, d = self.members, self.num_qo_heads, self.head_dim
-        if self.q0 is None or self.q0.dtype != q.dtype:
-            self.q0 = torch.empty((1, m * hq, d), dtype=q.dtype, device=q.device)
-        B.paged_cascade_stack_q(q, _pd_dtype(q), m, hq, self.num_kv_heads, d, self.q0, stream)
-        self.level0.partial(self.q0, k_pool, v_pool, sm_scale, stream)
+        """One decode step: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32)."""
+        if self.flat is not None:
+            return self.flat.run(q, k_pool, v_pool, sm_scale, stream)
+        hq, d, hkv = self.num_qo_heads, self.head_dim, self.num_kv_heads
+        for j, sub in enumerate(self.subgroups):
+            if self.q0[j] is None or self.q0[j].dtype != q.dtype:
+                self.q0[j] = torch.empty((1, sub.size * hq, d), dtype=q.dtype, device=q.device)
+            B.paged_cascade_stack_q(q, _pd_dtype(q), self.d_members[j], sub.size, hq, hkv, d,
+                                    self.q0[j], stream)
+            self.level0[j].partial(self.q0[j], k_pool, v_pool, sm_scale, stream)
         self.level1.partial(q, k_pool, v_pool, sm_scale, stream)
-        B.paged_cascade_gather_states(self.level0.v_partial, self.level0.lse_partial, self.n0,
-                                      self.level1.v_partial, self.level1.lse_partial, self.n1,
-                                      self.level1.d_req, m, hq, self.num_kv_heads, d,
-                                      self.v_cat, self.lse_cat, stream)
-        B.paged_merge_states(self.v_cat, self.lse_cat, self.d_oindptr, m, hq, d, self.out,
-                             self.lse, stream)
+        for j, sub in enumerate(self.subgroups):
+            last = j == len(self.subgroups) - 1       # the last call also moves level 1
+            B.paged_cascade_gather_states(
+                self.level0[j].v_partial, self.level0[j].lse_partial, self.n0, sub.size,
+                self.d_dst0[j], self.level1.v_partial if last else None,
+                self.level1.lse_partial if last else None, self.n1 if last else 0,
+                self.d_dst1 if last else None, hq, hkv, d, self.v_cat, self.lse_cat, stream)
+        B.paged_merge_states(self.v_cat, self.lse_cat, self.d_oindptr, self.batch, hq, d,
+                             self.out, self.lse, stream)
         return self.out, self.lse
 
 

@@ -209,24 +209,35 @@ def test_token_sparse_page_size_one(orc):
     check_close(out, lse, ref_v, ref_l, workloads.FP16, "sparse final")
 
 
+def _cascade(w, **kw):
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            w.k_pool.shape[0])
+    return PD.CascadeDecode(csr, page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                            num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                            head_dim=w.head_dim, **kw)
+
+
+def _oracle_flat(orc, w):
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    return orc.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                         nthreads=NTHREADS)
+
+
 def test_cascade_matches_flat_and_oracle(orc):
     w = workloads.cascade_fp16(poison_unused=True)
     flat = run_flat(orc, w, target=0, check_partials=False)
     sp = w.extra["shared_pages"]
-    say("case cascade members=%d shared_pages=%d suffix=%s" % (
-        w.batch, sp, list(w.extra["suffix_tokens"])))
-    cas = PD.CascadeDecode(w.block_tables, w.written_len, shared_pages=sp,
-                           page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
-                           num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
-                           head_dim=w.head_dim)
-    say("  level0", cas.level0.plan_summary(), "level1", cas.level1.plan_summary())
+    cas = _cascade(w)
+    say("case cascade members=%d shared_pages=%d suffix=%s plan=%s" % (
+        w.batch, sp, list(w.extra["suffix_tokens"]), cas.plan_summary()))
+    # detection finds the whole batch sharing the 8192-token prefix
+    assert cas.active and list(cas.member_req) == list(range(w.batch))
+    assert cas.shared_pages == sp and len(cas.subgroups) == 1
     q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
     out, lse = cas.run(q, k, v, w.sm_scale)
     torch.cuda.synchronize()
-    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
-                                     w.page_size)
-    ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
-                                 nthreads=NTHREADS)
+    ref_v, ref_l = _oracle_flat(orc, w)
     check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "cascade")
     fo, fl = flat.run(q, k, v, w.sm_scale)
     torch.cuda.synchronize()
@@ -234,26 +245,91 @@ def test_cascade_matches_flat_and_oracle(orc):
                 fl.cpu().numpy().astype(np.float64), w.dtype, "cascade-vs-flat")
 
 
+def _mixed_batch(seed, members, hq=32, hkv=8, prefix_pages=40, ps=16):
+    """A batch in which `members` requests share a prefix of pages, one more
+    request holds the same pages but starts mid-page (so detection leaves it
+    out), and two unrelated requests hold their own pages."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_other = 3
+    suf = rng.integers(1, 9, size=members + n_other)
+    live = prefix_pages + int(suf.sum()) + 2 * prefix_pages
+    pool = 2 * live
+    perm = rng.permutation(pool).astype(np.int32)
+    prefix = perm[:prefix_pages]
+    pos = prefix_pages
+    tables, ls, wl = [], [], []
+    for i in range(members + 1):
+        tail = perm[pos:pos + suf[i]]
+        pos += suf[i]
+        tables.append(np.concatenate([prefix, tail]))
+        n_tok = (prefix_pages + suf[i] - 1) * ps + int(rng.integers(1, ps + 1))
+        start = 5 if i == members else 0                  # the mid-page window
+        ls.append(start)
+        wl.append(n_tok)
+    for i in range(2):
+        own = perm[pos:pos + prefix_pages]
+        pos += prefix_pages
+        tables.append(own)
+        ls.append(0)
+        wl.append(prefix_pages * ps - 3)
+    q = rng.standard_normal((len(tables), hq, 128), dtype=np.float32).astype(np.float16)
+    k = rng.standard_normal((pool, ps, hkv, 128), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((pool, ps, hkv, 128), dtype=np.float32).astype(np.float16)
+    w = workloads.Workload(name="mixed_cascade", dtype=workloads.FP16, page_size=ps,
+                           num_qo_heads=hq, num_kv_heads=hkv, head_dim=128,
+                           sm_scale=1.0 / np.sqrt(128), q=q, k_pool=k, v_pool=v,
+                           block_tables=tables, logical_start=np.array(ls, np.int32),
+                           written_len=np.array(wl, np.int32))
+    return workloads.poison_invisible(w)
+
+
+@pytest.mark.parametrize("members,hq", [(3, 32), (6, 32), (5, 16)])
+def test_cascade_mixed_batch_and_subgroups(orc, members, hq):
+    """Members, a mid-page window over the same pages, and unrelated requests in
+    one batch; with G = 4 and 6 members the level-0 heads split into two
+    stacked launches (16 + 8 query heads per KV head)."""
+    w = _mixed_batch(80 + members, members, hq=hq)
+    cas = _cascade(w, min_shared_pages=16)
+    say("case mixed cascade members=%d hq=%d plan=%s" % (members, hq, cas.plan_summary()))
+    assert cas.active and list(cas.member_req) == list(range(members))
+    assert cas.shared_pages == 40
+    g = hq // w.num_kv_heads
+    assert all(sub.size * g <= 16 for sub in cas.subgroups)
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    out, lse = cas.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ref_v, ref_l = _oracle_flat(orc, w)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "mixed cascade")
+
+
+def test_cascade_without_sharing_is_flat(orc):
+    w = workloads.batched_fp16(poison_unused=True)
+    cas = _cascade(w)
+    assert not cas.active
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    out, lse = cas.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ref_v, ref_l = _oracle_flat(orc, w)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "no-share cascade")
+
+
 def test_cascade_member_major_stacking_is_wrong(orc):
     """Negative control: stacking heads member-major (a plain reshape) launches
     fine and reads the wrong KV heads, so it must not match."""
     w = workloads.cascade_fp16(seed=6, prefix_tokens=1024, suffix_lo=64, suffix_hi=128)
-    sp = w.extra["shared_pages"]
-    cas = PD.CascadeDecode(w.block_tables, w.written_len, shared_pages=sp,
-                           page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
-                           num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
-                           head_dim=w.head_dim)
+    cas = _cascade(w)
+    assert cas.active and len(cas.subgroups) == 1
     q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
     good, _ = cas.run(q, k, v, w.sm_scale)
     good = good.cpu().numpy().copy()
     wrong_q0 = q.reshape(1, -1, w.head_dim).contiguous()        # member-major
-    cas.level0.partial(wrong_q0, k, v, w.sm_scale)
+    cas.level0[0].partial(wrong_q0, k, v, w.sm_scale)
     cas.level1.partial(q, k, v, w.sm_scale)
-    B.paged_cascade_gather_states(cas.level0.v_partial, cas.level0.lse_partial, cas.n0,
-                                  cas.level1.v_partial, cas.level1.lse_partial, cas.n1,
-                                  cas.level1.d_req, cas.members, w.num_qo_heads,
+    B.paged_cascade_gather_states(cas.level0[0].v_partial, cas.level0[0].lse_partial, cas.n0,
+                                  cas.member_req.size, cas.d_dst0[0], cas.level1.v_partial,
+                                  cas.level1.lse_partial, cas.n1, cas.d_dst1, w.num_qo_heads,
                                   w.num_kv_heads, w.head_dim, cas.v_cat, cas.lse_cat)
-    B.paged_merge_states(cas.v_cat, cas.lse_cat, cas.d_oindptr, cas.members, w.num_qo_heads,
+    B.paged_merge_states(cas.v_cat, cas.lse_cat, cas.d_oindptr, w.batch, w.num_qo_heads,
                          w.head_dim, cas.out, cas.lse)
     torch.cuda.synchronize()
     bad = cas.out.cpu().numpy()
