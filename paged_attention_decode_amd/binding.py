@@ -235,8 +235,10 @@ def paged_decode_kernel_kind(dtype, head_dim, group_size, page_size, token_strid
                                                          token_stride))
 
 
-def paged_decode_set_kernel_choice(force_token_kernel):
-    _check(load().paged_decode_set_kernel_choice(1 if force_token_kernel else 0))
+def paged_decode_set_kernel_choice(choice):
+    """0 (or False): default choice; 1 (or True): every shape on the token
+    kernel; 2: no MFMA kernel (VALU page or token kernel)."""
+    _check(load().paged_decode_set_kernel_choice(int(choice)))
 
 
 def paged_merge_states(v_in, lse_in, o_indptr, num_out_rows, num_heads, head_dim, v_out,

@@ -959,6 +959,289 @@ constexpr int token_rows_per_step()
     return G <= 4 ? 4 : (G <= 8 ? 2 : 1);
 }
 
+// ----------------------------------------------------------------- MFMA kernel
+// For large query groups (G >= 8) the scores and the value sum are real
+// dense products.  A tile of 16 tokens of one KV head against the group's
+// queries is S^T [16 tokens x 16 heads] = K [16 x 128] . Q^T [128 x 16]:
+// four v_mfma_f32_16x16x32_f16.  The value sum is taken transposed,
+// O^T [16 dims x 16 heads] += V^T [16 dims x 16 tokens] . P^T [16 tokens x
+// 16 heads]: one v_mfma_f32_16x16x16_f16 per 16 dims.
+//
+// Lane layouts of the 16x16xK products (checked on gfx950): A [M x K] --
+// lane l holds row l%16, k = (K/4)*(l/16) + e; B [K x N] -- lane l holds
+// column l%16, the same k; C [M x N] -- lane l holds column l%16, rows
+// 4*(l/16) + i.  With S^T in C layout, lane l holds head l%16 for tokens
+// 4*(l/16) + i: that is P^T's B layout for the value product, and O^T's C
+// layout puts the same head in lane l.  So a lane owns one head's running
+// max and sum and 32 of its output dims, and a rescale is a per-lane scalar.
+//
+// K rows go straight from memory into the A operand (lane l: token l%16, 16
+// bytes at dims 8*(l/16) + 32*kc).  V^T's A operand (4 tokens of one dim per
+// lane) is read from an LDS copy of the V tile with the gfx950 transpose
+// read ds_read_b64_tr_b16: in each 16-lane group, lanes 4r..4r+3 name 4
+// consecutive halves each (together row r of a 4 x 16 tile) and lane c
+// receives column c.  Each wave has its own LDS tile, rows padded by 16
+// bytes against bank conflicts.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per V row of the tile
+
+// max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float group_max4(float x)
+{
+    float a = x, b = x;
+    swap16(a, b);
+    x = fmaxf(a, b);
+    a = x;
+    b = x;
+    swap32(a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float group_sum4(float x)
+{
+    float a = x, b = x;
+    swap16(a, b);
+    x = a + b;
+    a = x;
+    b = x;
+    swap32(a, b);
+    return a + b;
+}
+
+template <int G, int HPW>
+__global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
+{
+    constexpr int HT = (G + 15) / 16;   // 16-head tiles
+    constexpr int D = 128;
+    constexpr int ESZ = 2;
+    static_assert(G >= 8 && G <= 32, "group");
+
+    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+
+    const int groups = a.num_kv_heads / HPW;
+    const int wg = blockIdx.x;
+    const int n = wg / groups;
+    const int kvg = wg - n * groups;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kvh = kvg * HPW + wave;
+    const int lane = tid & 63;
+    const int grp = lane >> 4;          // 16-lane group
+    const int col = lane & 15;          // head of a tile (C / B layouts) or token (A layout)
+
+    const int r = ld_uniform(a.req_idx + n);
+    const int t = ld_uniform(a.tile_idx + n);
+    const int pbeg = ld_uniform(a.indptr + r);
+    const int npages = ld_uniform(a.indptr + r + 1) - pbeg;
+    const int fpo = ld_uniform(a.fpo + r);
+    const int lpl = ld_uniform(a.lpl + r);
+    const int ps = a.page_size;
+    const int cp0 = t * a.pages_per_chunk;
+    const int cp1 = min(npages, cp0 + a.pages_per_chunk);
+    const int spp_log2 = a.spp_log2;    // 16-token tiles per page = 2^spp_log2
+
+    auto load_ids = [&](int w0) -> int32_t {
+        const int cnt = __builtin_amdgcn_readfirstlane(max(0, min(cp1 - w0, 64)));
+        const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(a.indices) + pbeg + w0, 0, cnt * 4, kBufferWord3);
+        return int32_t(__builtin_amdgcn_raw_buffer_load_b32(ri, lane * 4, 0, 0));
+    };
+    int32_t idv = load_ids(cp0);
+
+    // Q^T as the B operand of the score product: lane l holds head
+    // 16*ht + l%16 (zero past G) at dims 32*kc + 8*(l/16) .. + 7
+    half8_t qb[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int h = ht * 16 + col;
+        const _Float16 *qp = static_cast<const _Float16 *>(a.q) +
+                             (int64_t(r) * a.num_qo_heads + int64_t(kvh) * G + min(h, G - 1)) * D +
+                             8 * grp;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * kc);
+            qb[ht][kc] = h < G ? __builtin_bit_cast(half8_t, u) : half8_t{};
+        }
+    }
+
+    const char *kb = static_cast<const char *>(a.k) + int64_t(kvh) * a.head_stride * ESZ;
+    const char *vb = static_cast<const char *>(a.v) + int64_t(kvh) * a.head_stride * ESZ;
+    const int64_t page_bytes = a.page_stride * ESZ;
+    const int32_t tsb = int32_t(a.token_stride * ESZ);
+    const uint32_t tile_bytes = uint32_t(tsb) * 16u;
+    const int32_t page_span = int32_t(int64_t(ps - 1) * a.token_stride * ESZ + D * ESZ);
+    // K: lane l reads token l%16 at dims 8*(l/16) + 32*kc; V: lane l reads
+    // row l/16 + 4*j at bytes 16*(l%16) (16 lanes per whole row)
+    const int32_t k_off = col * tsb + 16 * grp;
+    const int32_t v_off = grp * tsb + 16 * col;
+
+    // per 16-head tile: the lane's head's running max and its share of the sum
+    float m_run[HT], l_part[HT];
+    float4_t acc[HT][8];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        m_run[ht] = kNoMax;
+        l_part[ht] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    char *vt = s_v[wave];
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    // transpose-read address of dim tile dt: row 4*(l/16) + (l%16)/4, halves
+    // 16*dt + 4*(l%4)
+    const int tr_off = (4 * grp + (col >> 2)) * kMfmaRowBytes + 8 * (lane & 3);
+
+    for (int wp0 = cp0; wp0 < cp1; wp0 += 64) {
+        const int wcount = min(cp1 - wp0, 64);
+        const int32_t idn = load_ids(wp0 + 64);    // the next window's ids, one window ahead
+        const int nsteps = wcount << spp_log2;
+
+        auto load = [&](int s, uint4 (&kr)[4], uint4 (&vr)[4]) {
+            const bool live = s < nsteps;
+            const int p = min(s >> spp_log2, wcount - 1);
+            const int sub = s & ((1 << spp_log2) - 1);
+            const int pid = __builtin_amdgcn_readlane(idv, p);
+            const int64_t base = int64_t(pid) * page_bytes;
+            const int32_t span = live ? page_span : 0;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(kb + base), 0, span, kBufferWord3);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char *>(vb + base), 0, span, kBufferWord3);
+            const int soff = int(sub * tile_bytes);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * j, soff, kLoadNT));
+                vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + 4 * j * tsb, soff, kLoadNT));
+            }
+        };
+
+        auto compute = [&](int s, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+            const int p = wp0 + (s >> spp_log2);          // request-relative page
+            const int slot0 = (s & ((1 << spp_log2) - 1)) * 16;
+            const bool edge = (p == 0 && fpo > 0) || (p == npages - 1 && lpl < ps);
+            const int lo = p == 0 ? fpo : 0;
+            const int hi_slot = p == npages - 1 ? lpl : ps;
+            // V tile -> this wave's LDS rows (tokens outside the visible range
+            // as zeros: whatever they hold never reaches the sum)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint4 v = vr[j];
+                if (edge) {
+                    const int slot = slot0 + grp + 4 * j;
+                    const bool ok = slot >= lo && slot < hi_slot;
+                    v.x = ok ? v.x : 0u;
+                    v.y = ok ? v.y : 0u;
+                    v.z = ok ? v.z : 0u;
+                    v.w = ok ? v.w : 0u;
+                }
+                *reinterpret_cast<uint4 *>(vt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = v;
+            }
+            // scores S^T = K . Q^T, per 16-head tile
+            float4_t sc[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                sc[ht] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+                    sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(half8_t, kr[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
+            }
+            // the V rows written above are read back below by the same wave:
+            // LDS operations of a wave complete in order, so only the
+            // compiler must keep them in order
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            half4_t vtr[8];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                vtr[dt] = __builtin_bit_cast(
+                    half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                 (lds_short4 *)(vt + tr_off + 32 * dt)));
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                float x[4];
+                float mb = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = sc[ht][i] * a.scale_log2;
+                    if (edge) {
+                        const int slot = slot0 + 4 * grp + i;
+                        v = (slot >= lo && slot < hi_slot) ? v : -INFINITY;
+                    }
+                    x[i] = v;
+                    mb = fmaxf(mb, v);
+                }
+                mb = group_max4(mb);                       // over the tile's 16 tokens
+                const bool need = mb > m_run[ht] + kLazyMargin;
+                if (__builtin_amdgcn_ballot_w64(need)) {
+                    const float m_new = need ? mb : m_run[ht];
+                    const float alpha = fast_exp2(m_run[ht] - m_new);
+                    m_run[ht] = m_new;
+                    l_part[ht] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) acc[ht][dt] *= alpha;
+                }
+                half4_t pb;
+                float ls = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const _Float16 ph = _Float16(fast_exp2(x[i] - m_run[ht]));
+                    pb[i] = ph;
+                    ls += float(ph);        // the sum takes the weights the products use
+                }
+                l_part[ht] += ls;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vtr[dt], pb, acc[ht][dt],
+                                                                        0, 0, 0);
+            }
+        };
+
+        uint4 kbuf[kDepth][4], vbuf[kDepth][4];
+        int s = 0;
+#pragma unroll
+        for (int d = 0; d < kDepth - 1; ++d) load(s + d, kbuf[d], vbuf[d]);
+        const int rounds = (nsteps + kDepth - 1) / kDepth;
+        for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+            for (int u = 0; u < kDepth; ++u) {
+                load(s + kDepth - 1, kbuf[(u + kDepth - 1) % kDepth], vbuf[(u + kDepth - 1) % kDepth]);
+                if (s < nsteps) compute(s, kbuf[u], vbuf[u]);
+                ++s;
+            }
+            if constexpr (kLockstep > 0 && HPW > 1) {
+                constexpr int every = kLockstep > 0 ? kLockstep : 1;
+                if (rd % every == every - 1) __builtin_amdgcn_s_barrier();
+            }
+        }
+        idv = idn;
+    }
+
+    // per head: the sum over the four 16-lane groups; each group holds 4 of
+    // every 16 dims, so the accumulators need no combine
+    const int hq = a.num_qo_heads;
+    float *vrow = a.v_out + int64_t(n) * hq * D;
+    float *lrow = a.lse_out + int64_t(n) * hq;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const float l = group_sum4(l_part[ht]);
+        const int h = ht * 16 + col;
+        if (h >= G) continue;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int64_t qh = int64_t(kvh) * G + h;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const float4_t o = acc[ht][dt] * inv;
+            *reinterpret_cast<float4 *>(vrow + qh * D + 16 * dt + 4 * grp) =
+                make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (grp == 0) lrow[qh] = l > 0.f ? m_run[ht] + fast_log2(l) : -INFINITY;
+    }
+}
+
 template <typename T, int D, bool FUSED>
 KernelFn pick_token(int g)
 {
@@ -1019,16 +1302,62 @@ struct Choice {
     int spp_log2;
     int heads_per_wg;   // KV heads one workgroup covers
     int threads;
+    int kind;           // 0 token kernel, 1 page kernel, 2 MFMA kernel
 };
 
-// The page kernel serves 256-byte rows, G in {4, 8, 16}, and page sizes that
-// are a power-of-two multiple of its 64/G slots per step with 32-bit lane
-// offsets; every other shape takes the token kernel.
-Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
-            bool allow_page = true, int hkv = 1)
+template <int G>
+KernelFn pick_mfma_shape(int hpw)
 {
-    Choice c{nullptr, 0, 1, kThreads};
+    switch (hpw) {
+    case 8: return partial_mfma_kernel<G, 8>;
+    case 4: return partial_mfma_kernel<G, 4>;
+    case 2: return partial_mfma_kernel<G, 2>;
+    default: return partial_mfma_kernel<G, 1>;
+    }
+}
+
+KernelFn pick_mfma(int g, int hpw)
+{
+    switch (g) {
+    case 8: return pick_mfma_shape<8>(hpw);
+    case 12: return pick_mfma_shape<12>(hpw);
+    case 16: return pick_mfma_shape<16>(hpw);
+    case 32: return pick_mfma_shape<32>(hpw);
+    default: return nullptr;
+    }
+}
+
+// The MFMA kernel serves fp16 with D = 128, G in {8, 12, 16, 32} and page
+// sizes that are a power-of-two multiple of 16 (two-launch mode); the page
+// kernel 256-byte rows, G in {4, 8, 16}, and page sizes that are a
+// power-of-two multiple of its 64/G slots per step; every other shape takes
+// the token kernel.  All need 32-bit in-page offsets.
+Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
+            bool allow_page = true, int hkv = 1, bool allow_mfma = true)
+{
+    Choice c{nullptr, 0, 1, kThreads, 0};
     const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
+    if (allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 && d == 128 &&
+        (g == 8 || g == 12 || g == 16 || g == 32) && page_size % 16 == 0 &&
+        token_stride * esz * page_size < (int64_t(1) << 31)) {
+        const int tiles = page_size / 16;
+        if ((tiles & (tiles - 1)) == 0) {
+            int lg = 0;
+            while ((1 << lg) < tiles) ++lg;
+            int hpw = 1;
+            for (int h = 8; h > 1; h >>= 1)
+                if (hkv % h == 0) {
+                    hpw = h;
+                    break;
+                }
+            c.fn = pick_mfma(g, hpw);
+            c.spp_log2 = lg;
+            c.heads_per_wg = hpw;
+            c.threads = 64 * hpw;
+            c.kind = 2;
+            return c;
+        }
+    }
     const bool row256 = (dtype == PD_DTYPE_FP16 && d == 128) || (dtype == PD_DTYPE_FP32 && d == 64);
     if (allow_page && row256 && (g == 4 || g == 8 || g == 16)) {
         const int sps = 64 / g;
@@ -1041,6 +1370,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
                 const int hpw = page_heads_per_wg(hkv, g);
                 c.heads_per_wg = hpw;
                 c.threads = page_threads(hpw);
+                c.kind = 1;
                 if (dtype == PD_DTYPE_FP16) c.fn = fused ? pick_page<_Float16, true>(g, hpw) : pick_page<_Float16, false>(g, hpw);
                 else c.fn = fused ? pick_page<float, true>(g, hpw) : pick_page<float, false>(g, hpw);
                 return c;
@@ -1126,7 +1456,9 @@ int launch(const Choice &c, const PartialArgs &a, int32_t num_chunks, void *stre
     return PD_OK;
 }
 
-int g_force_token_kernel = 0;   // testing hook: route every shape to the token kernel
+// kernel choice hook: 0 default, 1 every shape to the token kernel, 2 no MFMA kernel
+int g_force_token_kernel = 0;
+int g_no_mfma = 0;
 
 }  // namespace
 }  // namespace pd
@@ -1155,7 +1487,7 @@ extern "C" int paged_decode_partial(const void *q, const void *k_pool, const voi
                             who);
     if (rc) return rc;
     const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
-                          false, !g_force_token_kernel, num_kv_heads);
+                          false, !g_force_token_kernel, num_kv_heads, !g_no_mfma);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_partial: no kernel for this (dtype, D, group)");
     if (num_chunks == 0) return PD_OK;
     return launch(c, a, num_chunks, stream, who);
@@ -1192,9 +1524,11 @@ extern "C" int paged_decode_fused(const void *q, const void *k_pool, const void 
     return launch(c, a, num_chunks, stream, who);
 }
 
-extern "C" int paged_decode_set_kernel_choice(int32_t force_token_kernel)
+extern "C" int paged_decode_set_kernel_choice(int32_t choice)
 {
-    g_force_token_kernel = force_token_kernel != 0;
+    if (choice < 0 || choice > 2) return fail(PD_E_ARG, "paged_decode_set_kernel_choice: 0, 1 or 2");
+    g_force_token_kernel = choice == 1;
+    g_no_mfma = choice == 2;
     return PD_OK;
 }
 
@@ -1202,10 +1536,9 @@ extern "C" int paged_decode_kernel_kind(int32_t dtype, int32_t head_dim, int32_t
                                         int32_t page_size, int64_t token_stride)
 {
     const Choice c = pick(dtype, head_dim, group_size, page_size, token_stride, false,
-                          !g_force_token_kernel);
+                          !g_force_token_kernel, 1, !g_no_mfma);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_kernel_kind: unsupported shape");
-    const Choice t = pick(dtype, head_dim, group_size, page_size, token_stride, false, false);
-    return c.fn == t.fn ? 0 : 1;   // 0 token kernel, 1 page kernel
+    return c.kind;   // 0 token kernel, 1 page kernel, 2 MFMA kernel
 }
 
 extern "C" int paged_decode_default_target_wgs(int32_t device, int32_t group_size,
@@ -1215,7 +1548,7 @@ extern "C" int paged_decode_default_target_wgs(int32_t device, int32_t group_siz
     if (num_kv_heads < 1)
         return fail(PD_E_ARG, "paged_decode_default_target_wgs: num_kv_heads must be >= 1");
     const Choice c = pick(dtype, head_dim, group_size, 16, int64_t(num_kv_heads) * head_dim,
-                          false, !g_force_token_kernel, num_kv_heads);
+                          false, !g_force_token_kernel, num_kv_heads, !g_no_mfma);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_default_target_wgs: unsupported shape");
     int dev = device;
     if (dev < 0 && hipGetDevice(&dev) != hipSuccess)

@@ -72,16 +72,21 @@ def cached(name, **kw):
     return _WORKLOADS[key]
 
 
-MODES = [("auto", False), ("auto", True), ("token", False), ("token", True)]
-MODE_IDS = ["page-2launch", "page-fused", "token-2launch", "token-fused"]
+# "auto" takes the default kernel (the MFMA kernel where it applies in the
+# two-launch mode), "valu" every shape off the MFMA kernel, "token" every
+# shape on the token kernel
+MODES = [("auto", False), ("auto", True), ("token", False), ("token", True), ("valu", False)]
+MODE_IDS = ["page-2launch", "page-fused", "token-2launch", "token-fused", "valu-2launch"]
+CHOICE = {"auto": 0, "token": 1, "valu": 2}
+KIND = {0: "token", 1: "page", 2: "mfma"}
 
 
 @pytest.fixture(params=MODES, ids=MODE_IDS)
 def mode(request):
     kernel, fused = request.param
-    B.paged_decode_set_kernel_choice(kernel == "token")
+    B.paged_decode_set_kernel_choice(CHOICE[kernel])
     yield dict(fused=fused, kernel=kernel)
-    B.paged_decode_set_kernel_choice(False)
+    B.paged_decode_set_kernel_choice(0)
 
 
 def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None, fused=False,
@@ -107,7 +112,7 @@ def run_flat(orc, w, target=0, fixed=0, check_partials=True, stream=None, fused=
                                       B.PD_DTYPE_FP32, w.head_dim,
                                       w.num_qo_heads // w.num_kv_heads, w.page_size,
                                       w.k_pool.shape[2] * w.head_dim)
-    say("  plan", dec.plan_summary(), "kernel", "page" if kind else "token")
+    say("  plan", dec.plan_summary(), "kernel", "fused-" if fused else "", KIND[kind])
     oplan = orc.plan(ocsr["indptr"], w.num_kv_heads, info.target_wgs,
                      fixed_pages_per_chunk=fixed)
     assert oplan["pages_per_chunk"] == info.pages_per_chunk
@@ -364,12 +369,37 @@ def test_page_kernel_shapes_ragged(orc, g, ps, mode):
     run_flat(orc, w, target=48, fused=mode["fused"])
 
 
+@pytest.mark.parametrize("g", [8, 12, 16, 32])
+@pytest.mark.parametrize("ps,hkv", [(16, 8), (32, 2), (64, 1)])
+def test_mfma_kernel_ragged(orc, g, ps, hkv):
+    """The MFMA kernel over ragged windows, mid-page starts, partial last
+    pages, empty requests and NaN-poisoned pools, at each group size and
+    workgroup shape (8, 2 or 1 KV heads per workgroup)."""
+    w = workloads.random_geometry(300 + g + ps, batch=6, page_size=ps, max_len=2500,
+                                  num_qo_heads=g * hkv, num_kv_heads=hkv, p_empty=0.15,
+                                  p_trim=0.5)
+    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, 128, g, ps, hkv * 128) == 2
+    for target, fixed in ((0, 0), (64, 0), (0, 1)):
+        run_flat(orc, w, target=target, fixed=fixed)
+
+
 def test_kernel_choice():
     kk = B.paged_decode_kernel_kind
     assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1024) == 1
-    assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 1
-    assert kk(B.PD_DTYPE_FP16, 128, 16, 16, 1024) == 1
+    assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 2    # MFMA from G = 8
+    assert kk(B.PD_DTYPE_FP16, 128, 12, 32, 1024) == 2
+    assert kk(B.PD_DTYPE_FP16, 128, 16, 16, 1024) == 2
+    assert kk(B.PD_DTYPE_FP16, 128, 32, 64, 1024) == 2
+    assert kk(B.PD_DTYPE_FP16, 128, 16, 4, 1024) == 1    # page smaller than an MFMA tile
+    assert kk(B.PD_DTYPE_FP16, 128, 8, 48, 1024) == 0    # 3 MFMA tiles per page
+    assert kk(B.PD_DTYPE_FP32, 64, 16, 16, 128) == 1
     assert kk(B.PD_DTYPE_FP32, 64, 4, 16, 128) == 1
+    B.paged_decode_set_kernel_choice(2)
+    try:
+        assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 1
+        assert kk(B.PD_DTYPE_FP16, 128, 12, 16, 1024) == 0
+    finally:
+        B.paged_decode_set_kernel_choice(0)
     assert kk(B.PD_DTYPE_FP16, 128, 4, 8, 1024) == 0     # page smaller than a step
     assert kk(B.PD_DTYPE_FP16, 128, 12, 1, 128) == 0     # token-sparse page_size 1
     assert kk(B.PD_DTYPE_FP16, 64, 4, 16, 512) == 0      # 128-byte rows
@@ -417,8 +447,10 @@ def test_many_pages_per_chunk_cross_lds_window(orc):
 
 @pytest.mark.parametrize("dtype", [workloads.FP16, workloads.FP32])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("g", [1, 2, 4, 8, 12, 16])
+@pytest.mark.parametrize("g", [1, 2, 4, 8, 12, 16, 32])
 def test_group_and_head_dim_variants(orc, dtype, d, g):
+    if g == 32 and (dtype != workloads.FP16 or d != 128):
+        pytest.skip("G = 32 runs on the MFMA kernel only (fp16, D = 128)")
     hkv = 2
     w = workloads.random_geometry(70 + g + d, batch=3, page_size=16, max_len=900, dtype=dtype,
                                   num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d)
