@@ -226,10 +226,11 @@ int64_t fit_target(int32_t batch, const int32_t *indptr, int64_t wg_per_chunk, i
 
 extern "C" int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dtype)
 {
-    // G = 32 only on the MFMA kernel: fp16, head dim 128
+    // G = 24 and 32 only on the MFMA kernel: fp16, head dim 128
     const bool g_ok = group_size == 1 || group_size == 2 || group_size == 4 ||
                       group_size == 8 || group_size == 12 || group_size == 16 ||
-                      (group_size == 32 && dtype == PD_DTYPE_FP16 && head_dim == 128);
+                      ((group_size == 24 || group_size == 32) && dtype == PD_DTYPE_FP16 &&
+                       head_dim == 128);
     const bool d_ok = head_dim == 64 || head_dim == 128;
     const bool t_ok = dtype == PD_DTYPE_FP16 || dtype == PD_DTYPE_FP32;
     if (!g_ok || !d_ok || !t_ok)

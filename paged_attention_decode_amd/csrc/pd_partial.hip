@@ -1322,12 +1322,13 @@ KernelFn pick_mfma(int g, int hpw)
     case 8: return pick_mfma_shape<8>(hpw);
     case 12: return pick_mfma_shape<12>(hpw);
     case 16: return pick_mfma_shape<16>(hpw);
+    case 24: return pick_mfma_shape<24>(hpw);
     case 32: return pick_mfma_shape<32>(hpw);
     default: return nullptr;
     }
 }
 
-// The MFMA kernel serves fp16 with D = 128, G in {8, 12, 16, 32} and page
+// The MFMA kernel serves fp16 with D = 128, G in {8, 12, 16, 24, 32} and page
 // sizes that are a power-of-two multiple of 16 (two-launch mode); the page
 // kernel 256-byte rows, G in {4, 8, 16}, and page sizes that are a
 // power-of-two multiple of its 64/G slots per step; every other shape takes
@@ -1338,7 +1339,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
     Choice c{nullptr, 0, 1, kThreads, 0};
     const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
     if (allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 && d == 128 &&
-        (g == 8 || g == 12 || g == 16 || g == 32) && page_size % 16 == 0 &&
+        (g == 8 || g == 12 || g == 16 || g == 24 || g == 32) && page_size % 16 == 0 &&
         token_stride * esz * page_size < (int64_t(1) << 31)) {
         const int tiles = page_size / 16;
         if ((tiles & (tiles - 1)) == 0) {

@@ -132,9 +132,9 @@ class CascadeDecode:
     Detection over the page table (``paged_cascade_detect``) picks the
     requests that share leading pages and the shared span, unless members and
     shared_pages are given.  Level 0 attends the span once per subgroup of
-    members with their query heads stacked (a launch stacks at most 16 query
-    heads per KV head, so M*G > 16 splits the members into subgroups that each
-    read the span); level 1 attends every request's own pages -- the members'
+    members with their query heads stacked (a launch stacks at most 32 query
+    heads per KV head, 16 off the MFMA kernel, so a larger M*G splits the
+    members into subgroups that each read the span); level 1 attends every request's own pages -- the members'
     pages after the span and the other requests' whole lists; one merge over
     the host-computed layout finishes every request.  With no qualifying span
     the step is the flat decode.
@@ -175,7 +175,7 @@ class CascadeDecode:
         pd_dtype = B.PD_DTYPE_FP32 if dtype == torch.float32 else B.PD_DTYPE_FP16
         per = 1
         for k in range(1, self.member_req.size + 1):
-            if k * g <= 16 and B.load().paged_decode_q_heads_per_wg(k * g, head_dim, pd_dtype) > 0:
+            if B.load().paged_decode_q_heads_per_wg(k * g, head_dim, pd_dtype) > 0:
                 per = k
         self.subgroups = [self.member_req[i:i + per] for i in range(0, self.member_req.size, per)]
         self.level0 = []

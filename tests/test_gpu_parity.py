@@ -288,18 +288,19 @@ def _mixed_batch(seed, members, hq=32, hkv=8, prefix_pages=40, ps=16):
     return workloads.poison_invisible(w)
 
 
-@pytest.mark.parametrize("members,hq", [(3, 32), (6, 32), (5, 16)])
+@pytest.mark.parametrize("members,hq", [(3, 32), (6, 32), (5, 16), (9, 32)])
 def test_cascade_mixed_batch_and_subgroups(orc, members, hq):
     """Members, a mid-page window over the same pages, and unrelated requests in
-    one batch; with G = 4 and 6 members the level-0 heads split into two
-    stacked launches (16 + 8 query heads per KV head)."""
+    one batch.  Stacked groups of 12 and 24 query heads per KV head run on the
+    MFMA kernel; 9 members at G = 4 split into launches of 8 + 1 members (32 + 4
+    heads), 5 members at G = 2 into 4 + 1 (8 + 2)."""
     w = _mixed_batch(80 + members, members, hq=hq)
     cas = _cascade(w, min_shared_pages=16)
     say("case mixed cascade members=%d hq=%d plan=%s" % (members, hq, cas.plan_summary()))
     assert cas.active and list(cas.member_req) == list(range(members))
     assert cas.shared_pages == 40
     g = hq // w.num_kv_heads
-    assert all(sub.size * g <= 16 for sub in cas.subgroups)
+    assert all(sub.size * g <= 32 for sub in cas.subgroups)
     q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
     out, lse = cas.run(q, k, v, w.sm_scale)
     torch.cuda.synchronize()
@@ -369,7 +370,7 @@ def test_page_kernel_shapes_ragged(orc, g, ps, mode):
     run_flat(orc, w, target=48, fused=mode["fused"])
 
 
-@pytest.mark.parametrize("g", [8, 12, 16, 32])
+@pytest.mark.parametrize("g", [8, 12, 16, 24, 32])
 @pytest.mark.parametrize("ps,hkv", [(16, 8), (32, 2), (64, 1)])
 def test_mfma_kernel_ragged(orc, g, ps, hkv):
     """The MFMA kernel over ragged windows, mid-page starts, partial last

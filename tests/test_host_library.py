@@ -187,9 +187,13 @@ def test_q_heads_per_wg_and_unsupported(lib):
         for d in (64, 128):
             for dt in (0, 1):
                 assert B.paged_decode_q_heads_per_wg(g, d, dt) == g
-    for g, d in ((3, 128), (4, 96), (32, 128)):
+    # 24 and 32 heads per KV head run on the MFMA kernel only: fp16, D = 128
+    for g in (24, 32):
+        assert B.paged_decode_q_heads_per_wg(g, 128, 0) == g
+    for g, d, dt in ((3, 128, 0), (4, 96, 0), (32, 128, 1), (32, 64, 0), (24, 128, 1), (20, 128, 0),
+                     (64, 128, 0)):
         with pytest.raises(B.PagedDecodeError) as ei:
-            B.paged_decode_q_heads_per_wg(g, d, 0)
+            B.paged_decode_q_heads_per_wg(g, d, dt)
         assert ei.value.name == "PD_E_UNSUPPORTED"
 
 
