@@ -86,6 +86,11 @@ def parse():
                    help="cascade workload: requests sharing the prefix")
     p.add_argument("--cascade-prefix", type=int, default=8192,
                    help="cascade workload: shared prefix tokens")
+    p.add_argument("--group-size", type=int, default=4,
+                   help="long_context_fp16: query heads per KV head (8 KV heads; the metric "
+                        "config is 4)")
+    p.add_argument("--kernel-choice", type=int, default=0, choices=[0, 1, 2],
+                   help="0 default kernels, 1 token kernel only, 2 no MFMA kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="approximate CPU work budget of the oracle baseline")
@@ -111,10 +116,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     B.load()
+    B.paged_decode_set_kernel_choice(args.kernel_choice)
     dev = torch.device("cuda:0")
     t0 = time.time()
     if args.workload == "cascade_fp16":
         w = workloads.cascade_fp16(members=args.cascade_members, prefix_tokens=args.cascade_prefix)
+    elif args.workload == "long_context_fp16":
+        w = workloads.long_context_fp16(num_qo_heads=8 * args.group_size)
     else:
         w = getattr(workloads, args.workload)()
     pool_pages = w.k_pool.shape[0]
@@ -303,10 +311,18 @@ def main():
         achieved = kv_bytes / part_s / 1e9
         res["partial_us"] = round(part_s * 1e6, 2)
         res["merge_and_gap_us"] = round((step_s - part_s) * 1e6, 2)
+        # the committed counter summary covers the default long-context run only
+        default_run = (args.workload == "long_context_fp16" and args.group_size == 4 and
+                       args.kernel_choice == 0)
+        kind = B.paged_decode_kernel_kind(B.PD_DTYPE_FP16 if w.dtype == workloads.FP16 else
+                                          B.PD_DTYPE_FP32, w.head_dim,
+                                          w.num_qo_heads // w.num_kv_heads, w.page_size,
+                                          w.k_pool.shape[2] * w.head_dim)
         res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
-                           "traffic": counter_traffic(),
+                           "traffic": counter_traffic() if default_run else None,
+                           "kernel_kind": {0: "token", 1: "page", 2: "mfma"}[kind],
                            "kernel": "paged_decode_partial", "kernel_sha": kernel_sha(),
                            "bytes_per_launch": int(kv_bytes)}
 
