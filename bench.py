@@ -74,7 +74,8 @@ def parse():
                    help="untimed steps run for this long before the warmup steps of each "
                         "timed region (the GPU takes a few ms to leave its idle state)")
     p.add_argument("--workload", default="long_context_fp16",
-                   choices=["long_context_fp16", "batched_fp16", "tiny_fp32", "cascade_fp16"])
+                   choices=["long_context_fp16", "batched_fp16", "tiny_fp32", "cascade_fp16",
+                            "token_sparse_fp16", "block_sparse_fp16"])
     p.add_argument("--target-wgs", type=int, default=0, help="plan target (0: device default)")
     p.add_argument("--fixed-pages-per-chunk", type=int, default=0)
     p.add_argument("--mode", default="two-launch", choices=["fused", "two-launch"],
@@ -118,9 +119,14 @@ def main():
     B.load()
     B.paged_decode_set_kernel_choice(args.kernel_choice)
     dev = torch.device("cuda:0")
+    if args.workload == "block_sparse_fp16":
+        return block_sparse(args, torch, B, PD, workloads, dev)
     t0 = time.time()
     if args.workload == "cascade_fp16":
         w = workloads.cascade_fp16(members=args.cascade_members, prefix_tokens=args.cascade_prefix)
+    elif args.workload == "token_sparse_fp16":
+        # the selection read through a page_size-1 table, one request per KV head
+        w = workloads.folded_sparse(workloads.token_sparse_fp16())
     elif args.workload == "long_context_fp16":
         w = workloads.long_context_fp16(num_qo_heads=8 * args.group_size)
     else:
@@ -351,6 +357,98 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = int(src.numel() * 2)
 
+    print(json.dumps(res), flush=True)
+
+
+def block_sparse(args, torch, B, PD, workloads, dev):
+    """Block-sparse decode (a selection of KV blocks per KV head): the
+    block-granular page table timed beside the token-exact one."""
+    import oracle
+    w = workloads.block_sparse_fp16()
+    b, hkv, cap, d = w.k_dense.shape
+    hq = w.q.shape[1]
+    kd = torch.from_numpy(w.k_dense).to(dev)
+    vd = torch.from_numpy(w.v_dense).to(dev)
+    q = torch.from_numpy(w.q).to(dev)
+    ids = torch.from_numpy(w.block_ids).to(dev)
+    runners = {exact: PD.BlockSparseDecode(kd, vd, num_qo_heads=hq, block_size=w.block_size,
+                                           blocks_per_request=w.block_ids.shape[1],
+                                           kv_len=w.kv_len, token_exact=exact,
+                                           target_wgs=args.target_wgs, device=dev)
+               for exact in (False, True)}
+    # parity of both granularities against attention over the selected positions
+    g = hq // hkv
+    t0 = time.time()
+    ref_v = np.zeros((b, hq, d))
+    ref_l = np.zeros((b, hq))
+    pos = [oracle.block_positions(w.block_ids[h], w.block_size, w.kv_len[0]) for h in range(hkv)]
+    for i in range(hq):
+        h = i // g
+        ref_v[0, i], ref_l[0, i] = oracle.attention_dense_f64(w.q[0, i], w.k_dense[0, h, pos[h]],
+                                                              w.v_dense[0, h, pos[h]], w.sm_scale)
+    oracle_s = time.time() - t0
+    worst = (0.0, 0.0)
+    for r in runners.values():
+        out, lse = r.run(q, ids, w.sm_scale)
+        torch.cuda.synchronize()
+        dv = float(np.max(np.abs(out.cpu().numpy() - ref_v)))
+        dl = float(np.max(np.abs(lse.cpu().numpy() - ref_l)))
+        worst = (max(worst[0], dv), max(worst[1], dl))
+    if not (worst[0] <= 2e-3 and worst[1] <= 1e-3):
+        print(json.dumps({"error": "parity failed", "max_abs_v": worst[0], "max_abs_lse": worst[1]}))
+        sys.exit(1)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        t_end = time.time() + args.settle_ms * 1e-3
+        while time.time() < t_end:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / args.steps
+
+    t_block = timed(lambda: runners[False].run(q, ids, w.sm_scale))
+    t_token = timed(lambda: runners[True].run(q, ids, w.sm_scale))
+    tokens = sum(len(p) for p in pos)
+    kv_bytes = tokens * d * 2 * 2
+    value = kv_bytes / t_block / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_block * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, random distinct blocks plus the final block)",
+        "config": {"workload": w.name, "batch": b, "num_qo_heads": hq, "num_kv_heads": hkv,
+                   "head_dim": d, "block_size": w.block_size,
+                   "blocks_per_kv_head": int(w.block_ids.shape[1]), "kv_len": int(w.kv_len[0]),
+                   "selected_positions": int(tokens), "kv_bytes_per_step": int(kv_bytes),
+                   "timing": "%d back-to-back steps (block-id expansion + partial + merge) "
+                             "after %.0f ms of settle steps; K/V resident (fits the last-level "
+                             "cache)" % (args.steps, args.settle_ms),
+                   "plan": runners[False].plan_summary()},
+        "step_us": round(t_block * 1e6, 2),
+        "block_vs_token": {"block_granular_step_us": round(t_block * 1e6, 2),
+                           "token_exact_step_us": round(t_token * 1e6, 2),
+                           "speedup": round(t_token / t_block, 3),
+                           "token_exact_plan": runners[True].plan_summary()},
+        "parity": {"max_abs_v": worst[0], "max_abs_lse2": worst[1], "tol_v": 2e-3,
+                   "tol_lse2": 1e-3, "ok": True},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = {"value": round(kv_bytes / oracle_s / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "the whole step (%d selected positions x %d KV heads),"
+                                         " f64 dense-position oracle, one run, %.3f s"
+                                         % (tokens // hkv, hkv, oracle_s),
+                               "cpu_model": cpu_model()}
     print(json.dumps(res), flush=True)
 
 

@@ -312,6 +312,43 @@ int paged_cascade_gather_states(const float *v0, const float *lse0, int32_t n0,
                                 float *v_dst, float *lse_dst, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Block selections -- mlxcel "Sparse paged decode" doc (the two page-table
+ * granularities and the block-to-token expansion).
+ *
+ * A sparse-attention model selects, per request (one per (sequence, KV head)
+ * after folding), blocks_per_request blocks of block_size positions; the
+ * request's last listed block is its final, partially written block and holds
+ * tail[r] in [1, block_size] positions.
+ *
+ * paged_sparse_csr (HOST): the page table's shape, which needs no selection
+ *   values.  token_exact = 1: page_size 1, request r holds (blocks-1)*block_size
+ *   + tail[r] one-token pages (last_page_len 1).  token_exact = 0
+ *   (block-granular): page_size = block_size, request r holds `blocks` pages,
+ *   last_page_len = tail[r].  first_page_offset 0.  Out: indptr [R+1],
+ *   last_page_len [R], first_page_offset [R].
+ *
+ * paged_sparse_expand_blocks (DEVICE arrays, caller's stream): one pass over
+ *   the selection.  Block j of request r (block_ids [R, blocks], int32)
+ *   becomes rows base[r] + id*span + t for t < span, written from
+ *   rows[out_indptr[r] + j*span]; the last block writes only tail[r] rows.
+ *   span = block_size gives token rows (token_exact tables, the pool read as
+ *   one-token pages); span = 1 gives page ids of block-granular tables (a pool
+ *   whose rows are blocks, row of block j of request r = base[r] + j).
+ *   Block ids must lie in [0, num_blocks); an id outside is clamped into it,
+ *   so the rows never leave the request's region of the pool.
+ *   base, tail [R]; out_indptr [R+1] (the table's indptr); rows
+ *   [out_indptr[R]].
+ * ---------------------------------------------------------------------- */
+int paged_sparse_csr(int32_t num_requests, int32_t blocks_per_request, int32_t block_size,
+                     int32_t token_exact, const int32_t *tail, int32_t *indptr,
+                     int32_t *last_page_len, int32_t *first_page_offset);
+
+int paged_sparse_expand_blocks(const int32_t *block_ids, int32_t num_requests,
+                               int32_t blocks_per_request, const int32_t *base, int32_t span,
+                               const int32_t *tail, const int32_t *out_indptr,
+                               int32_t num_blocks, int32_t *rows, void *stream);
+
+/* ------------------------------------------------------------------------
  * Helpers shared by the plan and the launcher, so the two cannot drift
  * (PR #984 kernel commit: the query-heads-per-workgroup and wave-count
  * helpers exported next to the kernels).

@@ -24,6 +24,8 @@ Functions and the passages of the mlxcel pages they follow:
 - ``plan``: exhaustive scan over pages-per-chunk (PR #984 body item 4, the
   commit "plan + launch": largest chunk size whose workgroup count reaches the
   target, 65535-chunk launch bound, >= 1 chunk per request, request order).
+- ``block_positions``: the positions a selection of KV blocks covers
+  (sparse-paged-decode doc, selection from blocks).
 - ``cascade_detect``: brute-force search for the shared page span that
   cascade decode attends once (cascade-attention doc, detection section:
   positional comparison of page ids, groups by first page, span capped one
@@ -250,6 +252,17 @@ def cascade_detect(indptr, indices, first_page_offset, min_shared_pages=16, min_
     if rc != 0:
         raise ValueError("oracle cascade detection failed (rc=%d)" % rc)
     return out[:nm.value].copy(), sp.value
+
+
+def block_positions(block_ids, block_size: int, kv_len: int):
+    """Positions a list of selected blocks covers: block j holds positions
+    [j*C, (j+1)*C), and nothing at or past the live length kv_len
+    (sparse-paged-decode doc, selection from blocks)."""
+    out = []
+    for j in np.asarray(block_ids, np.int64):
+        lo = int(j) * block_size
+        out.extend(range(lo, min(lo + block_size, int(kv_len))))
+    return np.asarray(out, np.int64)
 
 
 def attention_dense_f64(q_rows, k_rows, v_rows, sm_scale):

@@ -33,6 +33,7 @@ EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
             "paged_cascade_detect", "paged_cascade_split", "paged_cascade_layout",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
+            "paged_sparse_csr", "paged_sparse_expand_blocks",
             "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
             "paged_fastdiv_eval"]
 
@@ -79,6 +80,8 @@ _SIGS = {
     "paged_cascade_stack_q": (i32, [vp, i32, vp, i32, i32, i32, i32, vp, vp]),
     "paged_cascade_gather_states": (i32, [vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, i32, i32,
                                           vp, vp, vp]),
+    "paged_sparse_csr": (i32, [i32, i32, i32, i32, i32p, i32p, i32p, i32p]),
+    "paged_sparse_expand_blocks": (i32, [vp, i32, i32, vp, i32, vp, vp, i32, vp, vp]),
     "paged_decode_q_heads_per_wg": (i32, [i32, i32, i32]),
     "paged_decode_default_target_wgs": (i32, [i32, i32, i32, i32, i32]),
     "paged_fastdiv_eval": (i32, [i32, u32p, i64, u32p, u32p]),
@@ -312,6 +315,26 @@ def paged_cascade_gather_states(v0, lse0, n0, members, dst0, v1, lse1, n1, dst1,
                                               _dev(v1), _dev(lse1), n1, _dev(dst1),
                                               num_qo_heads, num_kv_heads, head_dim, _dev(v_dst),
                                               _dev(lse_dst), _stream(stream)))
+
+
+def paged_sparse_csr(blocks_per_request, block_size, tail, token_exact):
+    """Returns dict(indptr, last_page_len, first_page_offset) of a selection's
+    page table (host arrays)."""
+    tail = _host_i32(tail)
+    r = tail.size
+    indptr = np.zeros(r + 1, np.int32)
+    lpl = np.zeros(r, np.int32)
+    fpo = np.zeros(r, np.int32)
+    _check(load().paged_sparse_csr(r, blocks_per_request, block_size, 1 if token_exact else 0,
+                                   _hp(tail), _hp(indptr), _hp(lpl), _hp(fpo)))
+    return dict(indptr=indptr, last_page_len=lpl, first_page_offset=fpo)
+
+
+def paged_sparse_expand_blocks(block_ids, num_requests, blocks_per_request, base, span, tail,
+                               out_indptr, num_blocks, rows, stream=None):
+    _check(load().paged_sparse_expand_blocks(_dev(block_ids), num_requests, blocks_per_request,
+                                             _dev(base), span, _dev(tail), _dev(out_indptr),
+                                             num_blocks, _dev(rows), _stream(stream)))
 
 
 def paged_decode_q_heads_per_wg(group_size, head_dim, dtype):

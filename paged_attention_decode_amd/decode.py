@@ -269,3 +269,86 @@ def sparse_block_tables(positions, cap: int, batch: int = 1):
     del batch
     return [(r * cap + np.asarray(pos, np.int64)).astype(np.int32)
             for r, pos in enumerate(positions)]
+
+
+class BlockSparseDecode:
+    """Decode over a selection of KV blocks per (sequence, KV head) on a dense
+    [B, Hkv, Cap, D] allocation (sparse-paged-decode doc: the two page-table
+    granularities).
+
+    Every (sequence, KV head) is one request of the page table, holding its
+    query heads i // G == h (the ContiguousCacheLayout folding).  Each request
+    lists `blocks_per_request` block ids, its partially written final block
+    last; that block holds kv_len - final*block_size positions.
+
+    token_exact=False (block-granular): the allocation is read as a pool of
+    Cap/block_size-row blocks (page_size = block_size, needs Cap % block_size
+    == 0) and the block ids, offset by the request's region, are the page ids.
+    token_exact=True: the allocation is read as one-token pages and the block
+    ids are expanded into token rows.  Either way the ids are a device value
+    turned into the table's rows by one device pass per step; the table's
+    shape depends only on the selection size, so nothing is read back.
+    """
+
+    def __init__(self, k_dense, v_dense, *, num_qo_heads: int, block_size: int,
+                 blocks_per_request: int, kv_len, token_exact: bool = False,
+                 target_wgs: int = 0, device="cuda"):
+        b, hkv, cap, d = k_dense.shape
+        if v_dense.shape != k_dense.shape or not k_dense.is_contiguous() or \
+                not v_dense.is_contiguous():
+            raise ValueError("K and V allocations must be contiguous and of one shape")
+        if num_qo_heads % hkv:
+            raise ValueError("query heads must be a multiple of KV heads")
+        if not token_exact and cap % block_size:
+            raise ValueError("block-granular pages need Cap % block_size == 0")
+        kv_len = np.broadcast_to(np.asarray(kv_len, np.int64), (b,))
+        if np.any(kv_len < 1) or np.any(kv_len > cap):
+            raise ValueError("kv_len must be in [1, Cap]")
+        self.batch, self.num_kv_heads, self.num_qo_heads, self.head_dim = b, hkv, num_qo_heads, d
+        self.requests = b * hkv
+        self.blocks = blocks_per_request
+        self.block_size = block_size
+        self.token_exact = token_exact
+        final = (kv_len - 1) // block_size
+        tail = np.repeat((kv_len - final * block_size).astype(np.int32), hkv)
+        csr = B.paged_sparse_csr(blocks_per_request, block_size, tail, token_exact)
+        nnz = int(csr["indptr"][-1])
+        if token_exact:
+            self.page_size, self.span = 1, block_size
+            self.k_pool = k_dense.view(b * hkv * cap, 1, 1, d)
+            self.v_pool = v_dense.view(b * hkv * cap, 1, 1, d)
+            base = np.arange(self.requests, dtype=np.int64) * cap
+        else:
+            self.page_size, self.span = block_size, 1
+            self.k_pool = k_dense.view(b * hkv * cap // block_size, block_size, 1, d)
+            self.v_pool = v_dense.view(b * hkv * cap // block_size, block_size, 1, d)
+            base = np.arange(self.requests, dtype=np.int64) * (cap // block_size)
+        self.num_blocks = cap // block_size
+        # the table's rows are written on the device every step; placeholder
+        # rows (valid pool rows) let the host check the table's shape now
+        csr["indices"] = np.zeros(max(1, nnz), np.int32)[:nnz]
+        self.dec = PagedDecode(csr, page_size=self.page_size,
+                               num_pool_pages=self.k_pool.shape[0],
+                               num_qo_heads=num_qo_heads // hkv, num_kv_heads=1, head_dim=d,
+                               target_wgs=target_wgs, device=device)
+        dev = self.dec.device
+        self.d_base = _dev_i32(base.astype(np.int32), dev)
+        self.d_tail = _dev_i32(tail, dev)
+
+    def plan_summary(self) -> dict:
+        return dict(self.dec.plan_summary(), page_size=self.page_size,
+                    token_exact=self.token_exact)
+
+    def run(self, q, block_ids, sm_scale, stream=None):
+        """q [B, Hq, D]; block_ids [B*Hkv, blocks_per_request] int32 on the
+        device.  Returns (out [B, Hq, D], lse [B, Hq]) fp32, log2 LSE."""
+        if block_ids.dtype != torch.int32 or block_ids.numel() != self.requests * self.blocks:
+            raise ValueError("block_ids must be int32 [B*Hkv, blocks_per_request]")
+        B.paged_sparse_expand_blocks(block_ids, self.requests, self.blocks, self.d_base,
+                                     self.span, self.d_tail, self.dec.d_indptr,
+                                     self.num_blocks, self.dec.d_indices, stream)
+        qf = q.reshape(self.requests, self.num_qo_heads // self.num_kv_heads, self.head_dim)
+        out, lse = self.dec.run(qf, self.k_pool, self.v_pool, sm_scale, stream)
+        return (out.view(self.batch, self.num_qo_heads, self.head_dim),
+                lse.view(self.batch, self.num_qo_heads))
+

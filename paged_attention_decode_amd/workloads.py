@@ -243,6 +243,63 @@ def token_sparse_fp16(seed=4, cap=131072, topk=2048, hq=24, hkv=2, d=128):
                           sm_scale=1.0 / np.sqrt(d))
 
 
+def folded_sparse(s: SparseWorkload, name="token_sparse_fp16") -> Workload:
+    """The same selection laid out as a page_size-1 paged workload: the
+    dense [1, Hkv, Cap, D] allocation read as a pool of Hkv*Cap one-token
+    pages with one KV head, one request per KV head holding its selected
+    rows, and the query [1, Hq, 1, D] read as [Hkv, Hq/Hkv, D] (query head i
+    under KV head i // (Hq/Hkv)).  Pure relayout: no values change."""
+    _, hkv, cap, d = s.k_dense.shape
+    hq = s.q.shape[1]
+    k = s.k_dense.reshape(hkv * cap, 1, 1, d)
+    v = s.v_dense.reshape(hkv * cap, 1, 1, d)
+    q = s.q.reshape(hkv, hq // hkv, d)
+    tables = [(h * cap + np.asarray(p, np.int64)).astype(np.int32)
+              for h, p in enumerate(s.positions)]
+    lens = np.array([len(p) for p in s.positions], np.int32)
+    return Workload(name=name, dtype=FP16, page_size=1, num_qo_heads=hq // hkv,
+                    num_kv_heads=1, head_dim=d, sm_scale=s.sm_scale, q=q, k_pool=k,
+                    v_pool=v, block_tables=tables, logical_start=np.zeros(hkv, np.int32),
+                    written_len=lens)
+
+
+@dataclasses.dataclass
+class BlockSparseWorkload:
+    """A selection of KV blocks per (sequence, KV head) over a dense
+    [B, Hkv, Cap, D] allocation; each request's final, partially written
+    block is listed last."""
+    k_dense: np.ndarray     # [B, Hkv, Cap, D] fp16
+    v_dense: np.ndarray
+    q: np.ndarray           # [B, Hq, D] fp16
+    block_ids: np.ndarray   # [B*Hkv, blocks] int32
+    block_size: int
+    kv_len: np.ndarray      # [B] visible positions of each sequence
+    sm_scale: float
+    name: str = "block_sparse_fp16"
+
+
+def block_sparse_fp16(seed=7, hq=64, hkv=4, cap=65536, block_size=128, blocks=16,
+                      kv_len=65536 - 37, d=128):
+    """Block-sparse decode in the geometry of the sparse-paged-decode doc's
+    MiniMax-M3 example (64 query heads, 4 KV heads, head dim 128, blocks of
+    128 positions, 16 selected blocks): one sequence whose live window holds
+    kv_len positions of a Cap-position allocation; per KV head 15 distinct
+    blocks drawn from the scored set (every block but the final one) plus the
+    final block, listed last.  Positions at or past kv_len are NaN, so a
+    decode that reads past the final block's written positions produces NaN."""
+    rng = _rng(seed)
+    k = _normal(rng, (1, hkv, cap, d), FP16)
+    v = _normal(rng, (1, hkv, cap, d), FP16)
+    k[:, :, kv_len:] = np.nan
+    v[:, :, kv_len:] = np.nan
+    q = _normal(rng, (1, hq, d), FP16)
+    final = (kv_len - 1) // block_size
+    ids = np.stack([np.concatenate([rng.choice(final, size=blocks - 1, replace=False),
+                                    [final]]) for _ in range(hkv)]).astype(np.int32)
+    return BlockSparseWorkload(k_dense=k, v_dense=v, q=q, block_ids=ids, block_size=block_size,
+                               kv_len=np.array([kv_len], np.int64), sm_scale=1.0 / np.sqrt(d))
+
+
 def cascade_fp16(seed=5, members=4, prefix_tokens=8192, suffix_lo=256, suffix_hi=2048,
                  hq=32, hkv=8, d=128, ps=16, poison_unused=False):
     """Cascade shared prefix: ``members`` requests share the same physical

@@ -214,6 +214,69 @@ def test_token_sparse_page_size_one(orc):
     check_close(out, lse, ref_v, ref_l, workloads.FP16, "sparse final")
 
 
+def test_sparse_expand_blocks_exact():
+    """Block ids -> rows, both spans, against the definition; ids outside
+    [0, num_blocks) are clamped into the request's region."""
+    rng = np.random.Generator(np.random.PCG64(90))
+    r, blocks, c, nb = 5, 7, 16, 40
+    ids = rng.integers(-3, nb + 3, size=(r, blocks)).astype(np.int32)
+    tail = rng.integers(1, c + 1, size=r).astype(np.int32)
+    base = (np.arange(r) * 1000).astype(np.int32)
+    for span, exact in ((c, True), (1, False)):
+        csr = B.paged_sparse_csr(blocks, c, tail, exact)
+        ip = csr["indptr"]
+        rows = torch.full((int(ip[-1]),), -1, dtype=torch.int32, device=DEV)
+        B.paged_sparse_expand_blocks(to_dev(ids), r, blocks, to_dev(base), span, to_dev(tail),
+                                     to_dev(ip), nb, rows)
+        torch.cuda.synchronize()
+        want = []
+        for i in range(r):
+            for j in range(blocks):
+                cid = min(max(int(ids[i, j]), 0), nb - 1)
+                n = span if (j < blocks - 1 or not exact) else int(tail[i])
+                want.extend(int(base[i]) + cid * span + t for t in range(n))
+        assert rows.cpu().numpy().tolist() == want
+
+
+def _block_sparse_reference(orc, w):
+    b, hkv, cap, d = w.k_dense.shape
+    hq = w.q.shape[1]
+    g = hq // hkv
+    ref_v = np.zeros((b, hq, d))
+    ref_l = np.zeros((b, hq))
+    for s in range(b):
+        for i in range(hq):
+            h = i // g
+            pos = orc.block_positions(w.block_ids[s * hkv + h], w.block_size, w.kv_len[s])
+            ref_v[s, i], ref_l[s, i] = orc.attention_dense_f64(
+                w.q[s, i], w.k_dense[s, h, pos], w.v_dense[s, h, pos], w.sm_scale)
+    return ref_v, ref_l
+
+
+@pytest.mark.parametrize("token_exact", [False, True], ids=["block-granular", "token-exact"])
+@pytest.mark.parametrize("geom", [dict(), dict(seed=8, hq=16, hkv=4, cap=8192, block_size=64,
+                                                blocks=9, kv_len=8192)],
+                         ids=["minimax-like", "g4-full-final-block"])
+def test_block_sparse_decode(orc, token_exact, geom):
+    """The selection read through either page-table granularity matches
+    attention over the selected positions of the dense allocation; the
+    positions past the live length are NaN, so reading past the final
+    block's written positions would show."""
+    w = workloads.block_sparse_fp16(**geom)
+    b, hkv, cap, d = w.k_dense.shape
+    dec = PD.BlockSparseDecode(to_dev(w.k_dense), to_dev(w.v_dense), num_qo_heads=w.q.shape[1],
+                               block_size=w.block_size, blocks_per_request=w.block_ids.shape[1],
+                               kv_len=w.kv_len, token_exact=token_exact)
+    say("case block_sparse %s exact=%s plan=%s" % (geom, token_exact, dec.plan_summary()))
+    ids = to_dev(w.block_ids)
+    for it in range(2):
+        out, lse = dec.run(to_dev(w.q), ids, w.sm_scale)
+        torch.cuda.synchronize()
+    ref_v, ref_l = _block_sparse_reference(orc, w)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, workloads.FP16,
+                "block sparse")
+
+
 def _cascade(w, **kw):
     csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
                             w.k_pool.shape[0])
