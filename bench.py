@@ -92,6 +92,9 @@ def parse():
                         "config is 4)")
     p.add_argument("--kernel-choice", type=int, default=0, choices=[0, 1, 2],
                    help="0 default kernels, 1 token kernel only, 2 no MFMA kernel")
+    p.add_argument("--sweep-chunks", action="store_true",
+                   help="also time the step at every power-of-two pages-per-chunk up to the "
+                        "longest request (plus that length and the default plan's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="approximate CPU work budget of the oracle baseline")
@@ -218,6 +221,8 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / n, (time.time() - w0) / n
 
+    graph_steps = lambda n, fn: PD.graph_time(fn, n)   # noqa: E731
+
     def settle(fn):
         """Run fn back to back for --settle-ms of wall time (untimed): the
         first few ms of work after an idle period run measurably slower."""
@@ -244,6 +249,26 @@ def main():
             settle(lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
             run_steps(args.warmup, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
             part_s, _ = run_steps(args.steps, lambda i: partial_only.partial(q, *kk(i), w.sm_scale))
+
+    # the same step and partial replayed from HIP graphs (no host launch cost);
+    # the graph's last replay must still agree with the oracle
+    graph = None
+    if partial_only is not None and not partial_only.fused:
+        g_step = graph_steps(args.steps, step)
+        gv = runner.out.cpu().numpy().astype(np.float64)
+        gl = runner.lse.cpu().numpy().astype(np.float64)
+        g_ok = bool(np.max(np.abs(gv - ref_v)) <= tv and
+                    np.array_equal(np.isneginf(gl), ~fin) and
+                    (not fin.any() or np.max(np.abs(gl[fin] - ref_l[fin])) <= tl))
+        g_part = graph_steps(args.steps,
+                             lambda i: partial_only.partial(q, *kv[i % len(kv)], w.sm_scale))
+        graph = {"step_us": round(g_step * 1e6, 2), "partial_us": round(g_part * 1e6, 2),
+                 "parity_ok": g_ok}
+
+    sweep = None
+    if args.sweep_chunks and partial_only is not None:
+        sweep = chunk_sweep(args, torch, PD, w, csr, q, kv, ref_v, ref_l, (tv, tl), run_steps,
+                            settle, graph_steps, plan["pages_per_chunk"], dev)
 
     flat_s = None
     if flat_runner is not None:
@@ -313,6 +338,10 @@ def main():
             "flat_kv_bytes": int(flat_bytes),
             "flat_kv_gbs": round(flat_bytes / flat_s / 1e9, 2),
             "flat_plan": flat_runner.plan_summary()}
+    if sweep is not None:
+        res["chunk_sweep"] = sweep
+    if graph is not None:
+        res["graph"] = graph
     if part_s is not None:
         achieved = kv_bytes / part_s / 1e9
         res["partial_us"] = round(part_s * 1e6, 2)
@@ -358,6 +387,45 @@ def main():
         res["copy_calibration_bytes"] = int(src.numel() * 2)
 
     print(json.dumps(res), flush=True)
+
+
+
+
+def chunk_sweep(args, torch, PD, w, csr, q, kv, ref_v, ref_l, tols, run_steps, settle,
+                graph_steps, default_c, dev):
+    """Step and partial time at each candidate pages-per-chunk (plans with the
+    chunk size pinned); every candidate is checked against the oracle first."""
+    rows = []
+    for c in PD.chunk_candidates(csr["indptr"], default_c):
+        r = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                           num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                           head_dim=w.head_dim, fixed_pages_per_chunk=c,
+                           dtype=torch.float32 if w.dtype == "fp32" else torch.float16,
+                           device=dev)
+        out, lse = r.run(q, *kv[0], w.sm_scale)
+        torch.cuda.synchronize()
+        gv = out.cpu().numpy().astype(np.float64)
+        gl = lse.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_l)
+        ok = (float(np.max(np.abs(gv - ref_v))) <= tols[0] and
+              (not fin.any() or float(np.max(np.abs(gl[fin] - ref_l[fin]))) <= tols[1]))
+        if not ok:
+            print(json.dumps({"error": "parity failed in the chunk sweep", "c": c}))
+            sys.exit(1)
+        fn = lambda i: r.run(q, *kv[i % len(kv)], w.sm_scale)   # noqa: E731
+        settle(fn)
+        run_steps(args.warmup, fn)
+        st, _ = run_steps(args.steps, fn)
+        pf = lambda i: r.partial(q, *kv[i % len(kv)], w.sm_scale)   # noqa: E731
+        run_steps(args.warmup, pf)
+        pt, _ = run_steps(args.steps, pf)
+        gs = graph_steps(args.steps, fn)
+        gp = graph_steps(args.steps, pf)
+        rows.append({"pages_per_chunk": c, "num_chunks": r.info.num_chunks,
+                     "units": r.info.num_wgs, "step_us": round(st * 1e6, 2),
+                     "partial_us": round(pt * 1e6, 2), "graph_step_us": round(gs * 1e6, 2),
+                     "graph_partial_us": round(gp * 1e6, 2), "default": c == default_c})
+    return rows
 
 
 def block_sparse(args, torch, B, PD, workloads, dev):
@@ -418,6 +486,31 @@ def block_sparse(args, torch, B, PD, workloads, dev):
 
     t_block = timed(lambda: runners[False].run(q, ids, w.sm_scale))
     t_token = timed(lambda: runners[True].run(q, ids, w.sm_scale))
+    g_block = PD.graph_time(lambda i: runners[False].run(q, ids, w.sm_scale), args.steps)
+    g_token = PD.graph_time(lambda i: runners[True].run(q, ids, w.sm_scale), args.steps)
+    sweep = None
+    if args.sweep_chunks:
+        sweep = {}
+        for exact in (False, True):
+            rows = []
+            for c in PD.chunk_candidates(runners[exact].dec.indptr,
+                                         runners[exact].dec.info.pages_per_chunk):
+                r = PD.BlockSparseDecode(kd, vd, num_qo_heads=hq, block_size=w.block_size,
+                                         blocks_per_request=w.block_ids.shape[1],
+                                         kv_len=w.kv_len, token_exact=exact,
+                                         fixed_pages_per_chunk=c, device=dev)
+                out, lse = r.run(q, ids, w.sm_scale)
+                torch.cuda.synchronize()
+                if not (float(np.max(np.abs(out.cpu().numpy() - ref_v))) <= 2e-3 and
+                        float(np.max(np.abs(lse.cpu().numpy() - ref_l))) <= 1e-3):
+                    print(json.dumps({"error": "parity failed in the chunk sweep", "c": c}))
+                    sys.exit(1)
+                rows.append({"pages_per_chunk": c, "num_chunks": r.dec.info.num_chunks,
+                             "step_us": round(timed(lambda: r.run(q, ids, w.sm_scale)) * 1e6, 2),
+                             "graph_step_us": round(PD.graph_time(
+                                 lambda i: r.run(q, ids, w.sm_scale), args.steps) * 1e6, 2),
+                             "default": c == runners[exact].dec.info.pages_per_chunk})
+            sweep["token_exact" if exact else "block_granular"] = rows
     tokens = sum(len(p) for p in pos)
     kv_bytes = tokens * d * 2 * 2
     value = kv_bytes / t_block / 1e9
@@ -438,10 +531,14 @@ def block_sparse(args, torch, B, PD, workloads, dev):
         "block_vs_token": {"block_granular_step_us": round(t_block * 1e6, 2),
                            "token_exact_step_us": round(t_token * 1e6, 2),
                            "speedup": round(t_token / t_block, 3),
+                           "graph_block_granular_step_us": round(g_block * 1e6, 2),
+                           "graph_token_exact_step_us": round(g_token * 1e6, 2),
                            "token_exact_plan": runners[True].plan_summary()},
         "parity": {"max_abs_v": worst[0], "max_abs_lse2": worst[1], "tol_v": 2e-3,
                    "tol_lse2": 1e-3, "ok": True},
     }
+    if sweep is not None:
+        res["chunk_sweep"] = sweep
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = {"value": round(kv_bytes / oracle_s / 1e9, 4), "unit": "GB/s",
                                "cores": 1, "kind": "oracle",

@@ -118,9 +118,13 @@ int paged_csr_build(int32_t batch, int32_t page_size, int32_t num_pool_pages,
  * pages' CTAs: a workgroup of the token kernel is one unit, a wave of the
  * page kernel is one unit.  target_wgs <= 0 fits the device: with S =
  * paged_decode_default_target_wgs() units resident at once on the current
- * device, the target is the largest t <= S whose plan has at most S units
- * (reported in info->target_wgs); `dtype` (PD_DTYPE_*) selects the kernel
- * whose occupancy defines S and is otherwise unused.
+ * device, the target is the largest t <= S whose plan has at most S units,
+ * lowered if needed to the unit count at c_lo = min(c_max, ceil(32 /
+ * page_size)) so that chunks hold at least 32 token slots (the pages leave
+ * the target uncalibrated; this floor is this library's calibration on
+ * MI355X).  The target used is reported in info->target_wgs; `dtype`
+ * (PD_DTYPE_*) selects the kernel whose occupancy defines S, and page_size
+ * (>= 1) sets the floor; neither is used otherwise.
  *
  * Outputs (HOST): request_indices[n] / kv_tile_indices[n] for n < N, in
  * request order (chunk t of request r covers its pages [t*c, (t+1)*c));
@@ -143,7 +147,8 @@ typedef struct {
 
 int paged_decode_plan(int32_t batch, const int32_t *indptr,
                       int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t dtype, int32_t target_wgs, int32_t fixed_pages_per_chunk,
+                      int32_t dtype, int32_t page_size, int32_t target_wgs,
+                      int32_t fixed_pages_per_chunk,
                       int32_t capacity, int32_t *request_indices,
                       int32_t *kv_tile_indices, int32_t *o_indptr,
                       paged_decode_plan_info *info);

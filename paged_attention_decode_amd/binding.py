@@ -63,7 +63,7 @@ _SIGS = {
     "csr_validate": (i32, [i32, i32, i32, i32p, i32p, i32p, i32p, i32p, i32p]),
     "paged_csr_build": (i32, [i32, i32, i32, i32p, i32p, i32p, i32p, i32, i32p, i32p, i32p,
                               i32p, i32p, i32p]),
-    "paged_decode_plan": (i32, [i32, i32p, i32, i32, i32, i32, i32, i32, i32, i32p, i32p,
+    "paged_decode_plan": (i32, [i32, i32p, i32, i32, i32, i32, i32, i32, i32, i32, i32p, i32p,
                                 i32p, ctypes.POINTER(PlanInfo)]),
     "paged_decode_partial": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
                                    i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp]),
@@ -184,24 +184,26 @@ def paged_csr_build(block_tables, logical_start, written_len, page_size, num_poo
 
 
 def paged_decode_plan(indptr, num_qo_heads, num_kv_heads, head_dim, target_wgs=0,
-                      fixed_pages_per_chunk=0, sizes_only=False, dtype=PD_DTYPE_FP16):
-    """Returns (info: PlanInfo, request_indices, kv_tile_indices, o_indptr)."""
+                      fixed_pages_per_chunk=0, sizes_only=False, dtype=PD_DTYPE_FP16,
+                      page_size=16):
+    """Returns (info: PlanInfo, request_indices, kv_tile_indices, o_indptr).
+    page_size only matters for the device-default target (target_wgs <= 0)."""
     lib = load()
     ip = _host_i32(indptr)
     b = ip.size - 1
     info = PlanInfo()
     oi = np.zeros(b + 1, np.int32)
     _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, dtype,
-                                 target_wgs, fixed_pages_per_chunk, 0, None, None, _hp(oi),
-                                 ctypes.byref(info)))
+                                 page_size, target_wgs, fixed_pages_per_chunk, 0, None, None,
+                                 _hp(oi), ctypes.byref(info)))
     if sizes_only:
         return info, None, None, oi
     cap = max(1, info.num_chunks)
     ri = np.zeros(cap, np.int32)
     ti = np.zeros(cap, np.int32)
     _check(lib.paged_decode_plan(b, _hp(ip), num_qo_heads, num_kv_heads, head_dim, dtype,
-                                 target_wgs, fixed_pages_per_chunk, cap, _hp(ri), _hp(ti),
-                                 _hp(oi), ctypes.byref(info)))
+                                 page_size, target_wgs, fixed_pages_per_chunk, cap, _hp(ri),
+                                 _hp(ti), _hp(oi), ctypes.byref(info)))
     return info, ri[:info.num_chunks], ti[:info.num_chunks], oi
 
 

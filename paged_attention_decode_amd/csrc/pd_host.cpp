@@ -165,6 +165,14 @@ extern "C" int paged_csr_build(int32_t batch, int32_t page_size, int32_t num_poo
 
 namespace {
 
+// Smallest chunk, in token slots (pages x page_size), that the device-default
+// target lets the plan choose.  Calibrated on MI355X by timing every
+// power-of-two pages-per-chunk (bench.py --sweep-chunks, HIP-graph replay):
+// page_size-1 tables (token-sparse selections) were fastest at 16-32 slots
+// per chunk and 3-5x slower at the 2-4 slots the occupancy target alone gave;
+// paged pools (16-token pages) were unaffected.
+constexpr int64_t kMinChunkTokens = 32;
+
 int64_t chunks_at(int32_t batch, const int32_t *indptr, int64_t c)
 {
     int64_t total = 0;
@@ -242,16 +250,18 @@ extern "C" int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim,
 
 extern "C" int paged_decode_plan(int32_t batch, const int32_t *indptr,
                                  int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t dtype, int32_t target_wgs, int32_t fixed_pages_per_chunk,
+                                 int32_t dtype, int32_t page_size, int32_t target_wgs,
+                                 int32_t fixed_pages_per_chunk,
                                  int32_t capacity, int32_t *request_indices,
                                  int32_t *kv_tile_indices, int32_t *o_indptr,
                                  paged_decode_plan_info *info)
 {
     if (!indptr || !o_indptr || !info) return fail(PD_E_NULL, "paged_decode_plan: null argument");
-    if (batch < 1 || num_kv_heads < 1 || num_qo_heads < 1 || head_dim < 1 ||
+    if (batch < 1 || num_kv_heads < 1 || num_qo_heads < 1 || head_dim < 1 || page_size < 1 ||
         num_qo_heads % num_kv_heads != 0)
         return fail(PD_E_ARG, fmt("paged_decode_plan: bad sizes batch=%lld Hq=%lld Hkv=%lld",
-                                  batch, num_qo_heads, num_kv_heads));
+                                  batch, num_qo_heads, num_kv_heads) +
+                                  fmt(" page_size=%lld", page_size));
     if ((request_indices == nullptr) != (kv_tile_indices == nullptr))
         return fail(PD_E_NULL, "paged_decode_plan: pass both chunk arrays or neither");
     if (indptr[0] != 0) return fail(PD_E_INDPTR, "paged_decode_plan: indptr[0] != 0");
@@ -277,6 +287,15 @@ extern "C" int paged_decode_plan(int32_t batch, const int32_t *indptr,
                                                           head_dim, dtype, num_kv_heads);
         if (slots <= 0) return slots < 0 ? slots : fail(PD_E_ARG, "paged_decode_plan: no device target");
         target = fit_target(batch, indptr, wg_per_chunk, slots);
+        // ... but no target whose chunks hold fewer than kMinChunkTokens
+        // token slots: below that a unit's fixed cost (the dependent loads
+        // that start it, the G*(D+1)*4-byte partial it writes and the merge
+        // reads back) outweighs the K/V it streams.  The plan takes the
+        // largest c whose unit count reaches the target, so a target of
+        // units(c_lo) gives c >= c_lo.
+        const int64_t c_lo = std::min<int64_t>(
+            cmax, std::max<int64_t>(1, (kMinChunkTokens + page_size - 1) / page_size));
+        target = std::min<int64_t>(target, chunks_at(batch, indptr, c_lo) * wg_per_chunk);
     }
     if (target <= 0) target = 1;
     int64_t c;

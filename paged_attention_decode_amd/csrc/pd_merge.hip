@@ -133,12 +133,148 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
     if (dv == 0) lse_out[oh] = m + __builtin_amdgcn_logf(wsum);
 }
 
-// One workgroup per (output row, head): its 256 threads are `split` row
-// lanes x D/4 dim lanes.  Row lane k merges rows k, k + split, ... of the
-// group into a partial state (max, weight sum, weighted V) with the loads of
-// up to kUnroll rows in flight, and the split partial states are combined
-// through LDS.  Long groups (many chunks per request) thus finish in a few
-// load round trips instead of one per row.
+// One workgroup per (output row, head, dim slice) for heads whose D/4 float4
+// lanes are a multiple of 8: a slice is 32 dims, and the 256 threads are 32
+// row lanes x 8 dim lanes (each wave: 8 row lanes x 8 dim lanes, lane = 8 *
+// row lane + dim lane).  Row lane k merges rows k, k + 32, ... of the group
+// into a partial state (max, weight sum, weighted V) with the loads of up to
+// kSplitUnroll rows in flight: a group of up to 128 rows is loaded in a
+// single round trip.  The 8 row states of a wave are combined by a butterfly
+// of lane swaps (xor 8, 16, 32), the 4 wave states through LDS.  Slicing the
+// dims spreads one (row, head) over several CUs; the merge runs right after
+// the partial kernel and is bound by load latency, not bandwidth.
+constexpr int kSplitUnroll = 4;
+
+// State of a partial merge: running max m (NaN once a NaN lse was seen),
+// weight sum w relative to m, weighted sum a relative to m.
+template <typename V>
+struct MState {
+    float m, w;
+    V a;
+};
+
+// Combine two states; m = -inf means "no finite row yet", NaN propagates.
+template <typename V>
+__device__ __forceinline__ MState<V> combine(const MState<V> &x, const MState<V> &y)
+{
+    MState<V> r;
+    if (x.m != x.m || y.m != y.m) {
+        r.m = NAN;
+        r.w = 0.f;
+        r.a = filled<V>(0.f);
+        return r;
+    }
+    r.m = fmaxf(x.m, y.m);
+    if (r.m == -INFINITY) {
+        r.w = 0.f;
+        r.a = filled<V>(0.f);
+        return r;
+    }
+    const float sx = x.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x.m - r.m);
+    const float sy = y.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(y.m - r.m);
+    r.w = fmaf(x.w, sx, y.w * sy);
+    r.a = scaled(y.a, sy);
+    fma_into(r.a, sx, x.a);
+    return r;
+}
+
+__device__ __forceinline__ float4 shfl_xor4(const float4 &v, int mask)
+{
+    return make_float4(__shfl_xor(v.x, mask), __shfl_xor(v.y, mask), __shfl_xor(v.z, mask),
+                       __shfl_xor(v.w, mask));
+}
+
+__global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restrict__ v_in,
+                                                          const float *__restrict__ lse_in,
+                                                          const int32_t *__restrict__ o_indptr,
+                                                          int32_t num_heads, int32_t head_dim,
+                                                          float *__restrict__ v_out,
+                                                          float *__restrict__ lse_out)
+{
+    using V = float4;
+    constexpr int DL = 8;                        // float4 dim lanes per slice
+    constexpr int SPLIT = 256 / DL;              // row lanes
+    __shared__ MState<V> s_st[4][DL];
+    const int slices = head_dim / (4 * DL);      // head_dim % 32 == 0, checked by the launcher
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int dl_i = lane & (DL - 1);
+    const int k = wave * 8 + (lane >> 3);        // row lane
+    const int64_t ohs = blockIdx.x;              // (o * num_heads + h) * slices + slice
+    const int64_t oh = ohs / slices;
+    const int dv = int(ohs - oh * slices) * DL + dl_i;
+    const int h = int(oh % num_heads);
+    const int64_t o = oh / num_heads;
+    const int b = o_indptr[o];
+    const int e = o_indptr[o + 1];
+
+    MState<V> st;
+    st.m = -INFINITY;
+    st.w = 0.f;
+    st.a = filled<V>(0.f);
+    bool nan_seen = false;
+    for (int i0 = b + k; i0 < e; i0 += SPLIT * kSplitUnroll) {
+        float x[kSplitUnroll];
+        V vi[kSplitUnroll];
+#pragma unroll
+        for (int u = 0; u < kSplitUnroll; ++u) {
+            const int i = min(i0 + u * SPLIT, e - 1);
+            x[u] = lse_in[int64_t(i) * num_heads + h];
+            vi[u] = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
+        }
+        float mb = st.m;
+#pragma unroll
+        for (int u = 0; u < kSplitUnroll; ++u) {
+            nan_seen |= x[u] != x[u];
+            mb = fmaxf(mb, x[u]);
+        }
+        if (mb == -INFINITY) continue;              // nothing finite yet
+        const float sc = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mb);
+        st.w *= sc;
+        st.a = scaled(st.a, sc);
+        st.m = mb;
+#pragma unroll
+        for (int u = 0; u < kSplitUnroll; ++u) {
+            // a row past the group end or with lse = -inf (empty chunk) has no
+            // weight, and its V (possibly not finite) is never multiplied in
+            const bool live = i0 + u * SPLIT < e && x[u] != -INFINITY;
+            const float w = live ? __builtin_amdgcn_exp2f(x[u] - st.m) : 0.f;
+            st.w += w;
+            fma_live(st.a, live, w, vi[u]);
+        }
+    }
+    if (nan_seen) st.m = NAN;
+    // the 8 row lanes of the wave: lanes dl_i, dl_i + 8, ..., dl_i + 56
+#pragma unroll
+    for (int mask = 8; mask < 64; mask <<= 1) {
+        MState<V> y;
+        y.m = __shfl_xor(st.m, mask);
+        y.w = __shfl_xor(st.w, mask);
+        y.a = shfl_xor4(st.a, mask);
+        st = combine(st, y);
+    }
+    if (lane < DL) s_st[wave][lane] = st;
+    __syncthreads();
+    if (tid >= DL) return;
+    st = s_st[0][tid];
+#pragma unroll
+    for (int wv = 1; wv < 4; ++wv) st = combine(st, s_st[wv][tid]);
+    V *dst = reinterpret_cast<V *>(v_out + oh * head_dim) + dv;
+    const bool lse_lane = dv == 0;
+    if (st.m != st.m || st.m == -INFINITY) {
+        const bool nan = st.m != st.m;
+        *dst = filled<V>(nan ? NAN : 0.f);
+        if (lse_lane) lse_out[oh] = nan ? NAN : -INFINITY;
+        return;
+    }
+    *dst = scaled(st.a, 1.f / st.w);
+    if (lse_lane) lse_out[oh] = st.m + __builtin_amdgcn_logf(st.w);
+}
+
+// One workgroup per (output row, head), for any other head size: its 256
+// threads are `split` row lanes x D/W dim lanes; row lane k merges rows k,
+// k + split, ... of the group and the split states are combined through LDS.
 template <int W>
 __global__ void __launch_bounds__(256) merge_split_kernel(const float *__restrict__ v_in,
                                                           const float *__restrict__ lse_in,
@@ -163,9 +299,6 @@ __global__ void __launch_bounds__(256) merge_split_kernel(const float *__restric
     const int e = o_indptr[o + 1];
     const bool active = k < split;
 
-    // one pass: each batch of kUnroll rows is loaded at once (LSE and V
-    // together), and the running state is rescaled when a batch raises the
-    // max
     float m = -INFINITY;
     bool nan_seen = false;
     float wsum = 0.f;
@@ -193,8 +326,6 @@ __global__ void __launch_bounds__(256) merge_split_kernel(const float *__restric
             m = mb;
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                // a row past the group end or with lse = -inf (empty chunk) has
-                // no weight, and its V (possibly not finite) is never multiplied in
                 const bool live = i0 + u * split < e && x[u] != -INFINITY;
                 const float w = live ? __builtin_amdgcn_exp2f(x[u] - m) : 0.f;
                 wsum += w;
@@ -255,7 +386,13 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (head_dim / w <= 256) {
+    if (vec4 && head_dim % 32 == 0) {
+        // one workgroup per (output row, head, 32-dim slice)
+        const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / 32);
+        if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
+        hipLaunchKernelGGL(merge_slice_kernel, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
+                           lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
+    } else if (head_dim / w <= 256) {
         // one workgroup per (output row, head), rows split across lanes
         const int64_t nblk = int64_t(num_out_rows) * num_heads;
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");

@@ -46,6 +46,7 @@ class PagedDecode:
                  fixed_pages_per_chunk: int = 0, fused: bool = False, dtype=torch.float16,
                  device="cuda"):
         indptr = np.asarray(csr["indptr"], np.int32)
+        self.indptr = indptr
         self.batch = indptr.size - 1
         self.page_size = page_size
         self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
@@ -54,7 +55,7 @@ class PagedDecode:
         pd_dtype = B.PD_DTYPE_FP32 if dtype == torch.float32 else B.PD_DTYPE_FP16
         info, ri, ti, oi = B.paged_decode_plan(indptr, num_qo_heads, num_kv_heads, head_dim,
                                                target_wgs, fixed_pages_per_chunk,
-                                               dtype=pd_dtype)
+                                               dtype=pd_dtype, page_size=page_size)
         self.info, self.request_indices, self.kv_tile_indices, self.o_indptr = info, ri, ti, oi
         self.device = torch.device(device)
         idx = np.asarray(csr["indices"], np.int32)
@@ -292,7 +293,7 @@ class BlockSparseDecode:
 
     def __init__(self, k_dense, v_dense, *, num_qo_heads: int, block_size: int,
                  blocks_per_request: int, kv_len, token_exact: bool = False,
-                 target_wgs: int = 0, device="cuda"):
+                 target_wgs: int = 0, fixed_pages_per_chunk: int = 0, device="cuda"):
         b, hkv, cap, d = k_dense.shape
         if v_dense.shape != k_dense.shape or not k_dense.is_contiguous() or \
                 not v_dense.is_contiguous():
@@ -330,7 +331,8 @@ class BlockSparseDecode:
         self.dec = PagedDecode(csr, page_size=self.page_size,
                                num_pool_pages=self.k_pool.shape[0],
                                num_qo_heads=num_qo_heads // hkv, num_kv_heads=1, head_dim=d,
-                               target_wgs=target_wgs, device=device)
+                               target_wgs=target_wgs,
+                               fixed_pages_per_chunk=fixed_pages_per_chunk, device=device)
         dev = self.dec.device
         self.d_base = _dev_i32(base.astype(np.int32), dev)
         self.d_tail = _dev_i32(tail, dev)
@@ -352,3 +354,78 @@ class BlockSparseDecode:
         return (out.view(self.batch, self.num_qo_heads, self.head_dim),
                 lse.view(self.batch, self.num_qo_heads))
 
+
+
+def graph_time(fn, n: int = 120, per_graph: int = 30) -> float:
+    """GPU seconds per call of fn(i): per_graph calls are captured once in a
+    HIP graph and the graph is replayed n // per_graph times between events
+    on the current stream, so the host's per-launch cost is not counted.  fn
+    must launch work only (no allocation, no synchronization)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i)
+    torch.cuda.synchronize()
+    reps = max(1, n // per_graph)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(reps):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * per_graph)
+
+
+def chunk_candidates(indptr, default_c: int):
+    """Pages-per-chunk values worth timing for one batch: the powers of two
+    below the longest request's page count, that count itself, and the
+    default plan's choice."""
+    max_pages = max(1, int(np.max(np.diff(np.asarray(indptr)))))
+    cands = {max_pages, default_c}
+    c = 1
+    while c < max_pages:
+        cands.add(c)
+        c *= 2
+    return sorted(cands)
+
+
+def autotune(csr: dict, q, k_pool, v_pool, sm_scale, *, page_size: int, num_pool_pages: int,
+             num_qo_heads: int, num_kv_heads: int, head_dim: int, candidates=None,
+             n: int = 120, device="cuda"):
+    """Chunk-size autotune for one batch on this GPU: times a decode step
+    (partial + merge) at each candidate pages-per-chunk -- by default
+    chunk_candidates(), i.e. the powers of two within the batch's range plus
+    the device-default plan's choice -- and returns (the fastest PagedDecode,
+    [{pages_per_chunk, num_chunks, step_us}, ...]).  Every candidate reads
+    the given q and pools; the result does not depend on the choice beyond
+    rounding (split-KV is exact in real arithmetic)."""
+    dtype = q.dtype
+    base = PagedDecode(csr, page_size=page_size, num_pool_pages=num_pool_pages,
+                       num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+                       head_dim=head_dim, dtype=dtype, device=device)
+    if candidates is None:
+        candidates = chunk_candidates(csr["indptr"], base.info.pages_per_chunk)
+    best, table = None, []
+    for c in candidates:
+        dec = base if c == base.info.pages_per_chunk else PagedDecode(
+            csr, page_size=page_size, num_pool_pages=num_pool_pages,
+            num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+            fixed_pages_per_chunk=int(c), dtype=dtype, device=device)
+        t = graph_time(lambda i: dec.run(q, k_pool, v_pool, sm_scale), n)
+        table.append(dict(pages_per_chunk=dec.info.pages_per_chunk,
+                          num_chunks=dec.info.num_chunks, step_us=round(t * 1e6, 2)))
+        if best is None or t < best[0]:
+            best = (t, dec)
+    return best[1], table

@@ -277,6 +277,90 @@ def test_block_sparse_decode(orc, token_exact, geom):
                 "block sparse")
 
 
+@pytest.mark.parametrize("kind", ["flat", "block-sparse"])
+def test_decode_step_replayed_from_hip_graph(orc, kind):
+    """A decode step captured in a HIP graph (partial + merge; for the block
+    selection also the row expansion) and replayed: every replay equals the
+    eager step on the same inputs, with eager work and synchronization
+    between replays and a new query written into the captured buffer."""
+    if kind == "flat":
+        w = cached("batched_fp16", poison_unused=True)
+        csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                                w.k_pool.shape[0])
+        dec = PD.PagedDecode(csr, page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                             num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                             head_dim=w.head_dim)
+        assert dec.info.needs_merge
+        k, v = to_dev(w.k_pool), to_dev(w.v_pool)
+        qs = [w.q, workloads._normal(np.random.default_rng(3), w.q.shape, workloads.FP16)]
+        step = lambda qb: dec.run(qb, k, v, w.sm_scale)   # noqa: E731
+    else:
+        w = workloads.block_sparse_fp16(seed=8, hq=16, hkv=4, cap=8192, block_size=64,
+                                        blocks=9, kv_len=8000)
+        dec = PD.BlockSparseDecode(to_dev(w.k_dense), to_dev(w.v_dense),
+                                   num_qo_heads=w.q.shape[1], block_size=w.block_size,
+                                   blocks_per_request=w.block_ids.shape[1], kv_len=w.kv_len,
+                                   token_exact=True)
+        ids = to_dev(w.block_ids)
+        qs = [w.q, workloads._normal(np.random.default_rng(4), w.q.shape, workloads.FP16)]
+        step = lambda qb: dec.run(qb, ids, w.sm_scale)   # noqa: E731
+    qbuf = to_dev(qs[0])
+    eager = []
+    for qh in qs:
+        qbuf.copy_(to_dev(qh))
+        out, lse = step(qbuf)
+        torch.cuda.synchronize()
+        eager.append((out.cpu().numpy().copy(), lse.cpu().numpy().copy()))
+    qbuf.copy_(to_dev(qs[0]))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(qbuf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_g, lse_g = step(qbuf)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        which = rep % 2
+        qbuf.copy_(to_dev(qs[which]))
+        torch.cuda.synchronize()
+        _ = (qbuf.float() * 2).sum().item()          # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        ev, el = eager[which]
+        got_v, got_l = out_g.cpu().numpy(), lse_g.cpu().numpy()
+        say("  graph %s replay %d: max|dv|=%.3g" % (kind, rep, np.max(np.abs(got_v - ev))))
+        np.testing.assert_allclose(got_v, ev, rtol=0, atol=1e-6)
+        np.testing.assert_allclose(got_l, el, rtol=0, atol=1e-6)
+
+
+def test_autotune_times_every_candidate_and_stays_exact(orc):
+    """Chunk-size autotune on the token-sparse selection (page_size 1): every
+    power-of-two candidate and the default plan's choice are timed, the
+    fastest is kept, and its output matches the oracle."""
+    w = workloads.folded_sparse(workloads.token_sparse_fp16())
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            w.k_pool.shape[0])
+    k, v, q = to_dev(w.k_pool), to_dev(w.v_pool), to_dev(w.q)
+    dec, table = PD.autotune(csr, q, k, v, w.sm_scale, page_size=w.page_size,
+                             num_pool_pages=w.k_pool.shape[0], num_qo_heads=w.num_qo_heads,
+                             num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, n=60)
+    say("  autotune table: %s" % table)
+    cs = [row["pages_per_chunk"] for row in table]
+    assert cs == sorted(set(cs)) and {1, 2, 4, 1024, 2048} <= set(cs) and 32 in cs
+    fastest = min(table, key=lambda row: row["step_us"])
+    assert dec.info.pages_per_chunk == fastest["pages_per_chunk"]
+    out, lse = dec.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
+                                 nthreads=NTHREADS)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "autotuned")
+
+
 def _cascade(w, **kw):
     csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
                             w.k_pool.shape[0])
@@ -577,6 +661,24 @@ def test_merge_kernel_against_oracle(orc, d):
     assert np.all(gv[2] == 0) and np.all(np.isneginf(gl[2]))
 
 
+@pytest.mark.parametrize("d", [512, 96, 128])
+def test_merge_kernel_long_groups(orc, d):
+    """Groups longer than one load round of the row lanes (up to 300 rows),
+    head dims split into 16, 3 and 4 dim slices, and -inf rows spread over
+    every round."""
+    rng = np.random.default_rng(95 + d)
+    sizes = [300, 1, 129, 128, 33, 0, 257]
+    oi = np.concatenate([[0], np.cumsum(sizes)]).tolist()
+    n, h = oi[-1], 3
+    v = rng.standard_normal((n, h, d)).astype(np.float32)
+    l = (rng.standard_normal((n, h)) * 12).astype(np.float32)
+    l[rng.random((n, h)) < 0.3] = -np.inf
+    v[np.isneginf(l)] = 1e30                   # never read: carries no weight
+    gv, gl = _merge_gpu(v, l, oi)
+    rv, rl = orc.merge(v.astype(np.float64), l.astype(np.float64), oi)
+    check_close(gv, gl, rv, rl, workloads.FP32, "long merge d=%d" % d)
+
+
 def test_merge_kernel_regrouping(orc):
     rng = np.random.default_rng(90)
     n, h, d = 16, 4, 128
@@ -603,19 +705,37 @@ def test_default_target_is_cu_multiple():
         assert t >= cus and t % cus == 0, (g, hkv, t)
 
 
-@pytest.mark.parametrize("name", ["long_context_fp16", "batched_fp16", "tiny_fp32"])
+@pytest.mark.parametrize("name", ["long_context_fp16", "batched_fp16", "tiny_fp32",
+                                  "token_sparse_fp16"])
 def test_default_target_fits_one_round(orc, name):
     """Default plan: the largest target whose unit count fits the resident
-    capacity S, checked against the oracle's exhaustive plans."""
-    w = cached(name)
+    capacity S, lowered to the unit count of 32-slot chunks when the fit
+    would cut chunks smaller; checked against the oracle's exhaustive
+    plans."""
+    if name == "token_sparse_fp16":
+        w = workloads.folded_sparse(workloads.token_sparse_fp16())
+    else:
+        w = cached(name)
     csr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
                                     w.page_size)
     g = w.num_qo_heads // w.num_kv_heads
     dt = B.PD_DTYPE_FP16 if w.dtype == workloads.FP16 else B.PD_DTYPE_FP32
     slots = B.paged_decode_default_target_wgs(0, g, w.head_dim, dt, w.num_kv_heads)
     info, _, _, _ = B.paged_decode_plan(csr["indptr"], w.num_qo_heads, w.num_kv_heads,
-                                        w.head_dim, 0, 0, sizes_only=True, dtype=dt)
+                                        w.head_dim, 0, 0, sizes_only=True, dtype=dt,
+                                        page_size=w.page_size)
     units = lambda t: orc.plan(csr["indptr"], w.num_kv_heads, t)["num_chunks"] * w.num_kv_heads
     best = max([t for t in range(1, slots + 1) if units(t) <= slots] or [slots])
-    assert info.target_wgs == best
+    cmax = max(1, int(np.max(np.diff(csr["indptr"]))))
+    c_lo = min(cmax, -(-32 // w.page_size))
+    floor_units = orc.plan(csr["indptr"], w.num_kv_heads, 1,
+                           fixed_pages_per_chunk=c_lo)["num_chunks"] * w.num_kv_heads
+    assert info.target_wgs == min(best, floor_units)
+    assert info.pages_per_chunk >= c_lo
+    ref = orc.plan(csr["indptr"], w.num_kv_heads, info.target_wgs)
+    assert info.pages_per_chunk == ref["pages_per_chunk"]
     assert info.num_wgs <= slots or units(1) > slots
+    if name == "token_sparse_fp16":
+        assert info.pages_per_chunk == 32          # page_size 1: the floor binds
+    if name == "long_context_fp16":
+        assert info.pages_per_chunk == 26          # the fit binds
