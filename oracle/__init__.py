@@ -24,6 +24,10 @@ Functions and the passages of the mlxcel pages they follow:
 - ``plan``: exhaustive scan over pages-per-chunk (PR #984 body item 4, the
   commit "plan + launch": largest chunk size whose workgroup count reaches the
   target, 65535-chunk launch bound, >= 1 chunk per request, request order).
+- ``attention_mla``: decode with a second key stream (sparse-paged-decode
+  doc, DSA section): score = scale*(q . k[0:Dim]) + scale*(q_extra .
+  k_extra) over rows gathered one by one through the page table, one KV
+  head, the latent rows k[0:Dim] as values; whole requests or chunk ranges.
 - ``block_positions``: the positions a selection of KV blocks covers
   (sparse-paged-decode doc, selection from blocks).
 - ``cascade_detect``: brute-force search for the shared page span that
@@ -278,3 +282,53 @@ def attention_dense_f64(q_rows, k_rows, v_rows, sm_scale):
     w = np.exp(s - m)
     z = w.sum()
     return (w[:, None] * v).sum(0) / z, (m + np.log(z)) / np.log(2.0)
+
+
+def _row_strides(pool):
+    # element strides (page, entry) of a [pages, page_size, row] fp16 array
+    if pool.ndim != 3 or pool.strides[-1] != pool.itemsize:
+        raise ValueError("pool must be [pages, page_size, row] with contiguous rows")
+    return pool.strides[0] // pool.itemsize, pool.strides[1] // pool.itemsize
+
+
+def attention_mla(q, q_extra, k_pool, k_extra_pool, csr, page_size: int, sm_scale: float,
+                  chunks=None, nthreads: int = 1):
+    """q [B, Hq, Dim] and q_extra [B, Hq, E] fp16; k_pool [pages, page_size,
+    RowStride >= Dim] and k_extra_pool [pages, page_size, >= E] fp16.
+    chunks = (request_indices, kv_tile_indices, pages_per_chunk) selects
+    chunk mode.  Returns (out [rows, Hq, Dim] f64, lse2 [rows, Hq] f64)."""
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    qx = np.ascontiguousarray(q_extra)
+    for a in (q, qx, k_pool, k_extra_pool):
+        if a.dtype != np.float16:
+            raise TypeError("attention_mla takes fp16 arrays")
+    b, hq, dim = q.shape
+    ex = qx.shape[2]
+    if k_pool.shape[2] < dim or k_extra_pool.shape[2] < ex:
+        raise ValueError("pool rows narrower than the query")
+    kps, kts = _row_strides(k_pool)
+    xps, xts = _row_strides(k_extra_pool)
+    indptr, indices = _i32(csr["indptr"]), _i32(csr["indices"])
+    if indices.size == 0:
+        indices = np.zeros(1, np.int32)
+    lpl, fpo = _i32(csr["last_page_len"]), _i32(csr["first_page_offset"])
+    if chunks is None:
+        rows, ri, ti, c = b, None, None, 0
+    else:
+        ri, ti = _i32(chunks[0]), _i32(chunks[1])
+        rows, c = ri.size, int(chunks[2])
+    out = np.zeros((rows, hq, dim), np.float64)
+    lse = np.zeros((rows, hq), np.float64)
+    u16 = ctypes.POINTER(ctypes.c_uint16)
+    rc = lib.orc_attention_mla(
+        ctypes.c_int32(rows), ctypes.c_int32(hq), ctypes.c_int32(dim), ctypes.c_int32(ex),
+        ctypes.c_int32(page_size), _p(indptr), _p(indices), _p(lpl), _p(fpo),
+        q.ctypes.data_as(u16), qx.ctypes.data_as(u16), ctypes.c_void_p(k_pool.ctypes.data),
+        ctypes.c_void_p(k_extra_pool.ctypes.data), ctypes.c_int64(kps), ctypes.c_int64(kts),
+        ctypes.c_int64(xps), ctypes.c_int64(xts), ctypes.c_double(sm_scale),
+        _p(ri) if ri is not None else None, _p(ti) if ti is not None else None,
+        ctypes.c_int32(c), _p(out, f64p), _p(lse, f64p), ctypes.c_int32(nthreads))
+    if rc != 0:
+        raise ValueError("oracle attention_mla failed (rc=%d)" % rc)
+    return out, lse

@@ -457,3 +457,143 @@ int orc_cascade_detect(int32_t batch, const int32_t *indptr, const int32_t *indi
     *shared_pages = best_span;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* O8: decode with a second key stream (sparse-paged-decode doc, the   */
+/* DSA section: the score of a visible token t is                      */
+/*   sm_scale * (q . k[t][0:Dim]) + sm_scale * (q_extra . k_extra[t]), */
+/* with k read from rows of RowStride >= Dim elements and k_extra from */
+/* a pool of its own with the same page table).  One KV head.  The     */
+/* values are the first Dim elements of the k rows (the latent rows    */
+/* serve as keys and values).  Chunk mode restricts each (chunk, head) */
+/* to its chunk's token range, as orc_partial does.                    */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int32_t hq, dim, extra_dim, page_size;
+    const int32_t *indptr, *indices, *lpl, *fpo;
+    const uint16_t *q, *q_extra, *k, *k_extra;          /* fp16 bit patterns */
+    int64_t k_page_stride, k_token_stride, x_page_stride, x_token_stride;
+    double sm_scale;
+    int32_t pages_per_chunk;
+    const int32_t *request_indices, *kv_tile_indices;
+    double *out, *lse2;
+    int32_t num_units, nthreads, status;
+} mla_job_t;
+
+static int64_t mla_visible(const mla_job_t *j, int32_t r)
+{
+    int64_t pages = j->indptr[r + 1] - j->indptr[r];
+    if (pages == 0) return 0;
+    return (pages - 1) * j->page_size + j->lpl[r] - j->fpo[r];
+}
+
+static int mla_attend(const mla_job_t *j, int32_t r, int32_t h, int64_t tb, int64_t te,
+                      double *o, double *lse2)
+{
+    const int64_t n = te > tb ? te - tb : 0;
+    for (int32_t e = 0; e < j->dim; ++e) o[e] = 0.0;
+    if (n == 0) {
+        *lse2 = -INFINITY;
+        return ORC_OK;
+    }
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    int64_t *kb = (int64_t *)malloc(sizeof(int64_t) * (size_t)n);
+    if (!s || !kb) { free(s); free(kb); return ORC_NOMEM; }
+    const int64_t qb = ((int64_t)r * j->hq + h) * j->dim;
+    const int64_t xb = ((int64_t)r * j->hq + h) * j->extra_dim;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t slot = j->fpo[r] + tb + i;
+        int64_t page = j->indices[j->indptr[r] + slot / j->page_size];
+        int64_t entry = slot % j->page_size;
+        int64_t krow = page * j->k_page_stride + entry * j->k_token_stride;
+        int64_t xrow = page * j->x_page_stride + entry * j->x_token_stride;
+        kb[i] = krow;
+        double dot = 0.0, dot_x = 0.0;
+        for (int32_t e = 0; e < j->dim; ++e)
+            dot += half_to_double(j->q[qb + e]) * half_to_double(j->k[krow + e]);
+        for (int32_t e = 0; e < j->extra_dim; ++e)
+            dot_x += half_to_double(j->q_extra[xb + e]) * half_to_double(j->k_extra[xrow + e]);
+        s[i] = j->sm_scale * dot + j->sm_scale * dot_x;
+    }
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) if (s[i] > m) m = s[i];
+    double z = 0.0;
+    for (int64_t i = 0; i < n; ++i) z += exp(s[i] - m);
+    for (int64_t i = 0; i < n; ++i) {
+        double w = exp(s[i] - m) / z;
+        for (int32_t e = 0; e < j->dim; ++e) o[e] += w * half_to_double(j->k[kb[i] + e]);
+    }
+    *lse2 = (m + log(z)) / log(2.0);
+    free(s);
+    free(kb);
+    return ORC_OK;
+}
+
+static void *mla_worker(void *arg)
+{
+    mla_job_t *j = (mla_job_t *)((void **)arg)[0];
+    int32_t tid = (int32_t)(intptr_t)((void **)arg)[1];
+    for (int32_t u = tid; u < j->num_units; u += j->nthreads) {
+        int32_t row = u / j->hq, h = u % j->hq, r;
+        int64_t tb, te;
+        if (j->request_indices) {
+            r = j->request_indices[row];
+            int64_t t = j->kv_tile_indices[row];
+            int64_t span = (int64_t)j->pages_per_chunk * j->page_size;
+            tb = t * span - j->fpo[r];
+            te = (t + 1) * span - j->fpo[r];
+            if (tb < 0) tb = 0;
+            if (te > mla_visible(j, r)) te = mla_visible(j, r);
+        } else {
+            r = row;
+            tb = 0;
+            te = mla_visible(j, r);
+        }
+        int rc = mla_attend(j, r, h, tb, te, j->out + (int64_t)u * j->dim, j->lse2 + u);
+        if (rc != ORC_OK) j->status = rc;
+    }
+    return NULL;
+}
+
+/* rows = batch (whole requests) or num_chunks (chunk mode, request_indices
+ * non-NULL).  q [B, Hq, Dim], q_extra [B, Hq, ExtraDim]; k element (page,
+ * entry, e) at page*k_page_stride + entry*k_token_stride + e, likewise
+ * k_extra with its own strides.  out [rows, Hq, Dim], lse2 [rows, Hq]. */
+int orc_attention_mla(int32_t rows, int32_t num_qo_heads, int32_t dim, int32_t extra_dim,
+                      int32_t page_size, const int32_t *indptr, const int32_t *indices,
+                      const int32_t *last_page_len, const int32_t *first_page_offset,
+                      const uint16_t *q, const uint16_t *q_extra, const uint16_t *k_pool,
+                      const uint16_t *k_extra_pool, int64_t k_page_stride,
+                      int64_t k_token_stride, int64_t x_page_stride, int64_t x_token_stride,
+                      double sm_scale, const int32_t *request_indices,
+                      const int32_t *kv_tile_indices, int32_t pages_per_chunk,
+                      double *out, double *lse2, int32_t nthreads)
+{
+    if (rows < 0 || num_qo_heads < 1 || dim < 1 || extra_dim < 0 || page_size < 1)
+        return ORC_BAD;
+    mla_job_t j;
+    memset(&j, 0, sizeof(j));
+    j.hq = num_qo_heads; j.dim = dim; j.extra_dim = extra_dim; j.page_size = page_size;
+    j.indptr = indptr; j.indices = indices; j.lpl = last_page_len; j.fpo = first_page_offset;
+    j.q = q; j.q_extra = q_extra; j.k = k_pool; j.k_extra = k_extra_pool;
+    j.k_page_stride = k_page_stride; j.k_token_stride = k_token_stride;
+    j.x_page_stride = x_page_stride; j.x_token_stride = x_token_stride;
+    j.sm_scale = sm_scale; j.pages_per_chunk = pages_per_chunk;
+    j.request_indices = request_indices; j.kv_tile_indices = kv_tile_indices;
+    j.out = out; j.lse2 = lse2;
+    j.num_units = rows * num_qo_heads;
+    j.status = ORC_OK;
+    int32_t nt = nthreads < 1 ? 1 : (nthreads > 256 ? 256 : nthreads);
+    j.nthreads = nt;
+    pthread_t th[256];
+    void *args[256][2];
+    for (int32_t t = 0; t < nt; ++t) {
+        args[t][0] = &j;
+        args[t][1] = (void *)(intptr_t)t;
+        if (nt == 1) mla_worker(args[t]);
+        else pthread_create(&th[t], NULL, mla_worker, args[t]);
+    }
+    if (nt > 1)
+        for (int32_t t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+    return j.status;
+}

@@ -361,3 +361,112 @@ ALL = {
     "long_context_fp16": long_context_fp16,
     "cascade_fp16": cascade_fp16,
 }
+
+
+@dataclasses.dataclass
+class MlaWorkload:
+    """Decode with a second key stream (the DSA / paged-MLA shape of the
+    sparse-paged-decode doc): one KV head; k_pool rows hold the latent
+    (dim elements, also the values) followed by an indexer key up to
+    row_stride; k_extra_pool holds the rope keys; both share the page table."""
+    name: str
+    page_size: int
+    num_qo_heads: int
+    dim: int
+    extra_dim: int
+    row_stride: int
+    sm_scale: float
+    q: np.ndarray                   # [B, Hq, dim] fp16
+    q_extra: np.ndarray             # [B, Hq, extra_dim] fp16
+    k_pool: np.ndarray              # [pages, page_size, row_stride] fp16
+    k_extra_pool: np.ndarray        # [pages, page_size, extra_dim] fp16
+    block_tables: List[np.ndarray]
+    logical_start: np.ndarray
+    written_len: np.ndarray
+    dtype: str = FP16
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def visible_tokens(self) -> np.ndarray:
+        return (self.written_len - self.logical_start).astype(np.int64)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic bytes one decode step reads: every visible token's
+        latent and rope keys once (the latent doubles as the value)."""
+        return int(self.visible_tokens.sum()) * (self.dim + self.extra_dim) * 2
+
+
+def mla_paged(name="mla_paged", *, seed, logical_start, written_len, num_qo_heads=128,
+              page_size=64, dim=512, extra_dim=64, row_stride=640, pool_slack=2.0,
+              poison_unused=False, poison_indexer=False):
+    """A paged latent cache: per-request (logical_start, written_len), pages
+    drawn without replacement from a pool with 2x slack.  poison_unused sets
+    unused pages to NaN; poison_indexer sets the row columns past `dim` (the
+    indexer key, never read by the decode) to NaN."""
+    rng = _rng(seed)
+    ls = np.asarray(logical_start, dtype=np.int32)
+    wl = np.asarray(written_len, dtype=np.int32)
+    nlive = sum(max(0, (-(-int(w) // page_size) if w > 0 else 0) - int(s) // page_size)
+                for s, w in zip(ls, wl))
+    pool_pages = max(1, int(np.ceil(pool_slack * max(1, nlive))))
+    tables, used = _tables_from_lengths(rng, list(zip(ls.tolist(), wl.tolist())), page_size,
+                                        pool_pages)
+    b = ls.size
+    k = _normal(rng, (pool_pages, page_size, row_stride), FP16)
+    kx = _normal(rng, (pool_pages, page_size, extra_dim), FP16)
+    q = _normal(rng, (b, num_qo_heads, dim), FP16)
+    qx = _normal(rng, (b, num_qo_heads, extra_dim), FP16)
+    if poison_unused:
+        unused = np.ones(pool_pages, dtype=bool)
+        unused[np.asarray(used, dtype=np.int64)] = False
+        k[unused] = np.nan
+        kx[unused] = np.nan
+    if poison_indexer:
+        k[:, :, dim:] = np.nan
+    return MlaWorkload(name=name, page_size=page_size, num_qo_heads=num_qo_heads, dim=dim,
+                       extra_dim=extra_dim, row_stride=row_stride,
+                       sm_scale=1.0 / np.sqrt(dim + extra_dim), q=q, q_extra=qx, k_pool=k,
+                       k_extra_pool=kx, block_tables=tables, logical_start=ls, written_len=wl)
+
+
+def mla_paged_fp16(seed=9, batch=4, context=32768, **kw):
+    """Paged MLA decode in DeepSeek-V3.2's attention geometry (128 query
+    heads, latent 512, rope 64, indexer key 128, so rows of 640): `batch`
+    requests of `context` visible tokens in 64-token pages."""
+    return mla_paged("mla_paged_fp16", seed=seed, logical_start=[0] * batch,
+                     written_len=[context] * batch, **kw)
+
+
+def dsa_sparse_fp16(seed=10, batch=8, capacity=32768, kv_len=32768 - 29, topk=2048,
+                    num_qo_heads=128, dim=512, extra_dim=64, row_stride=640,
+                    poison_unselected=False):
+    """DSA decode over a dense latent cache: per sequence a [capacity,
+    row_stride] latent allocation and a [capacity, extra_dim] rope allocation,
+    read as page_size-1 pools (row = b * capacity + position); each sequence
+    selects `topk` distinct positions below kv_len (sorted).  The page table
+    lists the selected rows.  poison_unselected sets every unselected row (and
+    the indexer-key columns) to NaN."""
+    rng = _rng(seed)
+    k = _normal(rng, (batch * capacity, 1, row_stride), FP16)
+    kx = _normal(rng, (batch * capacity, 1, extra_dim), FP16)
+    q = _normal(rng, (batch, num_qo_heads, dim), FP16)
+    qx = _normal(rng, (batch, num_qo_heads, extra_dim), FP16)
+    tables = []
+    for s in range(batch):
+        pos = np.sort(rng.choice(kv_len, size=topk, replace=False)).astype(np.int32)
+        tables.append(s * capacity + pos)
+    if poison_unselected:
+        keep = np.zeros(batch * capacity, dtype=bool)
+        keep[np.concatenate(tables)] = True
+        k[~keep] = np.nan
+        kx[~keep] = np.nan
+        k[:, :, dim:] = np.nan
+    return MlaWorkload(name="dsa_sparse_fp16", page_size=1, num_qo_heads=num_qo_heads,
+                       dim=dim, extra_dim=extra_dim, row_stride=row_stride,
+                       sm_scale=1.0 / np.sqrt(dim + extra_dim), q=q, q_extra=qx, k_pool=k,
+                       k_extra_pool=kx, block_tables=tables,
+                       logical_start=np.zeros(batch, np.int32),
+                       written_len=np.full(batch, topk, np.int32))
