@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV GB/s and % of HBM peak, paged decode B=4 ctx=32k GQA fp16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, AMD published
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "partial_long_context_fp16_counters.md")
 PARTIAL_SRC = os.path.join(ROOT, "paged_attention_decode_amd", "csrc", "pd_partial.hip")
 
@@ -75,7 +76,8 @@ def parse():
                         "timed region (the GPU takes a few ms to leave its idle state)")
     p.add_argument("--workload", default="long_context_fp16",
                    choices=["long_context_fp16", "batched_fp16", "tiny_fp32", "cascade_fp16",
-                            "token_sparse_fp16", "block_sparse_fp16"])
+                            "token_sparse_fp16", "block_sparse_fp16", "mla_paged_fp16",
+                            "dsa_sparse_fp16"])
     p.add_argument("--target-wgs", type=int, default=0, help="plan target (0: device default)")
     p.add_argument("--fixed-pages-per-chunk", type=int, default=0)
     p.add_argument("--mode", default="two-launch", choices=["fused", "two-launch"],
@@ -124,6 +126,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "block_sparse_fp16":
         return block_sparse(args, torch, B, PD, workloads, dev)
+    if args.workload in ("mla_paged_fp16", "dsa_sparse_fp16"):
+        return mla(args, torch, B, PD, workloads, dev)
     t0 = time.time()
     if args.workload == "cascade_fp16":
         w = workloads.cascade_fp16(members=args.cascade_members, prefix_tokens=args.cascade_prefix)
@@ -426,6 +430,128 @@ def chunk_sweep(args, torch, PD, w, csr, q, kv, ref_v, ref_l, tols, run_steps, s
                      "partial_us": round(pt * 1e6, 2), "graph_step_us": round(gs * 1e6, 2),
                      "graph_partial_us": round(gp * 1e6, 2), "default": c == default_c})
     return rows
+
+
+def mla(args, torch, B, PD, workloads, dev):
+    """Paged-MLA / DSA decode (second key stream): the step (partial + merge)
+    and the partial alone, eager and replayed from a HIP graph, with the HBM
+    and the matrix-core roofline of the partial kernel."""
+    import oracle
+    t0 = time.time()
+    w = getattr(workloads, args.workload)()
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            w.k_pool.shape[0])
+    dec = PD.MlaDecode(csr, page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                       num_qo_heads=w.num_qo_heads, dim=w.dim, extra_dim=w.extra_dim,
+                       target_wgs=args.target_wgs,
+                       fixed_pages_per_chunk=args.fixed_pages_per_chunk, device=dev)
+    q, qx = torch.from_numpy(w.q).to(dev), torch.from_numpy(w.q_extra).to(dev)
+    # pool copies used in turn, so the steps stream from HBM when the pools
+    # exceed the last-level cache
+    kv = [(torch.from_numpy(w.k_pool).to(dev), torch.from_numpy(w.k_extra_pool).to(dev))]
+    for _ in range(args.pool_copies - 1):
+        kv.append((kv[0][0].clone(), kv[0][1].clone()))
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    step = lambda i: dec.run(q, qx, *kv[i % len(kv)], w.sm_scale)   # noqa: E731
+    part = lambda i: dec.partial(q, qx, *kv[i % len(kv)], w.sm_scale)   # noqa: E731
+    out, lse = step(0)
+    torch.cuda.synchronize()
+    # parity on a sample of query heads (both q groups, every 16-head wave)
+    sel = np.array([0, 21, 47, 63, 64, 90, 111, 127])
+    sel = sel[sel < w.num_qo_heads]
+    ocsr = oracle.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                        w.page_size)
+    cores = len(os.sched_getaffinity(0))
+    tc = time.time()
+    ref_v, ref_l = oracle.attention_mla(np.ascontiguousarray(w.q[:, sel]),
+                                        np.ascontiguousarray(w.q_extra[:, sel]), w.k_pool,
+                                        w.k_extra_pool, ocsr, w.page_size, w.sm_scale,
+                                        nthreads=cores)
+    oracle_s = time.time() - tc
+    dv = float(np.max(np.abs(out.cpu().numpy()[:, sel] - ref_v)))
+    dl = float(np.max(np.abs(lse.cpu().numpy()[:, sel] - ref_l)))
+    if not (dv <= 2e-3 and dl <= 1e-3):
+        print(json.dumps({"error": "parity failed", "max_abs_v": dv, "max_abs_lse": dl}))
+        sys.exit(1)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        t_end = time.time() + args.settle_ms * 1e-3
+        i = 0
+        while time.time() < t_end:
+            for _ in range(20):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / args.steps
+
+    step_s = timed(step)
+    part_s = timed(part)
+    g_step = PD.graph_time(step, args.steps)
+    g_part = PD.graph_time(part, args.steps)
+    kv_bytes = w.kv_bytes()
+    tokens = int(w.visible_tokens.sum())
+    flops = tokens * w.num_qo_heads * 2 * (w.dim + w.extra_dim + w.dim)
+    hbm = kv_bytes / part_s / 1e9
+    tflops = flops / part_s / 1e12
+    bound = "hbm" if kv_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_FP16_PEAK_TFLOPS * 1e12) \
+        else "mfma"
+    value = kv_bytes / step_s / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (seeded N(0,1) queries, latent and rope keys)",
+        "config": {"workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": 1, "dim": w.dim, "extra_dim": w.extra_dim,
+                   "row_stride": w.row_stride, "page_size": w.page_size,
+                   "visible_tokens": [int(x) for x in w.visible_tokens],
+                   "kv_bytes_per_step": int(kv_bytes), "flops_per_step": int(flops),
+                   "accumulate": "fp32",
+                   "timing": "%d back-to-back steps after %.0f ms of settle steps and %d "
+                             "warmup steps; step i reads pool copy i mod %d; events on the "
+                             "launch stream" % (args.steps, args.settle_ms, args.warmup,
+                                                len(kv)),
+                   "plan": dec.plan_summary()},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(tokens / step_s, 1),
+        "step_us": round(step_s * 1e6, 2), "partial_us": round(part_s * 1e6, 2),
+        "merge_and_gap_us": round((step_s - part_s) * 1e6, 2),
+        "graph": {"step_us": round(g_step * 1e6, 2), "partial_us": round(g_part * 1e6, 2)},
+        "setup_s": round(setup_s, 1),
+        "parity": {"max_abs_v": dv, "max_abs_lse2": dl, "tol_v": 2e-3, "tol_lse2": 1e-3,
+                   "ok": True, "heads_checked": sel.tolist()},
+        "roofline": {"bound": bound,
+                     "achieved": round(hbm, 2) if bound == "hbm" else round(tflops, 2),
+                     "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_FP16_PEAK_TFLOPS,
+                     "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                     "frac": round(hbm / HBM_PEAK_GBS if bound == "hbm"
+                                   else tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_mla_decode_partial",
+                     "hbm_gbs": round(hbm, 2), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
+                     "mfma_tflops": round(tflops, 2),
+                     "mfma_frac": round(tflops / MFMA_FP16_PEAK_TFLOPS, 4),
+                     "bytes_per_launch": int(kv_bytes), "flops_per_launch": int(flops)},
+    }
+    if not args.no_cpu_baseline:
+        scale = w.num_qo_heads / sel.size
+        res["cpu_baseline"] = {"value": round(kv_bytes / (oracle_s * scale) / 1e9, 4),
+                               "unit": "GB/s", "cores": cores, "kind": "oracle",
+                               "sample": "%d of %d query heads over the whole step, f64 oracle, "
+                                         "one run %.3f s, scaled to all heads"
+                                         % (sel.size, w.num_qo_heads, oracle_s),
+                               "cpu_model": cpu_model()}
+    print(json.dumps(res), flush=True)
 
 
 def block_sparse(args, torch, B, PD, workloads, dev):

@@ -124,7 +124,11 @@ int paged_csr_build(int32_t batch, int32_t page_size, int32_t num_pool_pages,
  * the target uncalibrated; this floor is this library's calibration on
  * MI355X).  The target used is reported in info->target_wgs; `dtype`
  * (PD_DTYPE_*) selects the kernel whose occupancy defines S, and page_size
- * (>= 1) sets the floor; neither is used otherwise.
+ * (>= 1) sets the floor; neither is used otherwise.  head_dim 512 plans the
+ * paged-MLA kernel (paged_mla_decode_partial; num_kv_heads must be 1): its
+ * workgroups own (chunk, q group) units of up to 64 query heads, so a chunk
+ * is ceil(Hq / 64) units (q_groups), as the pages' (chunk, KV head, q-head
+ * group) ownership allows.
  *
  * Outputs (HOST): request_indices[n] / kv_tile_indices[n] for n < N, in
  * request order (chunk t of request r covers its pages [t*c, (t+1)*c));
@@ -354,18 +358,61 @@ int paged_sparse_expand_blocks(const int32_t *block_ids, int32_t num_requests,
                                int32_t num_blocks, int32_t *rows, void *stream);
 
 /* ------------------------------------------------------------------------
+ * paged_mla_decode_partial -- sparse-paged-decode doc, the DSA section (the
+ * recommended kernel generalization: a row stride plus a second key stream,
+ * as paged-MLA kernels take a latent and a rope part).
+ *
+ * The decode-v2 partial with one KV head and two key streams: for visible
+ * token t of request r (page table as in paged_decode_partial) and query head
+ * h, score = sm_scale * (q[r,h,:] . k[t][0:dim]) + sm_scale * (q_extra[r,h,:]
+ * . k_extra[t][0:extra_dim]), evaluated in base 2; the values are the latent
+ * rows k[t][0:dim] themselves (the latent serves as key and value, the
+ * output projection is applied by the caller).  Output rows are normalized
+ * per chunk with log2 LSEs, exactly like paged_decode_partial, so
+ * paged_merge_states (head_dim = dim) finishes split requests.
+ *
+ * Layouts (DEVICE): q [batch, Hq, dim] and q_extra [batch, Hq, extra_dim]
+ * contiguous fp16; k_pool element (page p, entry e, d) at p*k_page_stride +
+ * e*k_token_stride + d, the row holding at least `dim` elements (e.g. the
+ * latent followed by an indexer key: a row stride of 640 for dim 512);
+ * k_extra_pool likewise with x_page_stride / x_token_stride.  Both pools are
+ * addressed through the same indices: page_size 1 views of dense [B, Cap,
+ * row] allocations and [pages, page_size, row] pools both fit.  Pointers
+ * 16-byte aligned, strides multiples of 8 elements.  The plan comes from
+ * paged_decode_plan(head_dim = dim, num_kv_heads = 1).  Outputs: v_partial
+ * [num_chunks, Hq, dim] fp32, lse_partial [num_chunks, Hq] fp32; an empty
+ * chunk writes zeros and -inf.
+ *
+ * Supported: dtype PD_DTYPE_FP16, dim 512, extra_dim 64, Hq in {16, 32, 64,
+ * 128}; anything else returns PD_E_UNSUPPORTED before any launch.  Launch
+ * errors return PD_E_HIP; device faults surface at the next synchronization.
+ * ---------------------------------------------------------------------- */
+int paged_mla_decode_partial(const void *q, const void *q_extra, const void *k_pool,
+                             const void *k_extra_pool, int64_t k_page_stride,
+                             int64_t k_token_stride, int64_t x_page_stride,
+                             int64_t x_token_stride, int32_t dim, int32_t extra_dim,
+                             int32_t dtype, const int32_t *indices, const int32_t *indptr,
+                             const int32_t *last_page_len, const int32_t *first_page_offset,
+                             const int32_t *request_indices, const int32_t *kv_tile_indices,
+                             int32_t num_chunks, int32_t pages_per_chunk, int32_t batch,
+                             int32_t num_qo_heads, int32_t page_size, float sm_scale,
+                             float *v_partial, float *lse_partial, void *stream);
+
+/* ------------------------------------------------------------------------
  * Helpers shared by the plan and the launcher, so the two cannot drift
  * (PR #984 kernel commit: the query-heads-per-workgroup and wave-count
  * helpers exported next to the kernels).
  * ---------------------------------------------------------------------- */
-/* Query heads one workgroup serves for group size G and head dim D (always
- * G: one workgroup per KV head), or a negative code if unsupported. */
+/* Query heads one workgroup serves for group size G and head dim D (G: one
+ * workgroup per KV head; head_dim 512, the paged-MLA kernel: min(G, 64)), or
+ * a negative code if unsupported. */
 int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dtype);
 
 /* (chunk, KV head) units the device holds resident at once for this shape:
  * compute units x resident partial-kernel workgroups per CU (HIP occupancy
  * query) x units per workgroup, on `device` (-1: the current device).
- * Returns the count, or a negative code. */
+ * head_dim 512 with one KV head counts paged-MLA workgroups.  Returns the
+ * count, or a negative code. */
 int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t head_dim,
                                     int32_t dtype, int32_t num_kv_heads);
 

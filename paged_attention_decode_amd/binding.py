@@ -33,7 +33,7 @@ EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
             "paged_cascade_detect", "paged_cascade_split", "paged_cascade_layout",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
-            "paged_sparse_csr", "paged_sparse_expand_blocks",
+            "paged_sparse_csr", "paged_sparse_expand_blocks", "paged_mla_decode_partial",
             "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
             "paged_fastdiv_eval"]
 
@@ -71,6 +71,9 @@ _SIGS = {
                                  i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                  vp]),
     "paged_merge_states": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
+    "paged_mla_decode_partial": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp,
+                                       vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp,
+                                       vp]),
     "paged_decode_kernel_kind": (i32, [i32, i32, i32, i32, i64]),
     "paged_decode_set_kernel_choice": (i32, [i32]),
     "paged_cascade_detect": (i32, [i32, i32p, i32p, i32p, i32, i32, i32p, i32p, i32p]),
@@ -219,6 +222,20 @@ def paged_decode_partial(q, k_pool, v_pool, page_stride, token_stride, head_stri
         _dev(request_indices), _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch,
         num_qo_heads, num_kv_heads, head_dim, page_size, float(sm_scale), _dev(v_partial),
         _dev(lse_partial), _stream(stream)))
+
+
+def paged_mla_decode_partial(q, q_extra, k_pool, k_extra_pool, k_page_stride, k_token_stride,
+                             x_page_stride, x_token_stride, dim, extra_dim, dtype, indices,
+                             indptr, last_page_len, first_page_offset, request_indices,
+                             kv_tile_indices, num_chunks, pages_per_chunk, batch, num_qo_heads,
+                             page_size, sm_scale, v_partial, lse_partial, stream=None):
+    lib = load()
+    _check(lib.paged_mla_decode_partial(
+        _dev(q), _dev(q_extra), _dev(k_pool), _dev(k_extra_pool), k_page_stride, k_token_stride,
+        x_page_stride, x_token_stride, dim, extra_dim, dtype, _dev(indices), _dev(indptr),
+        _dev(last_page_len), _dev(first_page_offset), _dev(request_indices),
+        _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch, num_qo_heads, page_size,
+        float(sm_scale), _dev(v_partial), _dev(lse_partial), _stream(stream)))
 
 
 def paged_decode_fused(q, k_pool, v_pool, page_stride, token_stride, head_stride, dtype,

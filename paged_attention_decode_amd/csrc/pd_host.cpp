@@ -173,6 +173,10 @@ namespace {
 // paged pools (16-token pages) were unaffected.
 constexpr int64_t kMinChunkTokens = 32;
 
+// latent width of the paged-MLA kernel: a plan or shape query with this head
+// dim is for that kernel
+constexpr int32_t kMlaDim = 512;
+
 int64_t chunks_at(int32_t batch, const int32_t *indptr, int64_t c)
 {
     int64_t total = 0;
@@ -234,6 +238,11 @@ int64_t fit_target(int32_t batch, const int32_t *indptr, int64_t wg_per_chunk, i
 
 extern "C" int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dtype)
 {
+    if (head_dim == kMlaDim) {   // the paged-MLA kernel: q groups of up to 64 heads
+        if (dtype != PD_DTYPE_FP16)
+            return fail(PD_E_UNSUPPORTED, "paged MLA decode: fp16 only");
+        return mla_q_heads_per_wg(group_size);
+    }
     // G = 24 and 32 only on the MFMA kernel: fp16, head dim 128
     const bool g_ok = group_size == 1 || group_size == 2 || group_size == 4 ||
                       group_size == 8 || group_size == 12 || group_size == 16 ||
@@ -271,7 +280,16 @@ extern "C" int paged_decode_plan(int32_t batch, const int32_t *indptr,
         if (pages < 0) return fail(PD_E_INDPTR, "paged_decode_plan: indptr decreases");
         cmax = std::max(cmax, pages);
     }
-    const int64_t q_groups = 1;  // a workgroup serves every query head of its KV head
+    // a workgroup serves every query head of its KV head, except on the
+    // paged-MLA kernel (head_dim 512, one KV head): q groups of 64 heads
+    int64_t q_groups = 1;
+    if (head_dim == kMlaDim) {
+        if (num_kv_heads != 1)
+            return fail(PD_E_UNSUPPORTED, "paged_decode_plan: head_dim 512 (paged MLA) needs one KV head");
+        const int qh = mla_q_heads_per_wg(num_qo_heads);
+        if (qh < 0) return qh;
+        q_groups = (num_qo_heads + qh - 1) / qh;
+    }
     const int64_t wg_per_chunk = int64_t(num_kv_heads) * q_groups;
     if (chunks_at(batch, indptr, cmax) > PD_MAX_CHUNKS)
         return fail(PD_E_INFEASIBLE,

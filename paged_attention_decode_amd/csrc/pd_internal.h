@@ -56,6 +56,12 @@ PD_HD uint32_t fastdiv_q(const FastDiv &f, uint32_t n)
     return (t + ((n - t) >> f.s1)) >> f.s2;
 }
 
+// paged-MLA kernel (latent width 512, one KV head): query heads per
+// workgroup for a group of num_qo_heads (or a negative code), and the
+// workgroups resident at once on `device` (-1: current)
+int mla_q_heads_per_wg(int32_t num_qo_heads);
+int mla_resident_wgs(int32_t device, int32_t num_qo_heads);
+
 // thread-local error message
 void set_error(const std::string &msg);
 int fail(int code, const std::string &msg);

@@ -133,16 +133,17 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
     if (dv == 0) lse_out[oh] = m + __builtin_amdgcn_logf(wsum);
 }
 
-// One workgroup per (output row, head, dim slice) for heads whose D/4 float4
-// lanes are a multiple of 8: a slice is 32 dims, and the 256 threads are 32
-// row lanes x 8 dim lanes (each wave: 8 row lanes x 8 dim lanes, lane = 8 *
-// row lane + dim lane).  Row lane k merges rows k, k + 32, ... of the group
-// into a partial state (max, weight sum, weighted V) with the loads of up to
-// kSplitUnroll rows in flight: a group of up to 128 rows is loaded in a
-// single round trip.  The 8 row states of a wave are combined by a butterfly
-// of lane swaps (xor 8, 16, 32), the 4 wave states through LDS.  Slicing the
-// dims spreads one (row, head) over several CUs; the merge runs right after
-// the partial kernel and is bound by load latency, not bandwidth.
+// One workgroup per (output row, head, dim slice) for heads whose D is a
+// multiple of 32: a slice is DL float4 dim lanes (DL = 8, 32 dims, for heads up
+// to 128 wide; DL = 32, 128 dims, for wider heads such as 512-wide latent
+// rows), and the 256 threads are 256 / DL row lanes x DL dim lanes (lane =
+// DL * row lane + dim lane within each wave).  Row lane k merges rows k, k +
+// 256 / DL, ... of the group into a partial state (max, weight sum, weighted
+// V) with the loads of up to kSplitUnroll rows in flight.  The row states of a
+// wave are combined by a butterfly of lane swaps (xor DL ... 32), the 4 wave
+// states through LDS.  Slicing the dims spreads one (row, head) over several
+// CUs; the merge runs right after the partial kernel and is bound by load
+// latency, not bandwidth.
 constexpr int kSplitUnroll = 4;
 
 // State of a partial merge: running max m (NaN once a NaN lse was seen),
@@ -184,6 +185,7 @@ __device__ __forceinline__ float4 shfl_xor4(const float4 &v, int mask)
                        __shfl_xor(v.w, mask));
 }
 
+template <int DL>
 __global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restrict__ v_in,
                                                           const float *__restrict__ lse_in,
                                                           const int32_t *__restrict__ o_indptr,
@@ -192,15 +194,14 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restric
                                                           float *__restrict__ lse_out)
 {
     using V = float4;
-    constexpr int DL = 8;                        // float4 dim lanes per slice
     constexpr int SPLIT = 256 / DL;              // row lanes
     __shared__ MState<V> s_st[4][DL];
-    const int slices = head_dim / (4 * DL);      // head_dim % 32 == 0, checked by the launcher
+    const int slices = head_dim / (4 * DL);      // a multiple of 4 * DL, checked by the launcher
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int dl_i = lane & (DL - 1);
-    const int k = wave * 8 + (lane >> 3);        // row lane
+    const int k = wave * (64 / DL) + lane / DL;  // row lane
     const int64_t ohs = blockIdx.x;              // (o * num_heads + h) * slices + slice
     const int64_t oh = ohs / slices;
     const int dv = int(ohs - oh * slices) * DL + dl_i;
@@ -245,9 +246,9 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restric
         }
     }
     if (nan_seen) st.m = NAN;
-    // the 8 row lanes of the wave: lanes dl_i, dl_i + 8, ..., dl_i + 56
+    // the row lanes of the wave: lanes dl_i, dl_i + DL, ...
 #pragma unroll
-    for (int mask = 8; mask < 64; mask <<= 1) {
+    for (int mask = DL; mask < 64; mask <<= 1) {
         MState<V> y;
         y.m = __shfl_xor(st.m, mask);
         y.w = __shfl_xor(st.w, mask);
@@ -386,11 +387,17 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (vec4 && head_dim % 32 == 0) {
+    if (vec4 && head_dim % 512 == 0) {
+        // wide heads: one workgroup per (output row, head, 128-dim slice)
+        const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / 128);
+        if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
+        hipLaunchKernelGGL(merge_slice_kernel<32>, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
+                           lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
+    } else if (vec4 && head_dim % 32 == 0) {
         // one workgroup per (output row, head, 32-dim slice)
         const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / 32);
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
-        hipLaunchKernelGGL(merge_slice_kernel, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
+        hipLaunchKernelGGL(merge_slice_kernel<8>, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
                            lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
     } else if (head_dim / w <= 256) {
         // one workgroup per (output row, head), rows split across lanes

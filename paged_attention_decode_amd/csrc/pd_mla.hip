@@ -1,0 +1,519 @@
+// Split-KV partial attention with a second key stream (paged MLA / DSA
+// decode), for gfx950.
+//
+// Method: mlxcel docs, "Sparse paged decode", the DSA section.  For a visible
+// token t the score is sm_scale * (q . k[t][0:Dim]) + sm_scale * (q_extra .
+// k_extra[t]): the first term reads the latent part of rows of a K
+// allocation whose rows are RowStride >= Dim elements wide (the latent plus
+// the indexer key), the second a pool of its own (the rope keys) through the
+// same page table.  There is one KV head, so every query head attends every
+// token.  The latent rows k[t][0:Dim] are also the values (the latent serves
+// as key and value; the output projection is applied outside).  Everything
+// else -- page table, chunk ownership, base-2 scores, normalized partial rows
+// with log2 LSEs -- is the decode-v2 partial (PR #984 body item 2).
+//
+// gfx950 mapping.  Dim = 512 and ExtraDim = 64: a token's key is 576 halves.
+// A workgroup is one (chunk, q group) unit of 64 query heads, one wave per 16
+// heads (a group of 16 or 32 heads leaves waves idle in the products; those
+// waves still move their share of every tile).  Tiles of 32 tokens x 576
+// halves are staged in LDS (two stages) and shared by the waves: each key and
+// value element is fetched from memory once per unit.  Per 32-token tile a
+// wave computes, for each 16-token half,
+//   S^T [16 tokens x 16 heads] = K [16 x 576] . Q^T [576 x 16]
+// with 18 v_mfma_f32_16x16x32_f16 (Q^T read from an LDS copy), then one softmax
+// update over the 32 tokens and
+//   O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] . P^T [32 x 16 heads]
+// with 32 v_mfma_f32_16x16x32_f16, V^T read from the LDS tile with the
+// transpose read ds_read_b64_tr_b16.  The lane layouts are those of the
+// decode-v2 MFMA kernel: a lane owns one head's running max and sum and 128 of
+// its output dims, so a rescale is a per-lane scalar.
+//
+// The q groups of one chunk read the same tiles.  Workgroup ids are dealt to
+// the 8 XCDs round robin, so the ids are arranged to put the q groups of a
+// chunk on one XCD, where the second reader finds the tiles in its L2.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "pd_device.h"
+#include "pd_internal.h"
+
+namespace pd {
+namespace {
+
+constexpr int kDim = 512;                     // latent: keys and values
+constexpr int kExtra = 64;                    // second key stream
+constexpr int kKey = kDim + kExtra;           // key halves per token
+constexpr int kPieces = kKey / 8;             // 16-byte pieces per token (64 latent + 8 extra)
+constexpr int kTile = 32;                     // tokens per LDS stage
+constexpr int kRowBytes = kKey * 2;           // LDS row: 1152 bytes, 9 blocks of 128
+
+// LDS swizzle.  Piece c (16 bytes) of row j is stored at piece c ^ swz(j),
+// i.e. permuted within its 128-byte block; rows are 1152 bytes, so odd rows
+// start half way into a 256-byte bank line (64 banks of 4 bytes).  With
+// swz(j) = 2*((j/2)%4) + (j/8)%2 both read patterns hit distinct banks: the
+// 16 rows a 16-byte read serves per pass (key and query fragments, one piece
+// each) land on 16 distinct 16-byte slots of a bank line, and the 8 rows of
+// two 16-lane groups of a transpose read (values, a 32-byte pair each) on 8
+// distinct 32-byte slots.  (Counters showed the padded-row layout losing
+// about 40% of LDS time to bank conflicts.)
+__device__ __forceinline__ int swz(int j) { return 2 * ((j >> 1) & 3) + ((j >> 3) & 1); }
+constexpr int kXcds = 8;
+constexpr int kWaves = 4;
+constexpr int kGroupHeads = 16 * kWaves;      // query heads per workgroup
+constexpr int kOffRing = 4;                   // tiles of row offsets kept (three ahead)
+#ifndef PD_MLA_KEY_AHEAD
+#define PD_MLA_KEY_AHEAD 3
+#endif
+#ifndef PD_MLA_VALUE_AHEAD
+#define PD_MLA_VALUE_AHEAD 6
+#endif
+constexpr int kKeyAhead = PD_MLA_KEY_AHEAD;   // key steps whose LDS reads run ahead of the products
+constexpr int kValueAhead = PD_MLA_VALUE_AHEAD;   // value steps likewise
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kMfma = 0x008;
+constexpr int kDsRead = 0x100;
+constexpr float kMlaNoMax = -1e30f;           // finite "no score yet" running max
+constexpr float kMlaLazyMargin = 8.0f;        // log2 units: p <= 2^8 between rescales
+
+// 16 zero bytes in device memory: the source of every masked piece (tokens
+// past the chunk, tiles past the last), so that all loads of the pipeline are
+// unconditional and masked rows reach LDS as zeros
+__device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
+
+struct MlaArgs {
+    const _Float16 *q;      // [B, Hq, 512]
+    const _Float16 *qx;     // [B, Hq, 64]
+    const char *k;          // latent rows (bytes)
+    const char *x;          // second-stream rows (bytes)
+    int64_t k_page_stride, k_token_stride, x_page_stride, x_token_stride;   // elements
+    const int32_t *indices, *indptr, *lpl, *fpo, *req_idx, *tile_idx;
+    int32_t num_chunks, num_qo_heads, page_size, pages_per_chunk, q_groups;
+    FastDiv fd;
+    float scale_log2;
+    float *v_out;           // [N, Hq, 512]
+    float *lse_out;         // [N, Hq]
+};
+
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_partial_kernel(MlaArgs a)
+{
+    constexpr int NT = 64 * kWaves;
+    constexpr int PIECES = kTile * kPieces;
+    constexpr int PPT = (PIECES + NT - 1) / NT;   // pieces each thread moves per tile
+
+    __shared__ __align__(16) char s_tile[2][kTile * kRowBytes];
+    __shared__ __align__(16) char s_q[kGroupHeads * kRowBytes];
+    __shared__ int64_t s_koff[kOffRing][kTile];   // byte offset of a token's rows; -1 = masked
+    __shared__ int64_t s_xoff[kOffRing][kTile];
+
+    // workgroup id -> (chunk, q group); the q groups of a chunk share id mod 8
+    const int qgs = a.q_groups;
+    const int b = blockIdx.x;
+    const int blk = b / (kXcds * qgs);
+    const int rem = b - blk * kXcds * qgs;
+    const int qg = rem / kXcds;
+    const int n = blk * kXcds + (rem - qg * kXcds);
+    if (n >= a.num_chunks) return;                // padding of the id space
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    const int r = ld_uniform(a.req_idx + n);
+    const int t = ld_uniform(a.tile_idx + n);
+    const int pbeg = ld_uniform(a.indptr + r);
+    const int npages = ld_uniform(a.indptr + r + 1) - pbeg;
+    const int fpo = ld_uniform(a.fpo + r);
+    const int lpl = ld_uniform(a.lpl + r);
+    const int ps = a.page_size;
+    const int64_t n_r = npages > 0 ? int64_t(npages - 1) * ps + lpl - fpo : 0;
+    const int64_t span = int64_t(a.pages_per_chunk) * ps;
+    const int64_t tok0 = max(int64_t(0), int64_t(t) * span - fpo);
+    const int64_t tok1 = min(n_r, int64_t(t + 1) * span - fpo);
+    const int ntok = tok1 > tok0 ? int(tok1 - tok0) : 0;
+    const int ntiles = (ntok + kTile - 1) / kTile;
+
+    const int head0 = qg * kGroupHeads + wave * 16;     // the wave's first head
+    const bool active = head0 < a.num_qo_heads;         // wave-uniform (groups of 16)
+    const int head = head0 + col;
+
+    // The workgroup's 64 query rows (latent then extra dims, 576 halves per
+    // head) are staged once in LDS, rows padded like the tiles; the score
+    // product reads its Q^T operand from there (lane l: head l%16 of the
+    // wave, key dims 32*kc + 8*(l/16) .. + 7).  Held in registers they would
+    // leave too few for the loads in flight.
+    {
+        constexpr int QPIECES = kGroupHeads * kPieces;
+#pragma unroll
+        for (int k = 0; k < QPIECES / NT; ++k) {
+            const int p = tid + k * NT;
+            const int hl = p / kPieces;               // head of the group
+            const int c = p - hl * kPieces;
+            const int h = min(qg * kGroupHeads + hl, a.num_qo_heads - 1);
+            const int64_t qrow = int64_t(r) * a.num_qo_heads + h;
+            const uint4 v = c < kDim / 8
+                ? *reinterpret_cast<const uint4 *>(a.q + qrow * kDim + 8 * c)
+                : *reinterpret_cast<const uint4 *>(a.qx + qrow * kExtra + 8 * (c - kDim / 8));
+            *reinterpret_cast<uint4 *>(s_q + hl * kRowBytes + 16 * (c ^ swz(hl))) = v;
+        }
+    }
+
+    // Row ids and byte offsets.  Every load of the pipeline is issued
+    // unconditionally (a masked piece reads the zero block), so the compiler's
+    // wait counts before each use cover exactly the loads that use waits for.
+    //
+    // Page id of token tid % 32 of tile i (clamped into the request's pages;
+    // tiles past the chunk load a valid id that is never used).
+    auto load_id = [&](int i) -> int32_t {
+        const int64_t tok = min(tok0 + int64_t(i) * kTile + (tid & (kTile - 1)), tok1 - 1);
+        const uint32_t pg = fastdiv_q(a.fd, uint32_t(fpo + max(tok, int64_t(0))));
+        return a.indices[pbeg + min(int64_t(pg), int64_t(npages - 1))];
+    };
+    // byte offsets of tile i's rows from its ids (one thread per token), kept
+    // in slot i % kOffRing; -1 marks a token outside the chunk
+    auto offsets = [&](int i, int32_t row) {
+        const int buf = i % kOffRing;
+        if (tid < kTile) {
+            const int64_t tok = tok0 + int64_t(i) * kTile + tid;
+            int64_t ko = -1, xo = -1;
+            if (tok < tok1) {
+                const uint32_t slot = uint32_t(fpo + tok);
+                const uint32_t pg = fastdiv_q(a.fd, slot);
+                const int64_t e = int64_t(slot - pg * uint32_t(ps));
+                ko = (int64_t(row) * a.k_page_stride + e * a.k_token_stride) * 2;
+                xo = (int64_t(row) * a.x_page_stride + e * a.x_token_stride) * 2;
+            }
+            s_koff[buf][tid] = ko;
+            s_xoff[buf][tid] = xo;
+        }
+    };
+    // Pieces a thread moves per tile: latent piece lc = tid % 64 of rows
+    // tid / 64 + 4*k (k < 8), and extra piece tid % 8 of row tid / 8.  The
+    // column is fixed per thread, so a piece's address is its row's offset
+    // (from LDS) plus a constant.  Two register sets: a tile's loads are
+    // issued one iteration before its pieces are stored to LDS.
+    constexpr int kLatPerThread = kTile * (kDim / 8) / NT;     // 8
+    static_assert(kTile * (kDim / 8) == kLatPerThread * NT && kTile * (kExtra / 8) == NT,
+                  "tile / thread layout");
+    const int lat_c = tid & 63;
+    const int lat_r = tid >> 6;
+    const int ext_c = tid & 7;
+    const int ext_r = tid >> 3;
+    uint4 pre[2][PPT];
+    const char *zero = reinterpret_cast<const char *>(&g_zero16);
+    auto load_tile = [&](int i, uint4 (&dst)[PPT]) {
+        const int buf = i % kOffRing;
+        const bool live = i < ntiles;
+#pragma unroll
+        for (int k = 0; k < kLatPerThread; ++k) {
+            const int64_t off = s_koff[buf][lat_r + 4 * k];
+            dst[k] = load_nt(live && off >= 0 ? a.k + off + 16 * lat_c : zero);
+        }
+        const int64_t xo = s_xoff[buf][ext_r];
+        dst[kLatPerThread] = load_nt(live && xo >= 0 ? a.x + xo + 16 * ext_c : zero);
+    };
+    auto store_tile = [&](const uint4 (&src)[PPT], int buf) {
+        char *t = s_tile[buf];
+#pragma unroll
+        for (int k = 0; k < kLatPerThread; ++k) {
+            const int j = lat_r + 4 * k;
+            *reinterpret_cast<uint4 *>(t + j * kRowBytes + 16 * (lat_c ^ swz(j))) = src[k];
+        }
+        *reinterpret_cast<uint4 *>(t + ext_r * kRowBytes + 16 * ((kDim / 8 + ext_c) ^ swz(ext_r))) =
+            src[kLatPerThread];
+    };
+
+    float m_run = kMlaNoMax;          // running max of this lane's head
+    float l_part = 0.f;               // this lane's share of its head's sum
+    float4_t acc[kDim / 16];          // O^T: dims 16*dt + 4*(l/16) + i of head l%16
+#pragma unroll
+    for (int dt = 0; dt < kDim / 16; ++dt) acc[dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    // transpose-read address of a 4-token x 16-dim block: row 4*(l/16) +
+    // (l%16)/4 of the subtile, halves 4*(l%4) of the dim block
+    //
+    // With the swizzle, lane l's read of row 4*g + r (g = l/16, r = (l%16)/4)
+    // at halves 16*dt + 4*(l%4), i.e. piece 2*dt + (l%4)/2, is at piece
+    // 2*(dt ^ t) + ((l%4)/2 ^ g/2) with t = 2*(g%2) + r/2 (the xor touching
+    // the low two bits of dt only): one base per value of dt % 4, plus
+    // 32 * (dt - dt % 4) bytes.
+    const int tr_r = col >> 2;
+    const int tr_t = 2 * (grp & 1) + (tr_r >> 1);
+    int tr_base[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        tr_base[d] = (4 * grp + tr_r) * kRowBytes + 32 * (d ^ tr_t) +
+                     16 * (((lane & 3) >> 1) ^ (grp >> 1)) + 8 * (lane & 1);
+
+    // One tile: S^T for both 16-token subtiles, one softmax update over its
+    // 32 tokens, then O^T += V^T . P^T as 32 products with K = 32 tokens.  The
+    // k order of the value product is the score layout's: lane l holds
+    // tokens 4*(l/16) + e of subtile 0 as k = 8*(l/16) + e and tokens
+    // 16 + 4*(l/16) + e as k = 8*(l/16) + 4 + e, so P^T needs no data
+    // movement and V^T is two transpose reads, one per subtile.
+    auto compute = [&](int i, int buf) {
+        const char *tile = s_tile[buf];
+        // key / query fragment kc of lane l is piece (4*kc + l/16) ^ swz(l%16)
+        // = 4*(kc ^ sb) + (l/16 ^ (swz & 3)), sb = swz / 4: the bases for even
+        // and odd kc differ
+        const int sw = swz(col);
+        const int sb = sw >> 2;
+        const int lo = 16 * (grp ^ (sw & 3));
+        const char *kr_even = tile + col * kRowBytes + lo + 64 * sb;
+        const char *kr_odd = tile + col * kRowBytes + lo - 64 * sb;
+        const char *qr_even = s_q + (wave * 16 + col) * kRowBytes + lo + 64 * sb;
+        const char *qr_odd = s_q + (wave * 16 + col) * kRowBytes + lo - 64 * sb;
+        float4_t sc0 = float4_t{0.f, 0.f, 0.f, 0.f};
+        float4_t sc1 = float4_t{0.f, 0.f, 0.f, 0.f};
+        // Fragment reads run ahead of the products (two key steps, four value
+        // steps), so each product waits for a read issued well before it: one
+        // wave per SIMD has no other wave to cover LDS latency.
+        auto kfrag = [&](int kc, half8_t &q, half8_t &k0, half8_t &k1) {
+            const char *kr = (kc & 1) ? kr_odd : kr_even;
+            const char *qr = (kc & 1) ? qr_odd : qr_even;
+            q = *reinterpret_cast<const half8_t *>(qr + 64 * kc);
+            k0 = *reinterpret_cast<const half8_t *>(kr + 64 * kc);
+            k1 = *reinterpret_cast<const half8_t *>(kr + 16 * kRowBytes + 64 * kc);
+        };
+        constexpr int KS = kPieces / 4;                    // 18 key steps
+        constexpr int KD = kKeyAhead + 1;                  // key fragment ring
+        half8_t fq[KD], fk0[KD], fk1[KD];
+#pragma unroll
+        for (int kc = 0; kc < KD - 1; ++kc) kfrag(kc, fq[kc], fk0[kc], fk1[kc]);
+#pragma unroll
+        for (int kc = 0; kc < KS; ++kc) {
+            if (kc + KD - 1 < KS)
+                kfrag(kc + KD - 1, fq[(kc + KD - 1) % KD], fk0[(kc + KD - 1) % KD],
+                      fk1[(kc + KD - 1) % KD]);
+            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fk0[kc % KD], fq[kc % KD], sc0, 0, 0, 0);
+            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fk1[kc % KD], fq[kc % KD], sc1, 0, 0, 0);
+        }
+        // the issue order the scheduler must keep: kKeyAhead steps of reads,
+        // then two products and one step of reads per step
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 3 * kKeyAhead, 0);
+#pragma unroll
+        for (int kc = 0; kc < KS - kKeyAhead; ++kc) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kMfma, 2 * kKeyAhead, 0);
+        float x[8];
+        float mb = -INFINITY;
+        const int base = i * kTile + 4 * grp;             // chunk-relative token of e = 0
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = base + e < ntok ? sc0[e] * a.scale_log2 : -INFINITY;
+            x[4 + e] = base + 16 + e < ntok ? sc1[e] * a.scale_log2 : -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mb = fmaxf(mb, x[e]);
+        mb = group_max4(mb);                               // over the tile's 32 tokens
+        const bool need = mb > m_run + kMlaLazyMargin;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float m_new = need ? mb : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < kDim / 16; ++dt) acc[dt] *= alpha;
+        }
+        half8_t pb;
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const _Float16 ph = _Float16(fast_exp2(x[e] - m_run));
+            pb[e] = ph;
+            ls += float(ph);              // the sum takes the weights the products use
+        }
+        l_part += ls;
+        auto vfrag = [&](int dt) -> half8_t {
+            const char *vd = tile + tr_base[dt & 3] + 32 * (dt & ~3);
+            const half4_t v0 = __builtin_bit_cast(
+                half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)vd));
+            const half4_t v1 = __builtin_bit_cast(
+                half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                             (lds_short4 *)(vd + 16 * kRowBytes)));
+            return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        constexpr int VS = kDim / 16;                      // 32 value steps
+        constexpr int VD = kValueAhead + 1;                // value fragment ring
+        half8_t fv[VD];
+#pragma unroll
+        for (int dt = 0; dt < VD - 1; ++dt) fv[dt] = vfrag(dt);
+#pragma unroll
+        for (int dt = 0; dt < VS; ++dt) {
+            if (dt + VD - 1 < VS) fv[(dt + VD - 1) % VD] = vfrag(dt + VD - 1);
+            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fv[dt % VD], pb, acc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kValueAhead, 1);
+#pragma unroll
+        for (int dt = 0; dt < VS - kValueAhead; ++dt) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(kMfma, kValueAhead, 1);
+    };
+
+    // Pipeline.  Before iteration i: LDS stage i%2 holds tile i, register
+    // set (i+1)%2 holds tile i+1 (loads in flight), the offsets of tile i+2
+    // are in their slot and id register (i+1)%2 holds tile i+3's ids.
+    // Iteration i loads tile i+4's ids into id register i%2 and tile i+2
+    // into set i%2 (whose tile i is in LDS already), computes tile i, writes
+    // tile i+3's offsets, stores set (i+1)%2 into stage (i+1)%2, and ends with
+    // the one barrier: every LDS region an iteration writes was last read
+    // before the previous iteration's barrier.  Loads are waited for one
+    // iteration after they are issued.  The loop is unrolled by two so that
+    // the register sets are named statically.
+    int32_t ids[2];
+    auto iteration = [&](int i, uint4 (&cur)[PPT], const uint4 (&nxt)[PPT], int32_t &id_cur,
+                         int32_t id_nxt) {
+        id_cur = load_id(i + 4);
+        load_tile(i + 2, cur);
+        if (active) compute(i, i & 1);
+        if (i + 3 < ntiles) offsets(i + 3, id_nxt);
+        if (i + 1 < ntiles) store_tile(nxt, (i + 1) & 1);
+        __syncthreads();
+    };
+    if (ntiles > 0) {
+        offsets(0, load_id(0));
+        offsets(1, load_id(1));
+        offsets(2, load_id(2));
+        ids[1] = load_id(3);
+        __syncthreads();
+        load_tile(0, pre[0]);
+        load_tile(1, pre[1]);
+        store_tile(pre[0], 0);
+        __syncthreads();
+        for (int i = 0; i < ntiles; i += 2) {
+            iteration(i, pre[0], pre[1], ids[0], ids[1]);
+            if (i + 1 < ntiles) iteration(i + 1, pre[1], pre[0], ids[1], ids[0]);
+        }
+    }
+
+    if (!active) return;
+    // head sum over the four 16-lane groups; each group holds 4 of every 16
+    // dims, so the accumulators need no combine
+    const float l = group_sum4(l_part);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float *vrow = a.v_out + (int64_t(n) * a.num_qo_heads + head) * kDim + 4 * grp;
+#pragma unroll
+    for (int dt = 0; dt < kDim / 16; ++dt) {
+        const float4_t o = acc[dt] * inv;
+        *reinterpret_cast<float4 *>(vrow + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (grp == 0)
+        a.lse_out[int64_t(n) * a.num_qo_heads + head] = l > 0.f ? m_run + fast_log2(l) : -INFINITY;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// Query heads one MLA workgroup serves, or a negative code if the group is
+// not supported.
+int mla_q_heads_per_wg(int32_t num_qo_heads)
+{
+    if (num_qo_heads != 16 && num_qo_heads != 32 && num_qo_heads != 64 && num_qo_heads != 128)
+        return fail(PD_E_UNSUPPORTED, "paged MLA decode: query heads must be 16, 32, 64 or 128");
+    return num_qo_heads < kGroupHeads ? num_qo_heads : kGroupHeads;
+}
+
+// Resident MLA workgroups on `device` (CUs x workgroups per CU).
+int mla_resident_wgs(int32_t device, int32_t num_qo_heads)
+{
+    const int qh = mla_q_heads_per_wg(num_qo_heads);
+    if (qh < 0) return qh;
+    int dev = device;
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess)
+        return fail(PD_E_HIP, "paged MLA decode: no current device");
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return fail(PD_E_HIP, "paged MLA decode: cannot query CU count");
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess)
+        return fail(PD_E_HIP, "paged MLA decode: cannot select device");
+    int per_cu = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void *>(mla_partial_kernel), 64 * kWaves, 0);
+    if (prev >= 0 && prev != dev && hipSetDevice(prev) != hipSuccess)
+        return fail(PD_E_HIP, "paged MLA decode: cannot restore device");
+    if (e != hipSuccess || per_cu < 1)
+        return fail(PD_E_HIP, "paged MLA decode: occupancy query failed");
+    return cus * per_cu;
+}
+
+}  // namespace pd
+
+using namespace pd;
+
+extern "C" int paged_mla_decode_partial(
+    const void *q, const void *q_extra, const void *k_pool, const void *k_extra_pool,
+    int64_t k_page_stride, int64_t k_token_stride, int64_t x_page_stride,
+    int64_t x_token_stride, int32_t dim, int32_t extra_dim, int32_t dtype,
+    const int32_t *indices, const int32_t *indptr, const int32_t *last_page_len,
+    const int32_t *first_page_offset, const int32_t *request_indices,
+    const int32_t *kv_tile_indices, int32_t num_chunks, int32_t pages_per_chunk, int32_t batch,
+    int32_t num_qo_heads, int32_t page_size, float sm_scale, float *v_partial,
+    float *lse_partial, void *stream)
+{
+    if (!q || !q_extra || !k_pool || !k_extra_pool || !indices || !indptr || !last_page_len ||
+        !first_page_offset || !request_indices || !kv_tile_indices || !v_partial || !lse_partial)
+        return fail(PD_E_NULL, "paged_mla_decode_partial: null pointer");
+    if (num_chunks < 0 || pages_per_chunk < 1 || batch < 1 || page_size < 1 || num_qo_heads < 1 ||
+        !(sm_scale > 0.f))
+        return fail(PD_E_ARG, "paged_mla_decode_partial: bad sizes");
+    if (dtype != PD_DTYPE_FP16 || dim != kDim || extra_dim != kExtra)
+        return fail(PD_E_UNSUPPORTED,
+                    "paged_mla_decode_partial: only fp16 with dim 512 and extra_dim 64");
+    const int qh = mla_q_heads_per_wg(num_qo_heads);
+    if (qh < 0) return qh;
+    if (!aligned16(q) || !aligned16(q_extra) || !aligned16(k_pool) || !aligned16(k_extra_pool) ||
+        (k_page_stride * 2) % 16 || (k_token_stride * 2) % 16 || (x_page_stride * 2) % 16 ||
+        (x_token_stride * 2) % 16 || k_page_stride < 0 || k_token_stride < 0 ||
+        x_page_stride < 0 || x_token_stride < 0)
+        return fail(PD_E_UNSUPPORTED,
+                    "paged_mla_decode_partial: pools and queries must be 16-byte aligned");
+    if (num_chunks == 0) return PD_OK;
+    if (num_chunks > PD_MAX_CHUNKS)
+        return fail(PD_E_ARG, "paged_mla_decode_partial: too many chunks");
+    MlaArgs a;
+    a.q = static_cast<const _Float16 *>(q);
+    a.qx = static_cast<const _Float16 *>(q_extra);
+    a.k = static_cast<const char *>(k_pool);
+    a.x = static_cast<const char *>(k_extra_pool);
+    a.k_page_stride = k_page_stride;
+    a.k_token_stride = k_token_stride;
+    a.x_page_stride = x_page_stride;
+    a.x_token_stride = x_token_stride;
+    a.indices = indices;
+    a.indptr = indptr;
+    a.lpl = last_page_len;
+    a.fpo = first_page_offset;
+    a.req_idx = request_indices;
+    a.tile_idx = kv_tile_indices;
+    a.num_chunks = num_chunks;
+    a.num_qo_heads = num_qo_heads;
+    a.page_size = page_size;
+    a.pages_per_chunk = pages_per_chunk;
+    a.q_groups = (num_qo_heads + kGroupHeads - 1) / kGroupHeads;
+    a.fd = make_fastdiv(uint32_t(page_size));
+    a.scale_log2 = float(double(sm_scale) * 1.4426950408889634);
+    a.v_out = v_partial;
+    a.lse_out = lse_partial;
+    const int64_t blocks = (int64_t(num_chunks) + kXcds - 1) / kXcds * kXcds * a.q_groups;
+    hipLaunchKernelGGL(mla_partial_kernel, dim3(uint32_t(blocks)), dim3(64 * kWaves), 0,
+                       static_cast<hipStream_t>(stream), a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PD_E_HIP, std::string("paged_mla_decode_partial: launch failed: ") +
+                                  hipGetErrorString(err));
+    return PD_OK;
+}

@@ -49,6 +49,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "pd_device.h"
 #include "pd_internal.h"
 
 namespace pd {
@@ -69,17 +70,6 @@ constexpr float kLazyMargin = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr float kNoMax = -1e30f;      // finite "no score yet" running max
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer descriptor dword 3 (32-bit data)
 constexpr int kLoadNT = 2;                 // cache policy "nt": K/V rows are read exactly once
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// streaming (non-temporal) 16-byte load
-__device__ __forceinline__ uint4 load_nt(const void *p)
-{
-    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 union Row16 {
     uint4 u;
@@ -105,9 +95,6 @@ struct PartialArgs {
     float *lse_final;    // [B, Hq]
     int32_t *counters;   // [B, Hkv], zero between launches
 };
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
@@ -149,33 +136,6 @@ __device__ __forceinline__ void row_bcast_all(float x, float (&out)[16])
     out[13] = row_bcast<13>(x);
     out[14] = row_bcast<14>(x);
     out[15] = row_bcast<15>(x);
-}
-
-// Read-only plan data (page table, request and chunk arrays) through the
-// scalar cache: the address is wave-uniform, and an address-space-4 (constant)
-// pointer lets the compiler use a scalar load instead of a vector load plus
-// readfirstlane.  Nothing in the kernel writes these arrays.
-__device__ __forceinline__ int32_t ld_uniform(const int32_t *p)
-{
-    typedef const __attribute__((address_space(4))) int32_t constant_i32;
-    return *(constant_i32 *)p;   // generic -> constant address space
-}
-
-// gfx950 permlane swaps.  After swap32(a, b) the lanes of the lower half
-// hold (a of lane l, a of lane l + 32) and those of the upper half hold (b of
-// lane l - 32, b of lane l): each half gets the (lower, upper) pair of one of
-// the two values.  swap16 does the same for each pair of 16-lane rows (even
-// row: the pair of a, odd row: the pair of b).  They are issued as inline
-// assembly because the compiler's builtins for them hand back the first
-// result in place of the second; the nop covers the wait states a permlane
-// needs after a VALU write of its operands.
-__device__ __forceinline__ void swap32(float &a, float &b)
-{
-    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap16(float &a, float &b)
-{
-    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
 // One level of the reduce-scatter combine of softmax states: the lane keeps
@@ -982,34 +942,7 @@ constexpr int token_rows_per_step()
 // consecutive halves each (together row r of a 4 x 16 tile) and lane c
 // receives column c.  Each wave has its own LDS tile, rows padded by 16
 // bytes against bank conflicts.
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per V row of the tile
-
-// max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float group_max4(float x)
-{
-    float a = x, b = x;
-    swap16(a, b);
-    x = fmaxf(a, b);
-    a = x;
-    b = x;
-    swap32(a, b);
-    return fmaxf(a, b);
-}
-__device__ __forceinline__ float group_sum4(float x)
-{
-    float a = x, b = x;
-    swap16(a, b);
-    x = a + b;
-    a = x;
-    b = x;
-    swap32(a, b);
-    return a + b;
-}
 
 template <int G, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
@@ -1548,6 +1481,12 @@ extern "C" int paged_decode_default_target_wgs(int32_t device, int32_t group_siz
 {
     if (num_kv_heads < 1)
         return fail(PD_E_ARG, "paged_decode_default_target_wgs: num_kv_heads must be >= 1");
+    if (head_dim == 512) {   // the paged-MLA kernel: one unit per workgroup
+        if (num_kv_heads != 1 || dtype != PD_DTYPE_FP16)
+            return fail(PD_E_UNSUPPORTED,
+                        "paged_decode_default_target_wgs: paged MLA needs fp16 and one KV head");
+        return mla_resident_wgs(device, group_size);
+    }
     const Choice c = pick(dtype, head_dim, group_size, 16, int64_t(num_kv_heads) * head_dim,
                           false, !g_force_token_kernel, num_kv_heads, !g_no_mfma);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_default_target_wgs: unsupported shape");

@@ -356,6 +356,99 @@ class BlockSparseDecode:
 
 
 
+
+def _row_pool_strides(pool: torch.Tensor):
+    """Element strides (page, entry) of a [pages, page_size, row] pool with
+    contiguous rows."""
+    if pool.dim() != 3 or pool.stride(2) != 1:
+        raise ValueError("MLA pools must be [pages, page_size, row] with contiguous rows")
+    return pool.stride(0), pool.stride(1)
+
+
+class MlaDecode:
+    """Paged MLA / DSA decode of one batch (sparse-paged-decode doc, the DSA
+    section): one KV head; scores over the latent (the first `dim` elements
+    of each k_pool row) plus a second key stream (k_extra_pool); the latent
+    rows are the values.  The plan is paged_decode_plan's with head_dim =
+    dim (q groups of 64 heads); each step is one partial launch plus a merge
+    when a request was split."""
+
+    def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
+                 dim: int = 512, extra_dim: int = 64, target_wgs: int = 0,
+                 fixed_pages_per_chunk: int = 0, device="cuda"):
+        indptr = np.asarray(csr["indptr"], np.int32)
+        self.indptr = indptr
+        self.batch = indptr.size - 1
+        self.page_size, self.num_qo_heads = page_size, num_qo_heads
+        self.dim, self.extra_dim = dim, extra_dim
+        self.num_pool_pages = num_pool_pages
+        B.csr_validate(self.batch, page_size, num_pool_pages, indptr, csr["indices"],
+                       csr["last_page_len"], csr["first_page_offset"], csr.get("seq_lens"))
+        info, ri, ti, oi = B.paged_decode_plan(indptr, num_qo_heads, 1, dim, target_wgs,
+                                               fixed_pages_per_chunk, dtype=B.PD_DTYPE_FP16,
+                                               page_size=page_size)
+        self.info, self.request_indices, self.kv_tile_indices, self.o_indptr = info, ri, ti, oi
+        self.device = torch.device(device)
+        idx = np.asarray(csr["indices"], np.int32)
+        self.d_indices = _dev_i32(idx if idx.size else np.zeros(1, np.int32), self.device)
+        self.d_indptr = _dev_i32(indptr, self.device)
+        self.d_lpl = _dev_i32(csr["last_page_len"], self.device)
+        self.d_fpo = _dev_i32(csr["first_page_offset"], self.device)
+        self.d_req = _dev_i32(ri, self.device)
+        self.d_tile = _dev_i32(ti, self.device)
+        self.d_oindptr = _dev_i32(oi, self.device)
+        n = info.num_chunks
+        self.v_partial = torch.empty((n, num_qo_heads, dim), dtype=torch.float32,
+                                     device=self.device)
+        self.lse_partial = torch.empty((n, num_qo_heads), dtype=torch.float32, device=self.device)
+        if info.needs_merge:
+            self.out = torch.empty((self.batch, num_qo_heads, dim), dtype=torch.float32,
+                                   device=self.device)
+            self.lse = torch.empty((self.batch, num_qo_heads), dtype=torch.float32,
+                                   device=self.device)
+        else:   # write-O-directly
+            self.out, self.lse = self.v_partial, self.lse_partial
+
+    def plan_summary(self) -> dict:
+        i = self.info
+        return dict(pages_per_chunk=i.pages_per_chunk, num_chunks=i.num_chunks,
+                    num_wgs=i.num_wgs, q_groups=i.q_groups, needs_merge=bool(i.needs_merge),
+                    target_wgs=i.target_wgs, workspace_bytes=i.workspace_bytes)
+
+    def partial(self, q, q_extra, k_pool, k_extra_pool, sm_scale, stream=None):
+        kps, kts = _row_pool_strides(k_pool)
+        xps, xts = _row_pool_strides(k_extra_pool)
+        B.paged_mla_decode_partial(q, q_extra, k_pool, k_extra_pool, kps, kts, xps, xts,
+                                   self.dim, self.extra_dim, _pd_dtype(q), self.d_indices,
+                                   self.d_indptr, self.d_lpl, self.d_fpo, self.d_req,
+                                   self.d_tile, self.info.num_chunks, self.info.pages_per_chunk,
+                                   self.batch, self.num_qo_heads, self.page_size, sm_scale,
+                                   self.v_partial, self.lse_partial, stream)
+
+    def merge(self, stream=None):
+        if self.info.needs_merge:
+            B.paged_merge_states(self.v_partial, self.lse_partial, self.d_oindptr, self.batch,
+                                 self.num_qo_heads, self.dim, self.out, self.lse, stream)
+
+    def run(self, q, q_extra, k_pool, k_extra_pool, sm_scale, stream=None):
+        """One decode step: returns (out [B, Hq, dim] fp32, lse [B, Hq] fp32,
+        log2 units); the tensors are this object's buffers."""
+        if q.shape != (self.batch, self.num_qo_heads, self.dim) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, dim] tensor")
+        if q_extra.shape != (self.batch, self.num_qo_heads, self.extra_dim) or \
+                not q_extra.is_contiguous():
+            raise ValueError("q_extra must be a contiguous [B, Hq, extra_dim] tensor")
+        if not (q.dtype == q_extra.dtype == k_pool.dtype == k_extra_pool.dtype == torch.float16):
+            raise TypeError("paged MLA decode takes fp16 queries and pools")
+        for pool, width in ((k_pool, self.dim), (k_extra_pool, self.extra_dim)):
+            if pool.dim() != 3 or pool.shape[0] < self.num_pool_pages or \
+                    pool.shape[1] != self.page_size or pool.shape[2] < width:
+                raise ValueError("pools must be [>= %d pages, %d, >= row width] (got %s)"
+                                 % (self.num_pool_pages, self.page_size, tuple(pool.shape)))
+        self.partial(q, q_extra, k_pool, k_extra_pool, sm_scale, stream)
+        self.merge(stream)
+        return self.out, self.lse
+
 def graph_time(fn, n: int = 120, per_graph: int = 30) -> float:
     """GPU seconds per call of fn(i): per_graph calls are captured once in a
     HIP graph and the graph is replayed n // per_graph times between events

@@ -1,0 +1,175 @@
+"""GPU parity of the paged-MLA / DSA decode (second key stream) against the
+f64 oracle (needs an MI355X).
+
+Every partial row and every final output is compared element by element
+(fp16 pools, fp32 accumulation: max |diff| <= 2e-3 on outputs, <= 1e-3 on
+log2 LSEs; -inf LSEs must match exactly); plans are the library's and are
+checked against the oracle's exhaustive plan.  Unused pages, unselected rows
+and the indexer-key columns of every row are NaN in the poisoned cases, so a
+read outside the page table or past the latent shows up as NaN.  At full size
+the oracle computes a sample of query heads.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from paged_attention_decode_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from paged_attention_decode_amd import binding as B  # noqa: E402
+from paged_attention_decode_amd import decode as PD  # noqa: E402
+
+NTHREADS = min(16, os.cpu_count() or 1)
+DEV = torch.device("cuda:0")
+TOL_V, TOL_L = 2e-3, 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def check(got_v, got_l, ref_v, ref_l, what):
+    got_v = np.asarray(got_v, np.float64)
+    got_l = np.asarray(got_l, np.float64)
+    assert got_v.shape == ref_v.shape and got_l.shape == ref_l.shape, what
+    assert np.all(np.isfinite(got_v)), what + ": non-finite output"
+    inf_ref = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(got_l), inf_ref), what + ": -inf LSE pattern differs"
+    dv = float(np.max(np.abs(got_v - ref_v))) if got_v.size else 0.0
+    fin = ~inf_ref
+    dl = float(np.max(np.abs(got_l[fin] - ref_l[fin]))) if fin.any() else 0.0
+    say("  %s: max|dv|=%.3g max|dlse|=%.3g" % (what, dv, dl))
+    assert dv <= TOL_V, "%s: max |dv| %.3g" % (what, dv)
+    assert dl <= TOL_L, "%s: max |dlse| %.3g" % (what, dl)
+
+
+def run_mla(orc, w, *, fixed=0, target=0, heads=None, partial_rows=True):
+    """Decode w on the GPU and compare with the oracle (all heads, or the
+    given sample of query heads)."""
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            w.k_pool.shape[0])
+    dec = PD.MlaDecode(csr, page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                       num_qo_heads=w.num_qo_heads, dim=w.dim, extra_dim=w.extra_dim,
+                       target_wgs=target, fixed_pages_per_chunk=fixed)
+    say("case %s B=%d Hq=%d ps=%d plan=%s" % (w.name, w.batch, w.num_qo_heads, w.page_size,
+                                              dec.plan_summary()))
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    for key in ("indptr", "indices", "last_page_len", "first_page_offset"):
+        assert np.array_equal(np.asarray(csr[key]), ocsr[key]), key
+    ref_plan = orc.plan(ocsr["indptr"], dec.info.q_groups, dec.info.target_wgs,
+                        fixed_pages_per_chunk=fixed)
+    assert dec.info.pages_per_chunk == ref_plan["pages_per_chunk"]
+    assert np.array_equal(dec.request_indices, ref_plan["request_indices"])
+    assert np.array_equal(dec.o_indptr, ref_plan["o_indptr"])
+    q, qx = to_dev(w.q), to_dev(w.q_extra)
+    k, kx = to_dev(w.k_pool), to_dev(w.k_extra_pool)
+    for _ in range(2):                      # a second step reuses the buffers
+        out, lse = dec.run(q, qx, k, kx, w.sm_scale)
+    torch.cuda.synchronize()
+    sel = np.arange(w.num_qo_heads) if heads is None else np.asarray(heads)
+    qs = np.ascontiguousarray(w.q[:, sel])
+    qxs = np.ascontiguousarray(w.q_extra[:, sel])
+    ref_v, ref_l = orc.attention_mla(qs, qxs, w.k_pool, w.k_extra_pool, ocsr, w.page_size,
+                                     w.sm_scale, nthreads=NTHREADS)
+    check(out.cpu().numpy()[:, sel], lse.cpu().numpy()[:, sel], ref_v, ref_l, "output")
+    if partial_rows and dec.info.needs_merge:
+        pv, pl = orc.attention_mla(qs, qxs, w.k_pool, w.k_extra_pool, ocsr, w.page_size,
+                                   w.sm_scale, chunks=(dec.request_indices, dec.kv_tile_indices,
+                                                       dec.info.pages_per_chunk),
+                                   nthreads=NTHREADS)
+        check(dec.v_partial.cpu().numpy()[:, sel], dec.lse_partial.cpu().numpy()[:, sel],
+              pv, pl, "partial rows")
+    return dec
+
+
+@pytest.mark.parametrize("hq", [16, 32, 64, 128])
+@pytest.mark.parametrize("ps", [1, 16, 64])
+def test_mla_ragged_poisoned(orc, hq, ps):
+    """Ragged batch: an empty request, windows starting mid-page, an exactly
+    full last page, a single token; unused pages and indexer columns NaN;
+    chunks of one page (every request split) and the default plan."""
+    lens = [(0, 700), (13, 300), (0, 0), (0, 64 * 5), (37, 38)]
+    w = workloads.mla_paged("mla_ragged", seed=100 + hq + ps,
+                            logical_start=[a for a, _ in lens],
+                            written_len=[b for _, b in lens], num_qo_heads=hq, page_size=ps,
+                            poison_unused=True, poison_indexer=True)
+    run_mla(orc, w, fixed=max(1, 48 // ps))
+    run_mla(orc, w)
+
+
+def test_dsa_selection_poisoned(orc):
+    """DSA decode: top-k positions of a dense latent cache read as
+    page_size-1 rows; every unselected row and the indexer columns NaN."""
+    w = workloads.dsa_sparse_fp16(batch=3, capacity=8192, kv_len=8000, topk=1000,
+                                  poison_unselected=True)
+    run_mla(orc, w)
+    run_mla(orc, w, fixed=64)
+
+
+def test_mla_paged_full_size_sampled_heads(orc):
+    """The benchmark geometry (4 requests x 32768 tokens, 128 heads, pages of
+    64) in the launch configuration the benchmark times; the oracle computes
+    heads from both q groups and every 16-head wave."""
+    w = workloads.mla_paged_fp16()
+    run_mla(orc, w, heads=[0, 21, 47, 63, 64, 90, 111, 127], partial_rows=False)
+
+
+def test_dsa_full_size_sampled_heads(orc):
+    w = workloads.dsa_sparse_fp16()
+    run_mla(orc, w, heads=[0, 17, 50, 63, 64, 99, 127])
+
+
+def test_mla_graph_replay_matches_eager(orc):
+    """The MLA step captured in a HIP graph and replayed equals the eager
+    step, replay after replay, with new queries written in between."""
+    w = workloads.dsa_sparse_fp16(batch=2, capacity=4096, kv_len=4000, topk=512)
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            w.k_pool.shape[0])
+    dec = PD.MlaDecode(csr, page_size=1, num_pool_pages=w.k_pool.shape[0],
+                       num_qo_heads=w.num_qo_heads)
+    assert dec.info.needs_merge
+    k, kx = to_dev(w.k_pool), to_dev(w.k_extra_pool)
+    qs = [(w.q, w.q_extra),
+          (workloads._normal(np.random.default_rng(5), w.q.shape, workloads.FP16),
+           workloads._normal(np.random.default_rng(6), w.q_extra.shape, workloads.FP16))]
+    qb, qxb = to_dev(w.q), to_dev(w.q_extra)
+    eager = []
+    for a, b in qs:
+        qb.copy_(to_dev(a))
+        qxb.copy_(to_dev(b))
+        out, lse = dec.run(qb, qxb, k, kx, w.sm_scale)
+        torch.cuda.synchronize()
+        eager.append((out.cpu().numpy().copy(), lse.cpu().numpy().copy()))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dec.run(qb, qxb, k, kx, w.sm_scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_g, lse_g = dec.run(qb, qxb, k, kx, w.sm_scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        a, b = qs[rep % 2]
+        qb.copy_(to_dev(a))
+        qxb.copy_(to_dev(b))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev, el = eager[rep % 2]
+        np.testing.assert_allclose(out_g.cpu().numpy(), ev, rtol=0, atol=1e-6)
+        np.testing.assert_allclose(lse_g.cpu().numpy(), el, rtol=0, atol=1e-6)

@@ -212,3 +212,46 @@ def test_fastdiv_wide_and_random(lib):
     for d in [1, 2, 3, 7, 16, 17, 64, 100, 128, 255, 256, 1000, 4096, 65537, (1 << 30) + 3]:
         q, r = B.paged_fastdiv_eval(d, n)
         assert np.array_equal(q, n // d) and np.array_equal(r, n % d), d
+
+
+def test_plan_paged_mla_q_groups(orc):
+    """head_dim 512 plans the paged-MLA kernel: (chunk, q group) units of 64
+    query heads; the chunk list itself is the ordinary plan's."""
+    indptr = np.array([0, 512, 1024, 1536, 2048], np.int32)
+    for hq, qg in ((128, 2), (64, 1), (32, 1), (16, 1)):
+        info, ri, ti, oi = B.paged_decode_plan(indptr, hq, 1, 512, 256, 0, page_size=64)
+        ref = orc.plan(indptr, qg, 256)
+        assert info.q_groups == qg and info.num_wgs == info.num_chunks * qg
+        assert info.pages_per_chunk == ref["pages_per_chunk"]
+        assert np.array_equal(ri, ref["request_indices"]) and np.array_equal(oi, ref["o_indptr"])
+        assert info.workspace_bytes == info.num_chunks * hq * 513 * 4
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_decode_plan(indptr, 128, 2, 512, 256, 0)
+    assert ei.value.name == "PD_E_UNSUPPORTED"
+    with pytest.raises(B.PagedDecodeError) as ei:
+        B.paged_decode_plan(indptr, 48, 1, 512, 256, 0)
+    assert ei.value.name == "PD_E_UNSUPPORTED"
+    assert B.paged_decode_q_heads_per_wg(128, 512, B.PD_DTYPE_FP16) == 64
+    assert B.paged_decode_q_heads_per_wg(32, 512, B.PD_DTYPE_FP16) == 32
+
+
+def test_mla_partial_argument_errors_before_launch():
+    """Argument checks of paged_mla_decode_partial return before any launch
+    (no device needed)."""
+    lib = B.load()
+    one = 16  # any non-null, 16-byte aligned address: nothing is dereferenced
+    args = [one] * 4 + [640 * 64, 640, 64 * 64, 64, 512, 64, B.PD_DTYPE_FP16] + [one] * 6 + \
+        [1, 1, 1, 128, 64, 0.04, one, one, None]
+    assert lib.paged_mla_decode_partial(*([None] + args[1:])) == B.CODES["PD_E_NULL"]
+    bad_dim = list(args)
+    bad_dim[8] = 256
+    assert lib.paged_mla_decode_partial(*bad_dim) == B.CODES["PD_E_UNSUPPORTED"]
+    bad_heads = list(args)
+    bad_heads[20] = 48
+    assert lib.paged_mla_decode_partial(*bad_heads) == B.CODES["PD_E_UNSUPPORTED"]
+    bad_stride = list(args)
+    bad_stride[5] = 641                  # a row start off a 16-byte boundary
+    assert lib.paged_mla_decode_partial(*bad_stride) == B.CODES["PD_E_UNSUPPORTED"]
+    fp32 = list(args)
+    fp32[10] = B.PD_DTYPE_FP32
+    assert lib.paged_mla_decode_partial(*fp32) == B.CODES["PD_E_UNSUPPORTED"]
