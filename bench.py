@@ -499,6 +499,24 @@ def mla(args, torch, B, PD, workloads, dev):
     part_s = timed(part)
     g_step = PD.graph_time(step, args.steps)
     g_part = PD.graph_time(part, args.steps)
+    sweep = None
+    if args.sweep_chunks:
+        sweep = []
+        for c in PD.chunk_candidates(csr["indptr"], dec.info.pages_per_chunk):
+            r = PD.MlaDecode(csr, page_size=w.page_size, num_pool_pages=w.k_pool.shape[0],
+                             num_qo_heads=w.num_qo_heads, dim=w.dim, extra_dim=w.extra_dim,
+                             fixed_pages_per_chunk=c, device=dev)
+            o2, l2 = r.run(q, qx, *kv[0], w.sm_scale)
+            torch.cuda.synchronize()
+            if not (float(np.max(np.abs(o2.cpu().numpy()[:, sel] - ref_v))) <= 2e-3 and
+                    float(np.max(np.abs(l2.cpu().numpy()[:, sel] - ref_l))) <= 1e-3):
+                print(json.dumps({"error": "parity failed in the chunk sweep", "c": c}))
+                sys.exit(1)
+            fs = lambda i: r.run(q, qx, *kv[i % len(kv)], w.sm_scale)   # noqa: E731
+            sweep.append({"pages_per_chunk": c, "num_chunks": r.info.num_chunks,
+                          "units": r.info.num_wgs,
+                          "graph_step_us": round(PD.graph_time(fs, args.steps) * 1e6, 2),
+                          "default": c == dec.info.pages_per_chunk})
     kv_bytes = w.kv_bytes()
     tokens = int(w.visible_tokens.sum())
     flops = tokens * w.num_qo_heads * 2 * (w.dim + w.extra_dim + w.dim)
@@ -543,6 +561,8 @@ def mla(args, torch, B, PD, workloads, dev):
                      "mfma_frac": round(tflops / MFMA_FP16_PEAK_TFLOPS, 4),
                      "bytes_per_launch": int(kv_bytes), "flops_per_launch": int(flops)},
     }
+    if sweep is not None:
+        res["chunk_sweep"] = sweep
     if not args.no_cpu_baseline:
         scale = w.num_qo_heads / sel.size
         res["cpu_baseline"] = {"value": round(kv_bytes / (oracle_s * scale) / 1e9, 4),
