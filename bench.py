@@ -280,6 +280,12 @@ def main():
         settle(fstep)
         run_steps(args.warmup, fstep)
         flat_s, _ = run_steps(args.steps, fstep)
+        # both arms replayed from HIP graphs (no host launch cost); the
+        # cascade's last replay must still agree with the oracle
+        g_casc = graph_steps(args.steps, step)
+        gv = runner.out.cpu().numpy().astype(np.float64)
+        g_casc_ok = bool(np.max(np.abs(gv - ref_v)) <= tv)
+        g_flat = graph_steps(args.steps, fstep)
 
     # reference: one isolated step after a cache flush, bracketed by its own
     # events (includes the fixed cost of an event pair around a launch)
@@ -341,6 +347,9 @@ def main():
             "speedup": round(flat_s / step_s, 3), "cascade_kv_bytes": int(kv_bytes),
             "flat_kv_bytes": int(flat_bytes),
             "flat_kv_gbs": round(flat_bytes / flat_s / 1e9, 2),
+            "graph_cascade_step_us": round(g_casc * 1e6, 2),
+            "graph_flat_step_us": round(g_flat * 1e6, 2),
+            "graph_speedup": round(g_flat / g_casc, 3), "graph_parity_ok": g_casc_ok,
             "flat_plan": flat_runner.plan_summary()}
     if sweep is not None:
         res["chunk_sweep"] = sweep

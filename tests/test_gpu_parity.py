@@ -507,6 +507,25 @@ def test_ragged_force_merge(orc, seed, ps, mode):
     run_flat(orc, w, fixed=1, fused=mode["fused"], repeat=2)
 
 
+@pytest.mark.parametrize("fixed", [0, 1])
+def test_many_requests(orc, fixed):
+    """3000 requests in one batch (mostly one or two pages, some empty, some
+    trimmed, a few long): the plan arrays, chunk lists and merge groups at
+    scale; pinned one-page chunks give 10k+ chunks."""
+    rng = np.random.default_rng(77)
+    b = 3000
+    wl = rng.integers(0, 40, size=b)                      # 0 to 3 pages of 16
+    wl[rng.choice(b, size=12, replace=False)] = rng.integers(500, 3000, size=12)
+    ls = np.where(rng.random(b) < 0.3, (wl * rng.random(b)).astype(np.int64), 0)
+    w = workloads.generic("many_requests", seed=78, dtype=workloads.FP16, page_size=16,
+                          num_qo_heads=8, num_kv_heads=2, head_dim=128, logical_start=ls,
+                          written_len=wl, poison_unused=True)
+    dec = run_flat(orc, w, fixed=fixed, check_partials=False)
+    assert dec.batch == b
+    if fixed:
+        assert dec.info.num_chunks > 3000
+
+
 @pytest.mark.parametrize("g", [4, 8, 16])
 @pytest.mark.parametrize("ps", [4, 16, 64])
 def test_page_kernel_shapes_ragged(orc, g, ps, mode):
