@@ -52,15 +52,18 @@ constexpr int kTile = 32;                     // tokens per LDS stage
 constexpr int kRowBytes = kKey * 2;           // LDS row: 1152 bytes, 9 blocks of 128
 
 // LDS swizzle.  Piece c (16 bytes) of row j is stored at piece c ^ swz(j),
-// i.e. permuted within its 128-byte block; rows are 1152 bytes, so odd rows
-// start half way into a 256-byte bank line (64 banks of 4 bytes).  With
-// swz(j) = 2*((j/2)%4) + (j/8)%2 both read patterns hit distinct banks: the
-// 16 rows a 16-byte read serves per pass (key and query fragments, one piece
-// each) land on 16 distinct 16-byte slots of a bank line, and the 8 rows of
-// two 16-lane groups of a transpose read (values, a 32-byte pair each) on 8
-// distinct 32-byte slots.  (Counters showed the padded-row layout losing
-// about 40% of LDS time to bank conflicts.)
-__device__ __forceinline__ int swz(int j) { return 2 * ((j >> 1) & 3) + ((j >> 3) & 1); }
+// i.e. permuted within its 128-byte block, with
+//   swz(j) = 2*s(j) + (j/2)%2,  s(j) = ((j/4)%4) ^ (3*((j/2)%2)).
+// Rows are 1152 bytes.  The 32-byte slot s(j) differs between the four rows
+// of every j%4 class and, for a fixed (j/4)%4, between rows j and j+2; the
+// low bit separates the rows that share a slot.  Measured on MI355X with a
+// read-only LDS microbenchmark (8 waves per CU): the key/query fragment reads
+// (16 rows, one 16-byte piece each, per 16-lane group) run at the rate of
+// lane-contiguous 16-byte reads, 5.5 clocks per instruction per CU, where the
+// previous swizzle 2*((j/2)%4) + (j/8)%2 took 8.4; the value transpose reads
+// run at the lane-contiguous rate under both.
+__device__ __forceinline__ int swz_slot(int j) { return ((j >> 2) & 3) ^ (3 * ((j >> 1) & 1)); }
+__device__ __forceinline__ int swz(int j) { return 2 * swz_slot(j) + ((j >> 1) & 1); }
 constexpr int kXcds = 8;
 constexpr int kWaves = 4;
 constexpr int kGroupHeads = 16 * kWaves;      // query heads per workgroup
@@ -239,18 +242,18 @@ mla_partial_kernel(MlaArgs a)
     // transpose-read address of a 4-token x 16-dim block: row 4*(l/16) +
     // (l%16)/4 of the subtile, halves 4*(l%4) of the dim block
     //
-    // With the swizzle, lane l's read of row 4*g + r (g = l/16, r = (l%16)/4)
-    // at halves 16*dt + 4*(l%4), i.e. piece 2*dt + (l%4)/2, is at piece
-    // 2*(dt ^ t) + ((l%4)/2 ^ g/2) with t = 2*(g%2) + r/2 (the xor touching
-    // the low two bits of dt only): one base per value of dt % 4, plus
-    // 32 * (dt - dt % 4) bytes.
+    // With the swizzle, lane l's read of row j = 4*g + r (g = l/16, r =
+    // (l%16)/4) at halves 16*dt + 4*(l%4), i.e. piece 2*dt + (l%4)/2, is at
+    // piece 2*((dt%4) ^ s(j)) + ((l%4)/2 ^ (r/2)) + 8*(dt/4), with s(j) =
+    // g ^ (3*(r/2)): one base per value of dt % 4, plus 32 * (dt - dt % 4)
+    // bytes.
     const int tr_r = col >> 2;
-    const int tr_t = 2 * (grp & 1) + (tr_r >> 1);
+    const int tr_s = grp ^ (3 * (tr_r >> 1));
     int tr_base[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-        tr_base[d] = (4 * grp + tr_r) * kRowBytes + 32 * (d ^ tr_t) +
-                     16 * (((lane & 3) >> 1) ^ (grp >> 1)) + 8 * (lane & 1);
+        tr_base[d] = (4 * grp + tr_r) * kRowBytes + 32 * (d ^ tr_s) +
+                     16 * (((lane & 3) >> 1) ^ (tr_r >> 1)) + 8 * (lane & 1);
 
     // One tile: S^T for both 16-token subtiles, one softmax update over its
     // 32 tokens, then O^T += V^T . P^T as 32 products with K = 32 tokens.  The
@@ -377,8 +380,10 @@ mla_partial_kernel(MlaArgs a)
         id_cur = load_id(i + 4);
         load_tile(i + 2, cur);
         if (active) compute(i, i & 1);
-        if (i + 3 < ntiles) offsets(i + 3, id_nxt);
-        if (i + 1 < ntiles) store_tile(nxt, (i + 1) & 1);
+        // unconditional: past the chunk the offsets are -1 and the registers
+        // hold zeros, written to a slot and a stage no later tile reads
+        offsets(i + 3, id_nxt);
+        store_tile(nxt, (i + 1) & 1);
         __syncthreads();
     };
     if (ntiles > 0) {
@@ -391,10 +396,16 @@ mla_partial_kernel(MlaArgs a)
         load_tile(1, pre[1]);
         store_tile(pre[0], 0);
         __syncthreads();
-        for (int i = 0; i < ntiles; i += 2) {
+        // the odd tail is peeled so that the loop's back edge always follows
+        // the store of register set 0: on a path that skipped it, those loads
+        // would count as pending at the top of the loop and the compiler would
+        // wait there for every load in flight
+        int i = 0;
+        for (; i + 1 < ntiles; i += 2) {
             iteration(i, pre[0], pre[1], ids[0], ids[1]);
-            if (i + 1 < ntiles) iteration(i + 1, pre[1], pre[0], ids[1], ids[0]);
+            iteration(i + 1, pre[1], pre[0], ids[1], ids[0]);
         }
+        if (i < ntiles) iteration(i, pre[0], pre[1], ids[0], ids[1]);
     }
 
     if (!active) return;
