@@ -199,8 +199,8 @@ mla_partial_kernel(MlaArgs a)
     // Pieces a thread moves per tile: latent piece lc = tid % 64 of rows
     // tid / 64 + 4*k (k < 8), and extra piece tid % 8 of row tid / 8.  The
     // column is fixed per thread, so a piece's address is its row's offset
-    // (from LDS) plus a constant.  Two register sets: a tile's loads are
-    // issued one iteration before its pieces are stored to LDS.
+    // (from LDS) plus a constant.  A tile's loads are issued one iteration
+    // before its pieces are stored to LDS.
     constexpr int kLatPerThread = kTile * (kDim / 8) / NT;     // 8
     static_assert(kTile * (kDim / 8) == kLatPerThread * NT && kTile * (kExtra / 8) == NT,
                   "tile / thread layout");
@@ -208,7 +208,6 @@ mla_partial_kernel(MlaArgs a)
     const int lat_r = tid >> 6;
     const int ext_c = tid & 7;
     const int ext_r = tid >> 3;
-    uint4 pre[2][PPT];
     const char *zero = reinterpret_cast<const char *>(&g_zero16);
     auto load_tile = [&](int i, uint4 (&dst)[PPT]) {
         const int buf = i % kOffRing;
@@ -364,48 +363,36 @@ mla_partial_kernel(MlaArgs a)
         __builtin_amdgcn_sched_group_barrier(kMfma, kValueAhead, 1);
     };
 
-    // Pipeline.  Before iteration i: LDS stage i%2 holds tile i, register
-    // set (i+1)%2 holds tile i+1 (loads in flight), the offsets of tile i+2
-    // are in their slot and id register (i+1)%2 holds tile i+3's ids.
-    // Iteration i loads tile i+4's ids into id register i%2 and tile i+2
-    // into set i%2 (whose tile i is in LDS already), computes tile i, writes
-    // tile i+3's offsets, stores set (i+1)%2 into stage (i+1)%2, and ends with
-    // the one barrier: every LDS region an iteration writes was last read
-    // before the previous iteration's barrier.  Loads are waited for one
-    // iteration after they are issued.  The loop is unrolled by two so that
-    // the register sets are named statically.
-    int32_t ids[2];
-    auto iteration = [&](int i, uint4 (&cur)[PPT], const uint4 (&nxt)[PPT], int32_t &id_cur,
-                         int32_t id_nxt) {
-        id_cur = load_id(i + 4);
-        load_tile(i + 2, cur);
-        if (active) compute(i, i & 1);
-        // unconditional: past the chunk the offsets are -1 and the registers
-        // hold zeros, written to a slot and a stage no later tile reads
-        offsets(i + 3, id_nxt);
-        store_tile(nxt, (i + 1) & 1);
-        __syncthreads();
-    };
+    // Pipeline, one register set.  Before iteration i: LDS stage i%2 holds
+    // tile i, the registers hold tile i+1 (loads in flight since the previous
+    // iteration) and the offsets of tile i+2 are in their slot.  Iteration i
+    // stores the registers into stage (i+1)%2 (last read by tile i-1, before
+    // the previous barrier), issues tile i+2's loads into the same registers
+    // and tile i+3's ids, computes tile i, writes tile i+3's offsets and ends
+    // with the one barrier.  Loads are waited for one iteration after they
+    // are issued.  The loop is not unrolled: one copy of the rare rescale
+    // path keeps the compiler from moving accumulator copies into the body.
+    // Past the chunk the offsets are -1 and the registers hold zeros, written
+    // to a slot and a stage no later tile reads.
+    uint4 regs[PPT];
     if (ntiles > 0) {
         offsets(0, load_id(0));
         offsets(1, load_id(1));
         offsets(2, load_id(2));
-        ids[1] = load_id(3);
         __syncthreads();
-        load_tile(0, pre[0]);
-        load_tile(1, pre[1]);
-        store_tile(pre[0], 0);
+        load_tile(0, regs);
+        store_tile(regs, 0);
+        load_tile(1, regs);
         __syncthreads();
-        // the odd tail is peeled so that the loop's back edge always follows
-        // the store of register set 0: on a path that skipped it, those loads
-        // would count as pending at the top of the loop and the compiler would
-        // wait there for every load in flight
-        int i = 0;
-        for (; i + 1 < ntiles; i += 2) {
-            iteration(i, pre[0], pre[1], ids[0], ids[1]);
-            iteration(i + 1, pre[1], pre[0], ids[1], ids[0]);
+#pragma clang loop unroll(disable)
+        for (int i = 0; i < ntiles; ++i) {
+            store_tile(regs, (i + 1) & 1);
+            const int32_t id = load_id(i + 3);
+            load_tile(i + 2, regs);
+            if (active) compute(i, i & 1);
+            offsets(i + 3, id);
+            __syncthreads();
         }
-        if (i < ntiles) iteration(i, pre[0], pre[1], ids[0], ids[1]);
     }
 
     if (!active) return;
