@@ -254,6 +254,11 @@ mla_partial_kernel(MlaArgs a)
         tr_base[d] = (4 * grp + tr_r) * kRowBytes + 32 * (d ^ tr_s) +
                      16 * (((lane & 3) >> 1) ^ (tr_r >> 1)) + 8 * (lane & 1);
 
+    constexpr int KS = kPieces / 4;                        // 18 key steps
+    // Q^T operand of the score product: lane l holds head l%16 of the wave,
+    // key dims 32*kc + 8*(l/16) .. + 7, for every key step kc
+    half8_t qf[KS];
+
     // One tile: S^T for both 16-token subtiles, one softmax update over its
     // 32 tokens, then O^T += V^T . P^T as 32 products with K = 32 tokens.  The
     // k order of the value product is the score layout's: lane l holds
@@ -270,40 +275,34 @@ mla_partial_kernel(MlaArgs a)
         const int lo = 16 * (grp ^ (sw & 3));
         const char *kr_even = tile + col * kRowBytes + lo + 64 * sb;
         const char *kr_odd = tile + col * kRowBytes + lo - 64 * sb;
-        const char *qr_even = s_q + (wave * 16 + col) * kRowBytes + lo + 64 * sb;
-        const char *qr_odd = s_q + (wave * 16 + col) * kRowBytes + lo - 64 * sb;
         float4_t sc0 = float4_t{0.f, 0.f, 0.f, 0.f};
         float4_t sc1 = float4_t{0.f, 0.f, 0.f, 0.f};
         // Fragment reads run ahead of the products (two key steps, four value
         // steps), so each product waits for a read issued well before it: one
         // wave per SIMD has no other wave to cover LDS latency.
-        auto kfrag = [&](int kc, half8_t &q, half8_t &k0, half8_t &k1) {
+        auto kfrag = [&](int kc, half8_t &k0, half8_t &k1) {
             const char *kr = (kc & 1) ? kr_odd : kr_even;
-            const char *qr = (kc & 1) ? qr_odd : qr_even;
-            q = *reinterpret_cast<const half8_t *>(qr + 64 * kc);
             k0 = *reinterpret_cast<const half8_t *>(kr + 64 * kc);
             k1 = *reinterpret_cast<const half8_t *>(kr + 16 * kRowBytes + 64 * kc);
         };
-        constexpr int KS = kPieces / 4;                    // 18 key steps
         constexpr int KD = kKeyAhead + 1;                  // key fragment ring
-        half8_t fq[KD], fk0[KD], fk1[KD];
+        half8_t fk0[KD], fk1[KD];
 #pragma unroll
-        for (int kc = 0; kc < KD - 1; ++kc) kfrag(kc, fq[kc], fk0[kc], fk1[kc]);
+        for (int kc = 0; kc < KD - 1; ++kc) kfrag(kc, fk0[kc], fk1[kc]);
 #pragma unroll
         for (int kc = 0; kc < KS; ++kc) {
             if (kc + KD - 1 < KS)
-                kfrag(kc + KD - 1, fq[(kc + KD - 1) % KD], fk0[(kc + KD - 1) % KD],
-                      fk1[(kc + KD - 1) % KD]);
-            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fk0[kc % KD], fq[kc % KD], sc0, 0, 0, 0);
-            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fk1[kc % KD], fq[kc % KD], sc1, 0, 0, 0);
+                kfrag(kc + KD - 1, fk0[(kc + KD - 1) % KD], fk1[(kc + KD - 1) % KD]);
+            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fk0[kc % KD], qf[kc], sc0, 0, 0, 0);
+            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(fk1[kc % KD], qf[kc], sc1, 0, 0, 0);
         }
         // the issue order the scheduler must keep: kKeyAhead steps of reads,
         // then two products and one step of reads per step
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 3 * kKeyAhead, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kKeyAhead, 0);
 #pragma unroll
         for (int kc = 0; kc < KS - kKeyAhead; ++kc) {
             __builtin_amdgcn_sched_group_barrier(kMfma, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kDsRead, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kMfma, 2 * kKeyAhead, 0);
         float x[8];
@@ -384,6 +383,13 @@ mla_partial_kernel(MlaArgs a)
         store_tile(regs, 0);
         load_tile(1, regs);
         __syncthreads();
+        // the wave's query fragments, read from LDS once
+#pragma unroll
+        for (int kc = 0; kc < KS; ++kc) {
+            const int sw = swz(col);
+            const char *qr = s_q + (wave * 16 + col) * kRowBytes;
+            qf[kc] = *reinterpret_cast<const half8_t *>(qr + 16 * ((4 * kc + grp) ^ sw));
+        }
 #pragma clang loop unroll(disable)
         for (int i = 0; i < ntiles; ++i) {
             store_tile(regs, (i + 1) & 1);
