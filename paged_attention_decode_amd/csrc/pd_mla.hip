@@ -109,7 +109,6 @@ mla_partial_kernel(MlaArgs a)
     constexpr int PPT = (PIECES + NT - 1) / NT;   // pieces each thread moves per tile
 
     __shared__ __align__(16) char s_tile[2][kTile * kRowBytes];
-    __shared__ __align__(16) char s_q[kGroupHeads * kRowBytes];
     __shared__ int64_t s_koff[kOffRing][kTile];   // byte offset of a token's rows; -1 = masked
     __shared__ int64_t s_xoff[kOffRing][kTile];
 
@@ -146,24 +145,21 @@ mla_partial_kernel(MlaArgs a)
     const bool active = head0 < a.num_qo_heads;         // wave-uniform (groups of 16)
     const int head = head0 + col;
 
-    // The workgroup's 64 query rows (latent then extra dims, 576 halves per
-    // head) are staged once in LDS, rows padded like the tiles; the score
-    // product reads its Q^T operand from there (lane l: head l%16 of the
-    // wave, key dims 32*kc + 8*(l/16) .. + 7).  Held in registers they would
-    // leave too few for the loads in flight.
+    // Q^T operand of the score product, loaded once into registers: lane l
+    // holds head l%16 of the wave (clamped to the last head in a short
+    // group), key dims 32*kc + 8*(l/16) .. + 7 for every key step kc -- the
+    // latent dims from q, the last two steps from q_extra.  Issued before
+    // the page ids so that both latencies overlap.
+    constexpr int KS = kPieces / 4;                        // 18 key steps
+    half8_t qf[KS];
     {
-        constexpr int QPIECES = kGroupHeads * kPieces;
+        const int64_t qrow = int64_t(r) * a.num_qo_heads + min(head, a.num_qo_heads - 1);
 #pragma unroll
-        for (int k = 0; k < QPIECES / NT; ++k) {
-            const int p = tid + k * NT;
-            const int hl = p / kPieces;               // head of the group
-            const int c = p - hl * kPieces;
-            const int h = min(qg * kGroupHeads + hl, a.num_qo_heads - 1);
-            const int64_t qrow = int64_t(r) * a.num_qo_heads + h;
-            const uint4 v = c < kDim / 8
-                ? *reinterpret_cast<const uint4 *>(a.q + qrow * kDim + 8 * c)
-                : *reinterpret_cast<const uint4 *>(a.qx + qrow * kExtra + 8 * (c - kDim / 8));
-            *reinterpret_cast<uint4 *>(s_q + hl * kRowBytes + 16 * (c ^ swz(hl))) = v;
+        for (int kc = 0; kc < KS; ++kc) {
+            const int d = 32 * kc + 8 * grp;
+            qf[kc] = kc < kDim / 32
+                ? *reinterpret_cast<const half8_t *>(a.q + qrow * kDim + d)
+                : *reinterpret_cast<const half8_t *>(a.qx + qrow * kExtra + (d - kDim));
         }
     }
 
@@ -253,11 +249,6 @@ mla_partial_kernel(MlaArgs a)
     for (int d = 0; d < 4; ++d)
         tr_base[d] = (4 * grp + tr_r) * kRowBytes + 32 * (d ^ tr_s) +
                      16 * (((lane & 3) >> 1) ^ (tr_r >> 1)) + 8 * (lane & 1);
-
-    constexpr int KS = kPieces / 4;                        // 18 key steps
-    // Q^T operand of the score product: lane l holds head l%16 of the wave,
-    // key dims 32*kc + 8*(l/16) .. + 7, for every key step kc
-    half8_t qf[KS];
 
     // One tile: S^T for both 16-token subtiles, one softmax update over its
     // 32 tokens, then O^T += V^T . P^T as 32 products with K = 32 tokens.  The
@@ -383,13 +374,6 @@ mla_partial_kernel(MlaArgs a)
         store_tile(regs, 0);
         load_tile(1, regs);
         __syncthreads();
-        // the wave's query fragments, read from LDS once
-#pragma unroll
-        for (int kc = 0; kc < KS; ++kc) {
-            const int sw = swz(col);
-            const char *qr = s_q + (wave * 16 + col) * kRowBytes;
-            qf[kc] = *reinterpret_cast<const half8_t *>(qr + 16 * ((4 * kc + grp) ^ sw));
-        }
 #pragma clang loop unroll(disable)
         for (int i = 0; i < ntiles; ++i) {
             store_tile(regs, (i + 1) & 1);
