@@ -87,6 +87,26 @@ constexpr float kMlaLazyMargin = 8.0f;        // log2 units: p <= 2^8 between re
 // unconditional and masked rows reach LDS as zeros
 __device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
 
+// One direct-to-LDS load: lane l's 16 bytes at src go to LDS byte address
+// lds + 16*l (lds wave-uniform).  Written as inline assembly so that the
+// compiler does not treat every later LDS read as waiting for it (it cannot
+// tell the stage being filled from the one being read and would wait for
+// all loads in flight before the first read).  The compiler does not count
+// these loads in its own waits; that only makes its waits for other loads
+// longer (the counter is in order), never shorter.  The caller waits for
+// them (wait_loads) before the barrier that publishes the stage.
+__device__ __forceinline__ void dma16(const char *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+// s_waitcnt vmcnt(0), leaving the other counters alone
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0xF70); }
+
 struct MlaArgs {
     const _Float16 *q;      // [B, Hq, 512]
     const _Float16 *qx;     // [B, Hq, 64]
@@ -192,39 +212,42 @@ mla_partial_kernel(MlaArgs a)
             s_xoff[buf][tid] = xo;
         }
     };
-    // Pieces a thread moves per tile: latent piece lc = tid % 64 of rows
-    // tid / 64 + 4*k (k < 8), and extra piece tid % 8 of row tid / 8.  The
-    // column is fixed per thread, so a piece's address is its row's offset
-    // (from LDS) plus a constant.  A tile's loads are issued one iteration
-    // before its pieces are stored to LDS.
-    constexpr int kLatPerThread = kTile * (kDim / 8) / NT;     // 8
-    static_assert(kTile * (kDim / 8) == kLatPerThread * NT && kTile * (kExtra / 8) == NT,
-                  "tile / thread layout");
-    const int lat_c = tid & 63;
-    const int lat_r = tid >> 6;
+    // Moving a tile.  The latent rows go from memory straight into LDS with
+    // direct-to-LDS loads (global_load_lds_dwordx4): one instruction moves a
+    // whole 1024-byte row, lane l's 16 bytes landing at byte 16*l of the row
+    // in LDS, so lane l loads the piece that the swizzle puts there, piece
+    // l ^ swz(j).  Wave w moves rows w + 4*k (k < 8).  The rope keys (128
+    // bytes per row, not contiguous between rows in LDS) go through a
+    // register: thread t moves piece t % 8 of row t / 8, loaded one
+    // iteration before it is written.  Each wave waits for its direct-to-LDS
+    // loads before the barrier that follows them; a stage is read only after
+    // that barrier.
+    constexpr int kLatRowsPerWave = kTile / kWaves;               // 8
+    static_assert(kTile * (kExtra / 8) == NT, "tile / thread layout");
     const int ext_c = tid & 7;
     const int ext_r = tid >> 3;
     const char *zero = reinterpret_cast<const char *>(&g_zero16);
-    auto load_tile = [&](int i, uint4 (&dst)[PPT]) {
+    typedef __attribute__((address_space(3))) char lds_char;
+    auto dma_latent = [&](int i) {
         const int buf = i % kOffRing;
         const bool live = i < ntiles;
+        char *t = s_tile[i & 1];
 #pragma unroll
-        for (int k = 0; k < kLatPerThread; ++k) {
-            const int64_t off = s_koff[buf][lat_r + 4 * k];
-            dst[k] = load_nt(live && off >= 0 ? a.k + off + 16 * lat_c : zero);
+        for (int k = 0; k < kLatRowsPerWave; ++k) {
+            const int j = wave + kWaves * k;
+            const int64_t off = s_koff[buf][j];
+            const char *src = live && off >= 0 ? a.k + off + 16 * (lane ^ swz(j)) : zero;
+            const uint32_t dst = uint32_t(uintptr_t((lds_char *)(t + j * kRowBytes)));
+            dma16(src, __builtin_amdgcn_readfirstlane(dst));
         }
-        const int64_t xo = s_xoff[buf][ext_r];
-        dst[kLatPerThread] = load_nt(live && xo >= 0 ? a.x + xo + 16 * ext_c : zero);
     };
-    auto store_tile = [&](const uint4 (&src)[PPT], int buf) {
-        char *t = s_tile[buf];
-#pragma unroll
-        for (int k = 0; k < kLatPerThread; ++k) {
-            const int j = lat_r + 4 * k;
-            *reinterpret_cast<uint4 *>(t + j * kRowBytes + 16 * (lat_c ^ swz(j))) = src[k];
-        }
-        *reinterpret_cast<uint4 *>(t + ext_r * kRowBytes + 16 * ((kDim / 8 + ext_c) ^ swz(ext_r))) =
-            src[kLatPerThread];
+    auto load_rope = [&](int i) -> uint4 {
+        const int64_t xo = s_xoff[i % kOffRing][ext_r];
+        return load_nt(i < ntiles && xo >= 0 ? a.x + xo + 16 * ext_c : zero);
+    };
+    auto store_rope = [&](const uint4 &v, int buf) {
+        *reinterpret_cast<uint4 *>(s_tile[buf] + ext_r * kRowBytes +
+                                   16 * ((kDim / 8 + ext_c) ^ swz(ext_r))) = v;
     };
 
     float m_run = kMlaNoMax;          // running max of this lane's head
@@ -353,34 +376,37 @@ mla_partial_kernel(MlaArgs a)
         __builtin_amdgcn_sched_group_barrier(kMfma, kValueAhead, 1);
     };
 
-    // Pipeline, one register set.  Before iteration i: LDS stage i%2 holds
-    // tile i, the registers hold tile i+1 (loads in flight since the previous
-    // iteration) and the offsets of tile i+2 are in their slot.  Iteration i
-    // stores the registers into stage (i+1)%2 (last read by tile i-1, before
-    // the previous barrier), issues tile i+2's loads into the same registers
-    // and tile i+3's ids, computes tile i, writes tile i+3's offsets and ends
-    // with the one barrier.  Loads are waited for one iteration after they
-    // are issued.  The loop is not unrolled: one copy of the rare rescale
-    // path keeps the compiler from moving accumulator copies into the body.
-    // Past the chunk the offsets are -1 and the registers hold zeros, written
-    // to a slot and a stage no later tile reads.
-    uint4 regs[PPT];
+    // Pipeline.  Before iteration i: LDS stage i%2 holds tile i, the rope
+    // register holds tile i+1's rope piece (loaded in the previous
+    // iteration) and the offsets of tiles i+1 and i+2 are in their slots.
+    // Iteration i writes tile i+1's rope piece into stage (i+1)%2 (last read
+    // by tile i-1, before the previous barrier), starts its latent rows into
+    // the same stage, loads tile i+2's rope piece and tile i+3's ids,
+    // computes tile i,
+    // writes tile i+3's offsets and ends with the one barrier, before which
+    // the kernel waits for tile i+1's loads.  The loop is not unrolled: one
+    // copy of the rare rescale path keeps the compiler from moving
+    // accumulator copies into the body.  Past the chunk the offsets are -1
+    // and the loads read zeros, written to a stage no later tile reads.
     if (ntiles > 0) {
         offsets(0, load_id(0));
         offsets(1, load_id(1));
         offsets(2, load_id(2));
         __syncthreads();
-        load_tile(0, regs);
-        store_tile(regs, 0);
-        load_tile(1, regs);
+        dma_latent(0);
+        store_rope(load_rope(0), 0);
+        uint4 rope = load_rope(1);
+        wait_loads();
         __syncthreads();
 #pragma clang loop unroll(disable)
         for (int i = 0; i < ntiles; ++i) {
-            store_tile(regs, (i + 1) & 1);
+            store_rope(rope, (i + 1) & 1);     // before the loads into the same stage,
+            dma_latent(i + 1);                 // which the compiler would otherwise wait for
+            rope = load_rope(i + 2);
             const int32_t id = load_id(i + 3);
-            load_tile(i + 2, regs);
             if (active) compute(i, i & 1);
             offsets(i + 3, id);
+            wait_loads();                      // tile i+1's rows, before the barrier publishes them
             __syncthreads();
         }
     }
