@@ -231,14 +231,18 @@ mla_partial_kernel(MlaArgs a)
     auto dma_latent = [&](int i) {
         const int buf = i % kOffRing;
         const bool live = i < ntiles;
-        char *t = s_tile[i & 1];
+        // all row offsets first: each load is a volatile statement that the
+        // compiler keeps in order with every memory access
+        int64_t off[kLatRowsPerWave];
+#pragma unroll
+        for (int k = 0; k < kLatRowsPerWave; ++k) off[k] = s_koff[buf][wave + kWaves * k];
+        const uint32_t t = __builtin_amdgcn_readfirstlane(
+            uint32_t(uintptr_t((lds_char *)s_tile[i & 1])));
 #pragma unroll
         for (int k = 0; k < kLatRowsPerWave; ++k) {
             const int j = wave + kWaves * k;
-            const int64_t off = s_koff[buf][j];
-            const char *src = live && off >= 0 ? a.k + off + 16 * (lane ^ swz(j)) : zero;
-            const uint32_t dst = uint32_t(uintptr_t((lds_char *)(t + j * kRowBytes)));
-            dma16(src, __builtin_amdgcn_readfirstlane(dst));
+            const char *src = live && off[k] >= 0 ? a.k + off[k] + 16 * (lane ^ swz(j)) : zero;
+            dma16(src, t + uint32_t(j * kRowBytes));
         }
     };
     auto load_rope = [&](int i) -> uint4 {
