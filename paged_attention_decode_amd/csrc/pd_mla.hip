@@ -16,12 +16,13 @@
 // A workgroup is one (chunk, q group) unit of 64 query heads, one wave per 16
 // heads (a group of 16 or 32 heads leaves waves idle in the products; those
 // waves still move their share of every tile).  Tiles of 32 tokens x 576
-// halves are staged in LDS (two stages) and shared by the waves: each key and
-// value element is fetched from memory once per unit.  Per 32-token tile a
+// halves are staged in LDS (two stages, the latent rows by direct-to-LDS
+// loads) and shared by the waves: each key and value element is fetched from
+// memory once per unit.  Per 32-token tile a
 // wave computes, for each 16-token half,
 //   S^T [16 tokens x 16 heads] = K [16 x 576] . Q^T [576 x 16]
-// with 18 v_mfma_f32_16x16x32_f16 (Q^T read from an LDS copy), then one softmax
-// update over the 32 tokens and
+// with 18 v_mfma_f32_16x16x32_f16 (Q^T held in registers, loaded once), then
+// one softmax update over the 32 tokens and
 //   O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] . P^T [32 x 16 heads]
 // with 32 v_mfma_f32_16x16x32_f16, V^T read from the LDS tile with the
 // transpose read ds_read_b64_tr_b16.  The lane layouts are those of the
