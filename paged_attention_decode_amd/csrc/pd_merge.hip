@@ -156,6 +156,19 @@ constexpr int kSplitUnroll = 4;
 #endif
 constexpr int kWideDL = PD_MERGE_WIDE_DL;     // dim lanes per slice for 512-wide rows
 constexpr int kWideUnroll = PD_MERGE_WIDE_UNROLL;
+// Other widths divisible by 32: 32-dim slices.  At 4 rows x 79 partials, 32
+// heads of 128 dims, 32-, 64- and 128-dim slices with 4 or 8 rows in flight
+// per lane all took 3.5-4.1 us of GPU time (HIP-graph replay); a merge of
+// 4 x 8 partials took 3.1 us: the kernel is bound by its fixed latency chain
+// (row bounds, one round of loads, the combine), not by its slice shape.
+#ifndef PD_MERGE_NARROW_DL
+#define PD_MERGE_NARROW_DL 8
+#endif
+#ifndef PD_MERGE_NARROW_UNROLL
+#define PD_MERGE_NARROW_UNROLL 4
+#endif
+constexpr int kNarrowDL = PD_MERGE_NARROW_DL;     // dim lanes per slice, other widths
+constexpr int kNarrowUnroll = PD_MERGE_NARROW_UNROLL;
 
 // State of a partial merge: running max m (NaN once a NaN lse was seen),
 // weight sum w relative to m, weighted sum a relative to m.
@@ -404,12 +417,13 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
         hipLaunchKernelGGL((merge_slice_kernel<kWideDL, kWideUnroll>), dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
                            lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
-    } else if (vec4 && head_dim % 32 == 0) {
-        // one workgroup per (output row, head, 32-dim slice)
-        const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / 32);
+    } else if (vec4 && head_dim % (4 * kNarrowDL) == 0) {
+        // one workgroup per (output row, head, 4*kNarrowDL-dim slice)
+        const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / (4 * kNarrowDL));
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
-        hipLaunchKernelGGL(merge_slice_kernel<8>, dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
-                           lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
+        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kNarrowUnroll>), dim3(uint32_t(nblk)),
+                           dim3(256), 0, s, v_in, lse_in, o_indptr, num_heads, head_dim, v_out,
+                           lse_out);
     } else if (head_dim / w <= 256) {
         // one workgroup per (output row, head), rows split across lanes
         const int64_t nblk = int64_t(num_out_rows) * num_heads;
