@@ -96,7 +96,7 @@ def run_mla(orc, w, *, fixed=0, target=0, heads=None, partial_rows=True):
 
 
 @pytest.mark.parametrize("hq", [16, 32, 64, 128])
-@pytest.mark.parametrize("ps", [1, 16, 64])
+@pytest.mark.parametrize("ps", [1, 16, 64, 128])
 def test_mla_ragged_poisoned(orc, hq, ps):
     """Ragged batch: an empty request, windows starting mid-page, an exactly
     full last page, a single token; unused pages and indexer columns NaN;
