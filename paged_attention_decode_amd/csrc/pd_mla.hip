@@ -58,7 +58,7 @@ constexpr int kRowBytes = kKey * 2;           // LDS row: 1152 bytes, 9 blocks o
 // Rows are 1152 bytes.  The 32-byte slot s(j) differs between the four rows
 // of every j%4 class and, for a fixed (j/4)%4, between rows j and j+2; the
 // low bit separates the rows that share a slot.  Measured on MI355X with a
-// read-only LDS microbenchmark (8 waves per CU): the key/query fragment reads
+// read-only LDS microbenchmark (8 waves per CU): the key fragment reads
 // (16 rows, one 16-byte piece each, per 16-lane group) run at the rate of
 // lane-contiguous 16-byte reads, 5.5 clocks per instruction per CU, where the
 // previous swizzle 2*((j/2)%4) + (j/8)%2 took 8.4; the value transpose reads
@@ -126,8 +126,6 @@ __global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_e
 mla_partial_kernel(MlaArgs a)
 {
     constexpr int NT = 64 * kWaves;
-    constexpr int PIECES = kTile * kPieces;
-    constexpr int PPT = (PIECES + NT - 1) / NT;   // pieces each thread moves per tile
 
     __shared__ __align__(16) char s_tile[2][kTile * kRowBytes];
     __shared__ int64_t s_koff[kOffRing][kTile];   // byte offset of a token's rows; -1 = masked
@@ -186,7 +184,8 @@ mla_partial_kernel(MlaArgs a)
 
     // Row ids and byte offsets.  Every load of the pipeline is issued
     // unconditionally (a masked piece reads the zero block), so the compiler's
-    // wait counts before each use cover exactly the loads that use waits for.
+    // wait counts before each use of a register it loads cover exactly the
+    // loads that use waits for.
     //
     // Page id of token tid % 32 of tile i (clamped into the request's pages;
     // tiles past the chunk load a valid id that is never used).
@@ -286,7 +285,7 @@ mla_partial_kernel(MlaArgs a)
     // movement and V^T is two transpose reads, one per subtile.
     auto compute = [&](int i, int buf) {
         const char *tile = s_tile[buf];
-        // key / query fragment kc of lane l is piece (4*kc + l/16) ^ swz(l%16)
+        // key fragment kc of lane l is piece (4*kc + l/16) ^ swz(l%16)
         // = 4*(kc ^ sb) + (l/16 ^ (swz & 3)), sb = swz / 4: the bases for even
         // and odd kc differ
         const int sw = swz(col);
@@ -296,9 +295,10 @@ mla_partial_kernel(MlaArgs a)
         const char *kr_odd = tile + col * kRowBytes + lo - 64 * sb;
         float4_t sc0 = float4_t{0.f, 0.f, 0.f, 0.f};
         float4_t sc1 = float4_t{0.f, 0.f, 0.f, 0.f};
-        // Fragment reads run ahead of the products (two key steps, four value
-        // steps), so each product waits for a read issued well before it: one
-        // wave per SIMD has no other wave to cover LDS latency.
+        // Fragment reads run ahead of the products (kKeyAhead key steps,
+        // kValueAhead value steps), so each product waits for a read issued
+        // well before it: one wave per SIMD has no other wave to cover LDS
+        // latency.
         auto kfrag = [&](int kc, half8_t &k0, half8_t &k1) {
             const char *kr = (kc & 1) ? kr_odd : kr_even;
             k0 = *reinterpret_cast<const half8_t *>(kr + 64 * kc);
@@ -387,12 +387,12 @@ mla_partial_kernel(MlaArgs a)
     // Iteration i writes tile i+1's rope piece into stage (i+1)%2 (last read
     // by tile i-1, before the previous barrier), starts its latent rows into
     // the same stage, loads tile i+2's rope piece and tile i+3's ids,
-    // computes tile i,
-    // writes tile i+3's offsets and ends with the one barrier, before which
-    // the kernel waits for tile i+1's loads.  The loop is not unrolled: one
-    // copy of the rare rescale path keeps the compiler from moving
-    // accumulator copies into the body.  Past the chunk the offsets are -1
-    // and the loads read zeros, written to a stage no later tile reads.
+    // computes tile i, writes tile i+3's offsets and ends with the one
+    // barrier, before which the kernel waits for tile i+1's loads.  The loop
+    // is not unrolled: one copy of the rare rescale path keeps the compiler
+    // from moving accumulator copies into the body.  Past the chunk the
+    // offsets are -1 and the loads read zeros, written to a stage no later
+    // tile reads.
     if (ntiles > 0) {
         offsets(0, load_id(0));
         offsets(1, load_id(1));
