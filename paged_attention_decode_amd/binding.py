@@ -127,11 +127,16 @@ def _hp(a: Optional[np.ndarray]):
 
 
 def _dev(x) -> Optional[int]:
-    """Device address of a torch tensor (or an int address, or None)."""
+    """Device address of a torch tensor (or an int address, or None).  A
+    tensor that is not in GPU memory is refused: the kernels would read its
+    host address as a device address."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError("paged_decode: kernel arguments must be GPU tensors (got %s on %s)"
+                         % (type(x).__name__, getattr(x, "device", "host")))
     return x.data_ptr()
 
 

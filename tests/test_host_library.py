@@ -255,3 +255,14 @@ def test_mla_partial_argument_errors_before_launch():
     fp32 = list(args)
     fp32[10] = B.PD_DTYPE_FP32
     assert lib.paged_mla_decode_partial(*fp32) == B.CODES["PD_E_UNSUPPORTED"]
+
+
+def test_kernel_wrappers_refuse_host_tensors():
+    """The binding refuses a CPU tensor where a kernel takes a device pointer,
+    before any call into the library."""
+    torch = pytest.importorskip("torch")
+    v = torch.zeros(2, 1, 4)
+    lse = torch.zeros(2, 1)
+    oi = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        B.paged_merge_states(v, lse, oi, 1, 1, 4, v[:1], lse[:1], stream=0)
