@@ -494,6 +494,24 @@ def chunk_candidates(indptr, default_c: int):
     return sorted(cands)
 
 
+def _autotune(make, run, indptr, candidates, n):
+    """Times run(dec) for make(0) (the device-default plan) and make(c) for
+    each candidate c (default: chunk_candidates()); returns (the fastest
+    decoder, [{pages_per_chunk, num_chunks, step_us}, ...])."""
+    base = make(0)
+    if candidates is None:
+        candidates = chunk_candidates(indptr, base.info.pages_per_chunk)
+    best, table = None, []
+    for c in candidates:
+        dec = base if c == base.info.pages_per_chunk else make(int(c))
+        t = graph_time(lambda i: run(dec), n)
+        table.append(dict(pages_per_chunk=dec.info.pages_per_chunk,
+                          num_chunks=dec.info.num_chunks, step_us=round(t * 1e6, 2)))
+        if best is None or t < best[0]:
+            best = (t, dec)
+    return best[1], table
+
+
 def autotune(csr: dict, q, k_pool, v_pool, sm_scale, *, page_size: int, num_pool_pages: int,
              num_qo_heads: int, num_kv_heads: int, head_dim: int, candidates=None,
              n: int = 120, device="cuda"):
@@ -505,20 +523,21 @@ def autotune(csr: dict, q, k_pool, v_pool, sm_scale, *, page_size: int, num_pool
     the given q and pools; the result does not depend on the choice beyond
     rounding (split-KV is exact in real arithmetic)."""
     dtype = q.dtype
-    base = PagedDecode(csr, page_size=page_size, num_pool_pages=num_pool_pages,
-                       num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
-                       head_dim=head_dim, dtype=dtype, device=device)
-    if candidates is None:
-        candidates = chunk_candidates(csr["indptr"], base.info.pages_per_chunk)
-    best, table = None, []
-    for c in candidates:
-        dec = base if c == base.info.pages_per_chunk else PagedDecode(
-            csr, page_size=page_size, num_pool_pages=num_pool_pages,
-            num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
-            fixed_pages_per_chunk=int(c), dtype=dtype, device=device)
-        t = graph_time(lambda i: dec.run(q, k_pool, v_pool, sm_scale), n)
-        table.append(dict(pages_per_chunk=dec.info.pages_per_chunk,
-                          num_chunks=dec.info.num_chunks, step_us=round(t * 1e6, 2)))
-        if best is None or t < best[0]:
-            best = (t, dec)
-    return best[1], table
+    make = lambda c: PagedDecode(  # noqa: E731
+        csr, page_size=page_size, num_pool_pages=num_pool_pages, num_qo_heads=num_qo_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, fixed_pages_per_chunk=c, dtype=dtype,
+        device=device)
+    return _autotune(make, lambda dec: dec.run(q, k_pool, v_pool, sm_scale), csr["indptr"],
+                     candidates, n)
+
+
+def autotune_mla(csr: dict, q, q_extra, k_pool, k_extra_pool, sm_scale, *, page_size: int,
+                 num_pool_pages: int, num_qo_heads: int, candidates=None, n: int = 120,
+                 device="cuda"):
+    """The chunk-size autotune of autotune() for the paged-MLA / DSA decode
+    (MlaDecode): returns (the fastest MlaDecode, its table)."""
+    make = lambda c: MlaDecode(  # noqa: E731
+        csr, page_size=page_size, num_pool_pages=num_pool_pages, num_qo_heads=num_qo_heads,
+        fixed_pages_per_chunk=c, device=device)
+    return _autotune(make, lambda dec: dec.run(q, q_extra, k_pool, k_extra_pool, sm_scale),
+                     csr["indptr"], candidates, n)

@@ -173,3 +173,29 @@ def test_mla_graph_replay_matches_eager(orc):
         ev, el = eager[rep % 2]
         np.testing.assert_allclose(out_g.cpu().numpy(), ev, rtol=0, atol=1e-6)
         np.testing.assert_allclose(lse_g.cpu().numpy(), el, rtol=0, atol=1e-6)
+
+
+def test_mla_autotune_times_every_candidate_and_stays_exact(orc):
+    """Chunk-size autotune of the MLA decode on a DSA selection: every
+    power-of-two candidate and the default plan's choice are timed, the
+    fastest is kept, and its output matches the oracle."""
+    w = workloads.dsa_sparse_fp16(batch=2, capacity=4096, kv_len=4000, topk=512)
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
+                            w.k_pool.shape[0])
+    q, qx = to_dev(w.q), to_dev(w.q_extra)
+    k, kx = to_dev(w.k_pool), to_dev(w.k_extra_pool)
+    dec, table = PD.autotune_mla(csr, q, qx, k, kx, w.sm_scale, page_size=w.page_size,
+                                 num_pool_pages=w.k_pool.shape[0],
+                                 num_qo_heads=w.num_qo_heads, n=30)
+    say("  autotune table: %s" % table)
+    cs = [row["pages_per_chunk"] for row in table]
+    assert cs == sorted(set(cs)) and {1, 2, 4, 256, 512} <= set(cs)
+    fastest = min(table, key=lambda row: row["step_us"])
+    assert dec.info.pages_per_chunk == fastest["pages_per_chunk"]
+    out, lse = dec.run(q, qx, k, kx, w.sm_scale)
+    torch.cuda.synchronize()
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    ref_v, ref_l = orc.attention_mla(w.q, w.q_extra, w.k_pool, w.k_extra_pool, ocsr,
+                                     w.page_size, w.sm_scale, nthreads=NTHREADS)
+    check(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, "autotuned")
