@@ -348,6 +348,14 @@ __device__ __forceinline__ void epilogue(const PartialArgs &a, EpilogueSmem<G, D
         // thread counts the chunk.  The workgroup that brings the count to
         // ntiles merges rows n - t .. n - t + ntiles - 1, reading them with
         // coherent loads, and resets the counter for the next launch.
+        //
+        // Ordering: the rows and LSEs are written and read only with
+        // agent-scope atomics, so no cache holds a stale copy; the writers'
+        // stores have completed before their count is added, and the
+        // merging workgroup's loads are issued after (and only because of)
+        // the count it read.  The counter therefore needs no acquire or
+        // release of its own, which on gfx950 would write back and
+        // invalidate the whole L2 of the XCD.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvh;
@@ -721,7 +729,8 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
         // fence is a plain vmcnt wait here, not a cache writeback), then one
         // thread counts the chunk.  The workgroup that brings the count to
         // ntiles merges rows n - t .. n - t + ntiles - 1 for its heads,
-        // reading them with coherent loads, and resets the counter.
+        // reading them with coherent loads, and resets the counter.  (The
+        // ordering argument is the one in epilogue(), above.)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();
         int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvg;
