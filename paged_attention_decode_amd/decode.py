@@ -449,6 +449,7 @@ class MlaDecode:
         self.merge(stream)
         return self.out, self.lse
 
+
 def graph_time(fn, n: int = 120, per_graph: int = 30) -> float:
     """GPU seconds per call of fn(i): per_graph calls are captured once in a
     HIP graph and the graph is replayed n // per_graph times between events

@@ -199,3 +199,31 @@ def test_mla_autotune_times_every_candidate_and_stays_exact(orc):
     ref_v, ref_l = orc.attention_mla(w.q, w.q_extra, w.k_pool, w.k_extra_pool, ocsr,
                                      w.page_size, w.sm_scale, nthreads=NTHREADS)
     check(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, "autotuned")
+
+
+def test_mla_strided_pools(orc):
+    """Pools that are views of wider allocations: each page holds one padding
+    row, latent rows are 1024 halves apart and rope rows 96 apart, and every
+    element outside the views is NaN -- the kernel must address rows by the
+    caller's strides alone."""
+    w = workloads.mla_paged("mla_strided", seed=321, logical_start=[0, 5, 0, 40],
+                            written_len=[500, 260, 1, 41], num_qo_heads=64, page_size=16,
+                            poison_unused=True, poison_indexer=True)
+    pages, ps = w.k_pool.shape[0], w.page_size
+    kw = np.full((pages, ps + 1, 1024), np.nan, np.float16)
+    kw[:, :ps, :w.k_pool.shape[2]] = w.k_pool
+    xw = np.full((pages, ps + 1, 96), np.nan, np.float16)
+    xw[:, :ps, :w.extra_dim] = w.k_extra_pool
+    k = to_dev(kw)[:, :ps, :w.k_pool.shape[2]]
+    kx = to_dev(xw)[:, :ps, :w.extra_dim]
+    assert k.stride() == ((ps + 1) * 1024, 1024, 1) and kx.stride() == ((ps + 1) * 96, 96, 1)
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, ps, pages)
+    for fixed in (0, 2):
+        dec = PD.MlaDecode(csr, page_size=ps, num_pool_pages=pages, num_qo_heads=w.num_qo_heads,
+                           fixed_pages_per_chunk=fixed)
+        out, lse = dec.run(to_dev(w.q), to_dev(w.q_extra), k, kx, w.sm_scale)
+        torch.cuda.synchronize()
+        ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len, ps)
+        ref_v, ref_l = orc.attention_mla(w.q, w.q_extra, w.k_pool, w.k_extra_pool, ocsr, ps,
+                                         w.sm_scale, nthreads=NTHREADS)
+        check(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, "strided c=%d" % fixed)
