@@ -293,6 +293,30 @@ int paged_merge_states(const float *v_in, const float *lse_in, const int32_t *o_
  *   Hq] fp32 with rows = o_indptr[batch] of the layout.  dst0, dst1: DEVICE
  *   copies of the layout's arrays.  head_dim % 4 == 0 and 16-byte aligned buffers
  *   (PD_E_UNSUPPORTED otherwise).
+ *
+ * paged_cascade_merge_layout (HOST): where the level-0 rows of each request
+ *   sit when the stacked launches write one buffer, launch after launch.
+ *   Members are stacked members_per_launch at a time in member_req order, so
+ *   launch j stacks S_j = min(members_per_launch, num_members - j *
+ *   members_per_launch) members and holds level0_rows x S_j*Hq rows of D
+ *   floats ([level0_rows, S_j*Hq, D], the partial kernel's output for that
+ *   launch), starting at row j * members_per_launch * level0_rows * Hq.
+ *   Out: l0_desc [batch, 3] int32 = (that first row, S_j, the request's
+ *   position in its launch) for a member, (0, 0, -1) for a non-member.
+ *   PD_E_ARG if member_req is not ascending within [0, batch) or the rows
+ *   exceed int32.
+ *
+ * paged_cascade_merge_states (DEVICE, caller's stream): the cascade's
+ *   merge, read in place (the same algebra as paged_merge_states).  Output
+ *   row r, head h = kv*G + g merges, in this order, the request's level-0
+ *   rows i < n0 (members only: row first + i*S*Hq + kv*S*G + p*G + g of v0 /
+ *   lse0, with (first, S, p) = l0_desc[r]) and its level-1 rows
+ *   o_indptr1[r] .. o_indptr1[r+1] of v1 [n1, Hq, D] / lse1 [n1, Hq].  This
+ *   is paged_cascade_gather_states followed by paged_merge_states without
+ *   the intermediate copy.  l0_desc, o_indptr1: DEVICE.  v_out [batch, Hq,
+ *   D], lse_out [batch, Hq] fp32 (log2), not aliasing the inputs.
+ *   head_dim % 32 == 0 and 16-byte aligned V buffers, else
+ *   PD_E_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 int paged_cascade_detect(int32_t batch, const int32_t *indptr, const int32_t *indices,
                          const int32_t *first_page_offset, int32_t min_shared_pages,
@@ -319,6 +343,16 @@ int paged_cascade_gather_states(const float *v0, const float *lse0, int32_t n0,
                                 const float *lse1, int32_t n1, const int32_t *dst1,
                                 int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                                 float *v_dst, float *lse_dst, void *stream);
+
+int paged_cascade_merge_layout(int32_t batch, const int32_t *member_req, int32_t num_members,
+                               int32_t members_per_launch, int32_t level0_rows,
+                               int32_t num_qo_heads, int32_t *l0_desc);
+
+int paged_cascade_merge_states(const float *v0, const float *lse0, int32_t n0,
+                               const int32_t *l0_desc, const float *v1, const float *lse1,
+                               const int32_t *o_indptr1, int32_t batch, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, float *v_out,
+                               float *lse_out, void *stream);
 
 /* ------------------------------------------------------------------------
  * Block selections -- mlxcel "Sparse paged decode" doc (the two page-table

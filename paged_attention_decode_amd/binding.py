@@ -33,6 +33,7 @@ EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
             "paged_cascade_detect", "paged_cascade_split", "paged_cascade_layout",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
+            "paged_cascade_merge_layout", "paged_cascade_merge_states",
             "paged_sparse_csr", "paged_sparse_expand_blocks", "paged_mla_decode_partial",
             "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
             "paged_fastdiv_eval"]
@@ -83,6 +84,9 @@ _SIGS = {
     "paged_cascade_stack_q": (i32, [vp, i32, vp, i32, i32, i32, i32, vp, vp]),
     "paged_cascade_gather_states": (i32, [vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, i32, i32,
                                           vp, vp, vp]),
+    "paged_cascade_merge_layout": (i32, [i32, i32p, i32, i32, i32, i32, i32p]),
+    "paged_cascade_merge_states": (i32, [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                         vp, vp]),
     "paged_sparse_csr": (i32, [i32, i32, i32, i32, i32p, i32p, i32p, i32p]),
     "paged_sparse_expand_blocks": (i32, [vp, i32, i32, vp, i32, vp, vp, i32, vp, vp]),
     "paged_decode_q_heads_per_wg": (i32, [i32, i32, i32]),
@@ -339,6 +343,27 @@ def paged_cascade_gather_states(v0, lse0, n0, members, dst0, v1, lse1, n1, dst1,
                                               _dev(v1), _dev(lse1), n1, _dev(dst1),
                                               num_qo_heads, num_kv_heads, head_dim, _dev(v_dst),
                                               _dev(lse_dst), _stream(stream)))
+
+
+def paged_cascade_merge_layout(batch, member_req, members_per_launch, level0_rows,
+                               num_qo_heads):
+    """Returns l0_desc [batch, 3] int32: (first level-0 row of the request's
+    launch, members stacked in it, position in it; -1 for a non-member)."""
+    member_req = _host_i32(member_req)
+    desc = np.zeros((batch, 3), np.int32)
+    _check(load().paged_cascade_merge_layout(batch, _hp(member_req), member_req.size,
+                                             members_per_launch, level0_rows, num_qo_heads,
+                                             _hp(desc)))
+    return desc
+
+
+def paged_cascade_merge_states(v0, lse0, n0, l0_desc, v1, lse1, o_indptr1, batch,
+                               num_qo_heads, num_kv_heads, head_dim, v_out, lse_out,
+                               stream=None):
+    _check(load().paged_cascade_merge_states(_dev(v0), _dev(lse0), n0, _dev(l0_desc), _dev(v1),
+                                             _dev(lse1), _dev(o_indptr1), batch, num_qo_heads,
+                                             num_kv_heads, head_dim, _dev(v_out), _dev(lse_out),
+                                             _stream(stream)))
 
 
 def paged_sparse_csr(blocks_per_request, block_size, tail, token_exact):

@@ -9,6 +9,9 @@
 // into each member's merge group, next to that member's own level-1 rows
 // (rows placed by the host layout; a non-member's group is its level-1 rows
 // alone), so a single merge pairing each member's states finishes the step.
+// The merge can also apply the inverse transpose itself and read the rows
+// where the launches wrote them (paged_cascade_merge_states); the copy here
+// serves other head sizes.
 
 #include <hip/hip_runtime.h>
 

@@ -185,3 +185,34 @@ extern "C" int paged_cascade_layout(int32_t batch, const int32_t *member_req, in
     }
     return PD_OK;
 }
+
+extern "C" int paged_cascade_merge_layout(int32_t batch, const int32_t *member_req,
+                                          int32_t num_members, int32_t members_per_launch,
+                                          int32_t level0_rows, int32_t num_qo_heads,
+                                          int32_t *l0_desc)
+{
+    if (!member_req || !l0_desc) return fail(PD_E_NULL, "paged_cascade_merge_layout: null pointer");
+    if (batch < 1 || num_members < 1 || members_per_launch < 1 || level0_rows < 1 ||
+        num_qo_heads < 1)
+        return fail(PD_E_ARG, "paged_cascade_merge_layout: bad sizes");
+    if (int64_t(level0_rows) * num_members * num_qo_heads > INT32_MAX)
+        return fail(PD_E_ARG, "paged_cascade_merge_layout: level-0 rows exceed int32");
+    for (int32_t r = 0; r < batch; ++r) {
+        l0_desc[3 * r] = 0;
+        l0_desc[3 * r + 1] = 0;
+        l0_desc[3 * r + 2] = -1;
+    }
+    for (int32_t m = 0; m < num_members; ++m) {
+        const int32_t r = member_req[m];
+        if (r < 0 || r >= batch || (m > 0 && r <= member_req[m - 1]))
+            return fail(PD_E_ARG,
+                        "paged_cascade_merge_layout: member_req must be ascending requests");
+        const int32_t j = m / members_per_launch;            // launch
+        const int32_t first_member = j * members_per_launch;
+        const int32_t stack = std::min(members_per_launch, num_members - first_member);
+        l0_desc[3 * r] = first_member * level0_rows * num_qo_heads;
+        l0_desc[3 * r + 1] = stack;
+        l0_desc[3 * r + 2] = m - first_member;
+    }
+    return PD_OK;
+}

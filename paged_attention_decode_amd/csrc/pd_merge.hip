@@ -10,8 +10,10 @@
 // One thread owns four consecutive dims of one (output row, head) and walks
 // the group's rows once for the max and once for the weighted sum; the lse
 // values it reads are shared by the D/4 threads of the head and come from
-// cache.  No LDS and no barrier, so any grouping works (the cascade reuses
-// it with its own o_indptr).
+// cache.  No LDS and no barrier, so any grouping works (the cascade's
+// gathered layout reuses it with its own o_indptr).  The slice kernel below
+// also reads a cascade step's groups in place: each member's stacked
+// level-0 rows followed by its own level-1 rows.
 
 #include <hip/hip_runtime.h>
 
@@ -209,11 +211,85 @@ __device__ __forceinline__ float4 shfl_xor4(const float4 &v, int mask)
                        __shfl_xor(v.w, mask));
 }
 
-template <int DL, int UNROLL = kSplitUnroll>
-__global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restrict__ v_in,
-                                                          const float *__restrict__ lse_in,
-                                                          const int32_t *__restrict__ o_indptr,
-                                                          int32_t num_heads, int32_t head_dim,
+// Where the rows of a merge group live.  bind(o, h, H, D) gives the group of
+// output row o, head h as rows [b, e) with lse(i) and v(i) (a pointer to row
+// i's head-h vector of D floats).
+//
+// FlatRows: the rows o_indptr[o] .. o_indptr[o+1] of v_in [N, H, D] and
+// lse_in [N, H].
+struct FlatRows {
+    const float *v_in, *lse_in;
+    const int32_t *o_indptr;
+    struct Group {
+        int b, e, h;
+        const float *v_in, *lse_in;
+        int32_t num_heads, head_dim;
+        __device__ float lse(int i) const { return lse_in[int64_t(i) * num_heads + h]; }
+        __device__ const float *v(int i) const
+        {
+            return v_in + (int64_t(i) * num_heads + h) * head_dim;
+        }
+    };
+    __device__ Group bind(int64_t o, int h, int32_t num_heads, int32_t head_dim) const
+    {
+        return Group{o_indptr[o], o_indptr[o + 1], h, v_in, lse_in, num_heads, head_dim};
+    }
+};
+
+// CascadeRows: a cascade step's groups read in place.  Output row r's group
+// is its level-0 rows (a member of a stacked launch; none otherwise)
+// followed by its own level-1 rows o_indptr1[r] .. o_indptr1[r+1] of v1 [n1,
+// Hq, D].  The level-0 launches' rows sit one after another in v0 as [D]
+// vectors: launch j, stacking S members, holds rows [first_j, first_j +
+// n0*S*Hq), chunk i's stacked head h0 at first_j + i*S*Hq + h0, and member
+// position p's head h = kv*G + g is stacked head kv*S*G + p*G + g.  l0_desc
+// [batch, 3] = (first_j, S, p) per request, p = -1 for a non-member.
+struct CascadeRows {
+    const float *v0, *lse0, *v1, *lse1;
+    const int32_t *l0_desc, *o_indptr1;
+    int32_t n0, group_size;
+    struct Group {
+        int b, e, n0r;
+        int64_t row0, step0, row1;      // level 0: row0 + i*step0; level 1: row1 + i*Hq
+        const float *v0, *lse0, *v1, *lse1;
+        int32_t num_heads, head_dim;
+        __device__ int64_t row(int i) const
+        {
+            return i < n0r ? row0 + int64_t(i) * step0 : row1 + int64_t(i) * num_heads;
+        }
+        __device__ float lse(int i) const { return (i < n0r ? lse0 : lse1)[row(i)]; }
+        __device__ const float *v(int i) const { return (i < n0r ? v0 : v1) + row(i) * head_dim; }
+    };
+    __device__ Group bind(int64_t r, int h, int32_t num_heads, int32_t head_dim) const
+    {
+        const int first = l0_desc[3 * r];
+        const int stack = l0_desc[3 * r + 1];
+        const int pos = l0_desc[3 * r + 2];
+        const int o1b = o_indptr1[r];
+        const int own = o_indptr1[r + 1] - o1b;
+        const int n0r = pos >= 0 ? n0 : 0;
+        const int kv = h / group_size;
+        const int g = h - kv * group_size;
+        Group q;
+        q.b = 0;
+        q.e = n0r + own;
+        q.n0r = n0r;
+        q.row0 = int64_t(first) + (int64_t(kv) * stack + pos) * group_size + g;
+        q.step0 = int64_t(stack) * num_heads;
+        q.row1 = (int64_t(o1b) - n0r) * num_heads + h;
+        q.v0 = v0;
+        q.lse0 = lse0;
+        q.v1 = v1;
+        q.lse1 = lse1;
+        q.num_heads = num_heads;
+        q.head_dim = head_dim;
+        return q;
+    }
+};
+
+template <int DL, int UNROLL, typename Rows>
+__global__ void __launch_bounds__(256) merge_slice_kernel(const Rows rows, int32_t num_heads,
+                                                          int32_t head_dim,
                                                           float *__restrict__ v_out,
                                                           float *__restrict__ lse_out)
 {
@@ -231,8 +307,9 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restric
     const int dv = int(ohs - oh * slices) * DL + dl_i;
     const int h = int(oh % num_heads);
     const int64_t o = oh / num_heads;
-    const int b = o_indptr[o];
-    const int e = o_indptr[o + 1];
+    const typename Rows::Group grp = rows.bind(o, h, num_heads, head_dim);
+    const int b = grp.b;
+    const int e = grp.e;
 
     MState<V> st;
     st.m = -INFINITY;
@@ -245,8 +322,8 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const float *__restric
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int i = min(i0 + u * SPLIT, e - 1);
-            x[u] = lse_in[int64_t(i) * num_heads + h];
-            vi[u] = reinterpret_cast<const V *>(v_in + (int64_t(i) * num_heads + h) * head_dim)[dv];
+            x[u] = grp.lse(i);
+            vi[u] = reinterpret_cast<const V *>(grp.v(i))[dv];
         }
         float mb = st.m;
 #pragma unroll
@@ -411,19 +488,21 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const FlatRows rows{v_in, lse_in, o_indptr};
     if (vec4 && head_dim % 512 == 0) {
         // wide heads: one workgroup per (output row, head, 4*kWideDL-dim slice)
         const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / (4 * kWideDL));
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
-        hipLaunchKernelGGL((merge_slice_kernel<kWideDL, kWideUnroll>), dim3(uint32_t(nblk)), dim3(256), 0, s, v_in,
-                           lse_in, o_indptr, num_heads, head_dim, v_out, lse_out);
+        hipLaunchKernelGGL((merge_slice_kernel<kWideDL, kWideUnroll, FlatRows>),
+                           dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_heads, head_dim,
+                           v_out, lse_out);
     } else if (vec4 && head_dim % (4 * kNarrowDL) == 0) {
         // one workgroup per (output row, head, 4*kNarrowDL-dim slice)
         const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / (4 * kNarrowDL));
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
-        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kNarrowUnroll>), dim3(uint32_t(nblk)),
-                           dim3(256), 0, s, v_in, lse_in, o_indptr, num_heads, head_dim, v_out,
-                           lse_out);
+        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kNarrowUnroll, FlatRows>),
+                           dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_heads, head_dim,
+                           v_out, lse_out);
     } else if (head_dim / w <= 256) {
         // one workgroup per (output row, head), rows split across lanes
         const int64_t nblk = int64_t(num_out_rows) * num_heads;
@@ -443,6 +522,48 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return fail(PD_E_HIP, std::string("paged_merge_states: launch failed: ") +
+                                  hipGetErrorString(err));
+    return PD_OK;
+}
+
+extern "C" int paged_cascade_merge_states(const float *v0, const float *lse0, int32_t n0,
+                                          const int32_t *l0_desc, const float *v1,
+                                          const float *lse1, const int32_t *o_indptr1,
+                                          int32_t batch, int32_t num_qo_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, float *v_out,
+                                          float *lse_out, void *stream)
+{
+    if (!v0 || !lse0 || !l0_desc || !v1 || !lse1 || !o_indptr1 || !v_out || !lse_out)
+        return fail(PD_E_NULL, "paged_cascade_merge_states: null pointer");
+    if (batch < 1 || n0 < 1 || num_qo_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+        num_qo_heads % num_kv_heads)
+        return fail(PD_E_ARG, "paged_cascade_merge_states: bad sizes");
+    if (head_dim % (4 * kNarrowDL) ||
+        ((reinterpret_cast<uintptr_t>(v0) | reinterpret_cast<uintptr_t>(v1) |
+          reinterpret_cast<uintptr_t>(v_out)) & 15u))
+        return fail(PD_E_UNSUPPORTED, "paged_cascade_merge_states: head_dim must be a multiple "
+                                      "of 32 and the V buffers 16-byte aligned");
+    const CascadeRows rows{v0, lse0, v1, lse1, l0_desc, o_indptr1, n0,
+                           num_qo_heads / num_kv_heads};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // The slice widths of paged_merge_states.  At 4 members x 8192 shared
+    // tokens (about 300 rows per group), 16- and 8-dim slices, or 8 rows in
+    // flight per lane, were as fast or slower (MI355X).
+    const bool wide = head_dim % (4 * kWideDL) == 0;
+    const int64_t nblk =
+        int64_t(batch) * num_qo_heads * (head_dim / (4 * (wide ? kWideDL : kNarrowDL)));
+    if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_cascade_merge_states: too large");
+    if (wide)
+        hipLaunchKernelGGL((merge_slice_kernel<kWideDL, kWideUnroll, CascadeRows>),
+                           dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_qo_heads, head_dim,
+                           v_out, lse_out);
+    else
+        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kNarrowUnroll, CascadeRows>),
+                           dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_qo_heads, head_dim,
+                           v_out, lse_out);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PD_E_HIP, std::string("paged_cascade_merge_states: launch failed: ") +
                                   hipGetErrorString(err));
     return PD_OK;
 }

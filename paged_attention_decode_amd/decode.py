@@ -89,6 +89,21 @@ class PagedDecode:
                     num_wgs=i.num_wgs, needs_merge=bool(i.needs_merge),
                     target_wgs=i.target_wgs, workspace_bytes=i.workspace_bytes)
 
+    def use_workspace(self, v_partial, lse_partial):
+        """Write the partial rows into caller-owned fp32 tensors of shape
+        [num_chunks, Hq, D] and [num_chunks, Hq] (e.g. views of a larger
+        buffer) instead of this object's own."""
+        n = self.info.num_chunks
+        if tuple(v_partial.shape) != (n, self.num_qo_heads, self.head_dim) or \
+                tuple(lse_partial.shape) != (n, self.num_qo_heads) or \
+                v_partial.dtype != torch.float32 or lse_partial.dtype != torch.float32 or \
+                not v_partial.is_contiguous() or not lse_partial.is_contiguous():
+            raise ValueError("workspace must be contiguous fp32 [%d, %d, %d] and [%d, %d]"
+                             % (n, self.num_qo_heads, self.head_dim, n, self.num_qo_heads))
+        if self.out is self.v_partial:
+            self.out, self.lse = v_partial, lse_partial
+        self.v_partial, self.lse_partial = v_partial, lse_partial
+
     def partial(self, q, k_pool, v_pool, sm_scale, stream=None):
         ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
         B.paged_decode_partial(q, k_pool, v_pool, ps_, ts_, hs_, _pd_dtype(q), self.d_indices,
@@ -135,16 +150,22 @@ class CascadeDecode:
     shared_pages are given.  Level 0 attends the span once per subgroup of
     members with their query heads stacked (a launch stacks at most 32 query
     heads per KV head, 16 off the MFMA kernel, so a larger M*G splits the
-    members into subgroups that each read the span); level 1 attends every request's own pages -- the members'
-    pages after the span and the other requests' whole lists; one merge over
-    the host-computed layout finishes every request.  With no qualifying span
-    the step is the flat decode.
+    members into subgroups that each read the span); level 1 attends every
+    request's own pages -- the members' pages after the span and the other
+    requests' whole lists; one merge finishes every request.  The merge reads
+    the level-0 rows where the stacked launches wrote them
+    (``paged_cascade_merge_states``; head_dim a multiple of 32), or, with
+    merge_in_place=False or another head size, from a copy that un-stacks
+    them into the host-computed layout (``paged_cascade_gather_states`` +
+    ``paged_merge_states``).  With no qualifying span the step is the flat
+    decode.
     """
 
     def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
                  num_kv_heads: int, head_dim: int, members=None, shared_pages: int = 0,
                  min_shared_pages: int = 16, min_members: int = 2, target_wgs: int = 0,
-                 target_wgs_level0: int = 0, dtype=torch.float16, device="cuda"):
+                 target_wgs_level0: int = 0, merge_in_place: bool = True,
+                 dtype=torch.float16, device="cuda"):
         indptr = np.asarray(csr["indptr"], np.int32)
         indices = np.asarray(csr["indices"], np.int32)
         lpl = np.asarray(csr["last_page_len"], np.int32)
@@ -190,6 +211,24 @@ class CascadeDecode:
         self.level1 = PagedDecode(csr1, num_qo_heads=num_qo_heads, target_wgs=target_wgs, **kw)
         self.n0 = self.level0[0].info.num_chunks
         self.n1 = self.level1.info.num_chunks
+        self.rows0 = None
+        if merge_in_place and head_dim % 32 == 0:
+            # the merge reads the level-0 rows in place: the launches write one
+            # buffer, one after another
+            total = sum(self.n0 * sub.size * num_qo_heads for sub in self.subgroups)
+            self.rows0 = (torch.empty((total, head_dim), dtype=torch.float32, device=self.device),
+                          torch.empty(total, dtype=torch.float32, device=self.device))
+            first = 0
+            for lv, sub in zip(self.level0, self.subgroups):
+                rows = self.n0 * sub.size * num_qo_heads
+                lv.use_workspace(
+                    self.rows0[0][first:first + rows].view(self.n0, sub.size * num_qo_heads,
+                                                           head_dim),
+                    self.rows0[1][first:first + rows].view(self.n0, sub.size * num_qo_heads))
+                first += rows
+            self.d_l0_desc = _dev_i32(
+                B.paged_cascade_merge_layout(self.batch, self.member_req, per, self.n0,
+                                             num_qo_heads), self.device)
         dst0, dst1, oi = B.paged_cascade_layout(self.member_req, self.n0, self.level1.o_indptr)
         self.o_indptr = oi
         self.d_oindptr = _dev_i32(oi, self.device)
@@ -229,10 +268,17 @@ class CascadeDecode:
         for j, sub in enumerate(self.subgroups):
             if self.q0[j] is None or self.q0[j].dtype != q.dtype:
                 self.q0[j] = torch.empty((1, sub.size * hq, d), dtype=q.dtype, device=q.device)
+        for j, sub in enumerate(self.subgroups):
             B.paged_cascade_stack_q(q, _pd_dtype(q), self.d_members[j], sub.size, hq, hkv, d,
                                     self.q0[j], stream)
             self.level0[j].partial(self.q0[j], k_pool, v_pool, sm_scale, stream)
         self.level1.partial(q, k_pool, v_pool, sm_scale, stream)
+        if self.rows0 is not None:
+            B.paged_cascade_merge_states(self.rows0[0], self.rows0[1], self.n0, self.d_l0_desc,
+                                         self.level1.v_partial, self.level1.lse_partial,
+                                         self.level1.d_oindptr, self.batch, hq, hkv, d,
+                                         self.out, self.lse, stream)
+            return self.out, self.lse
         for j, sub in enumerate(self.subgroups):
             last = j == len(self.subgroups) - 1       # the last call also moves level 1
             B.paged_cascade_gather_states(

@@ -157,3 +157,53 @@ def test_layout_groups_level0_rows_before_own_rows():
                 assert dst1[o1[r] + t] == oi[r] + lead + t
                 rows[dst1[o1[r] + t]] = 1
         assert np.all(rows >= 0)       # every merge-input row is written exactly by one source
+
+
+def test_merge_layout_locates_every_stacked_row():
+    """The in-place merge's descriptors against an enumeration of the stacked
+    launches' output: launch j stacks members j*per .. of member_req and writes
+    [n0, S*Hq] rows after the earlier launches; member position p's head
+    kv*G + g is stacked head kv*S*G + p*G + g (the head stacking)."""
+    rng = np.random.Generator(np.random.PCG64(73))
+    for _ in range(200):
+        batch = int(rng.integers(1, 12))
+        k = int(rng.integers(1, batch + 1))
+        members = np.sort(rng.choice(batch, size=k, replace=False)).astype(np.int32)
+        per = int(rng.integers(1, 5))
+        n0 = int(rng.integers(1, 6))
+        hkv = int(rng.integers(1, 4))
+        g = int(rng.integers(1, 5))
+        hq = hkv * g
+        desc = B.paged_cascade_merge_layout(batch, members, per, n0, hq)
+        where = {}
+        row = 0
+        for j in range(0, k, per):
+            launch = members[j:j + per]
+            s = launch.size
+            for i in range(n0):
+                for kv in range(hkv):
+                    for p in range(s):
+                        for gi in range(g):
+                            where[(int(launch[p]), i, kv * g + gi)] = row
+                            row += 1
+        assert row == n0 * k * hq
+        for r in range(batch):
+            first, s, p = (int(x) for x in desc[r])
+            if r not in members:
+                assert (first, s, p) == (0, 0, -1)
+                continue
+            for i in range(n0):
+                for h in range(hq):
+                    kv, gi = divmod(h, g)
+                    assert first + i * s * hq + kv * s * g + p * g + gi == where[(r, i, h)]
+
+
+def test_merge_layout_rejects_bad_members():
+    with pytest.raises(B.PagedDecodeError) as e:
+        B.paged_cascade_merge_layout(4, [2, 1], 2, 3, 8)
+    assert e.value.name == "PD_E_ARG"
+    with pytest.raises(B.PagedDecodeError):
+        B.paged_cascade_merge_layout(4, [0, 4], 2, 3, 8)
+    with pytest.raises(B.PagedDecodeError) as e:
+        B.paged_cascade_merge_layout(4, [0, 1], 2, 1 << 20, 1 << 12)   # rows past int32
+    assert e.value.name == "PD_E_ARG"

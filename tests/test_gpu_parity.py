@@ -277,12 +277,14 @@ def test_block_sparse_decode(orc, token_exact, geom):
                 "block sparse")
 
 
-@pytest.mark.parametrize("kind", ["flat", "block-sparse"])
+@pytest.mark.parametrize("kind", ["flat", "block-sparse", "cascade"])
 def test_decode_step_replayed_from_hip_graph(orc, kind):
     """A decode step captured in a HIP graph (partial + merge; for the block
-    selection also the row expansion) and replayed: every replay equals the
-    eager step on the same inputs, with eager work and synchronization
-    between replays and a new query written into the captured buffer."""
+    selection also the row expansion; for the cascade the head stacking,
+    both levels and the in-place merge) and replayed: every
+    replay equals the eager step on the same inputs, with eager work and
+    synchronization between replays and a new query written into the
+    captured buffer."""
     if kind == "flat":
         w = cached("batched_fp16", poison_unused=True)
         csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, w.page_size,
@@ -293,6 +295,14 @@ def test_decode_step_replayed_from_hip_graph(orc, kind):
         assert dec.info.needs_merge
         k, v = to_dev(w.k_pool), to_dev(w.v_pool)
         qs = [w.q, workloads._normal(np.random.default_rng(3), w.q.shape, workloads.FP16)]
+        step = lambda qb: dec.run(qb, k, v, w.sm_scale)   # noqa: E731
+    elif kind == "cascade":
+        w = workloads.cascade_fp16(seed=7, members=5, prefix_tokens=2048, suffix_lo=100,
+                                   suffix_hi=900, poison_unused=True)
+        dec = _cascade(w)
+        assert dec.active and dec.rows0 is not None
+        k, v = to_dev(w.k_pool), to_dev(w.v_pool)
+        qs = [w.q, workloads._normal(np.random.default_rng(5), w.q.shape, workloads.FP16)]
         step = lambda qb: dec.run(qb, k, v, w.sm_scale)   # noqa: E731
     else:
         w = workloads.block_sparse_fp16(seed=8, hq=16, hkv=4, cap=8192, block_size=64,
@@ -376,11 +386,13 @@ def _oracle_flat(orc, w):
                          nthreads=NTHREADS)
 
 
-def test_cascade_matches_flat_and_oracle(orc):
+@pytest.mark.parametrize("in_place", [True, False], ids=["in-place-merge", "gathered-merge"])
+def test_cascade_matches_flat_and_oracle(orc, in_place):
     w = workloads.cascade_fp16(poison_unused=True)
     flat = run_flat(orc, w, target=0, check_partials=False)
     sp = w.extra["shared_pages"]
-    cas = _cascade(w)
+    cas = _cascade(w, merge_in_place=in_place)
+    assert (cas.rows0 is not None) == in_place
     say("case cascade members=%d shared_pages=%d suffix=%s plan=%s" % (
         w.batch, sp, list(w.extra["suffix_tokens"]), cas.plan_summary()))
     # detection finds the whole batch sharing the 8192-token prefix
@@ -435,14 +447,15 @@ def _mixed_batch(seed, members, hq=32, hkv=8, prefix_pages=40, ps=16):
     return workloads.poison_invisible(w)
 
 
+@pytest.mark.parametrize("in_place", [True, False], ids=["in-place-merge", "gathered-merge"])
 @pytest.mark.parametrize("members,hq", [(3, 32), (6, 32), (5, 16), (9, 32)])
-def test_cascade_mixed_batch_and_subgroups(orc, members, hq):
+def test_cascade_mixed_batch_and_subgroups(orc, members, hq, in_place):
     """Members, a mid-page window over the same pages, and unrelated requests in
     one batch.  Stacked groups of 12 and 24 query heads per KV head run on the
     MFMA kernel; 9 members at G = 4 split into launches of 8 + 1 members (32 + 4
     heads), 5 members at G = 2 into 4 + 1 (8 + 2)."""
     w = _mixed_batch(80 + members, members, hq=hq)
-    cas = _cascade(w, min_shared_pages=16)
+    cas = _cascade(w, min_shared_pages=16, merge_in_place=in_place)
     say("case mixed cascade members=%d hq=%d plan=%s" % (members, hq, cas.plan_summary()))
     assert cas.active and list(cas.member_req) == list(range(members))
     assert cas.shared_pages == 40
@@ -453,6 +466,101 @@ def test_cascade_mixed_batch_and_subgroups(orc, members, hq):
     torch.cuda.synchronize()
     ref_v, ref_l = _oracle_flat(orc, w)
     check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "mixed cascade")
+
+
+@pytest.mark.parametrize("members,hq,d", [(9, 32, 128), (5, 16, 128), (4, 32, 64)])
+def test_cascade_in_place_merge_equals_gathered_merge(orc, members, hq, d):
+    """The merge that reads the stacked level-0 rows in place visits each
+    group's rows in the order the gathered copy lays them out, so the two
+    compositions agree bit for bit (several stacked launches included), and
+    both match the oracle."""
+    w = workloads.cascade_fp16(seed=90 + members, members=members, prefix_tokens=1024,
+                               suffix_lo=16, suffix_hi=400, hq=hq, hkv=hq // 4, d=d,
+                               poison_unused=True)
+    a = _cascade(w, merge_in_place=True)
+    b = _cascade(w, merge_in_place=False)
+    say("case cascade in-place vs gathered members=%d hq=%d d=%d plan=%s"
+        % (members, hq, d, a.plan_summary()))
+    assert a.active and a.rows0 is not None and b.rows0 is None
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    oa, la = (t.clone() for t in a.run(q, k, v, w.sm_scale))
+    ob, lb = b.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    ref_v, ref_l = _oracle_flat(orc, w)
+    check_close(oa.cpu().numpy(), la.cpu().numpy(), ref_v, ref_l, w.dtype, "in-place cascade")
+
+
+@pytest.mark.parametrize("d", [128, 512, 64])
+def test_cascade_merge_states_against_oracle(orc, d):
+    """The in-place cascade merge on synthetic states: members 0, 2, 3 of 5
+    requests stacked two per launch (launches of 2 and 1 members), empty
+    chunks (lse = -inf, V never read), a member with one own row, and a
+    non-member with none (zeros, -inf).  The expected groups are gathered on
+    the host from the stacking rule and merged by the oracle."""
+    rng = np.random.default_rng(95 + d)
+    batch, hkv, g, n0, per = 5, 2, 4, 7, 2
+    hq = hkv * g
+    members = np.array([0, 2, 3], np.int32)
+    counts = np.array([2, 0, 1, 4, 3])
+    o1 = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n1 = int(o1[-1])
+    rows0 = n0 * members.size * hq
+    v0 = rng.standard_normal((rows0, d)).astype(np.float32)
+    l0 = (rng.standard_normal(rows0) * 6).astype(np.float32)
+    v1 = rng.standard_normal((n1, hq, d)).astype(np.float32)
+    l1 = (rng.standard_normal((n1, hq)) * 6).astype(np.float32)
+    l0[rng.random(rows0) < 0.2] = -np.inf
+    l1[rng.random((n1, hq)) < 0.2] = -np.inf
+    v0[np.isneginf(l0)] = 1e30
+    v1[np.isneginf(l1)] = 1e30
+    desc = B.paged_cascade_merge_layout(batch, members, per, n0, hq)
+    # host gather from the stacking rule: launch j holds members j*per ..,
+    # [n0, S*Hq] rows, stacked head kv*S*G + p*G + g
+    gv, gl, oi = [], [], [0]
+    for r in range(batch):
+        if r in members:
+            m = int(np.where(members == r)[0][0])
+            j0 = (m // per) * per
+            s_ = min(per, members.size - j0)
+            p = m - j0
+            first = j0 * n0 * hq
+            for i in range(n0):
+                idx = [first + i * s_ * hq + (h // g) * s_ * g + p * g + h % g for h in range(hq)]
+                gv.append(v0[idx])
+                gl.append(l0[idx])
+        for n in range(o1[r], o1[r + 1]):
+            gv.append(v1[n])
+            gl.append(l1[n])
+        oi.append(len(gv))
+    rv, rl = orc.merge(np.array(gv, np.float64), np.array(gl, np.float64), oi)
+    dev = torch.device("cuda")
+    out = torch.empty((batch, hq, d), dtype=torch.float32, device=dev)
+    lo = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    B.paged_cascade_merge_states(torch.from_numpy(v0).to(dev), torch.from_numpy(l0).to(dev), n0,
+                                 torch.from_numpy(desc).to(dev), torch.from_numpy(v1).to(dev),
+                                 torch.from_numpy(l1).to(dev), torch.from_numpy(o1).to(dev),
+                                 batch, hq, hkv, d, out, lo)
+    torch.cuda.synchronize()
+    check_close(out.cpu().numpy(), lo.cpu().numpy(), rv, rl, workloads.FP32,
+                "cascade merge d=%d" % d)
+    assert np.all(out[1].cpu().numpy() == 0) and np.all(np.isneginf(lo[1].cpu().numpy()))
+
+
+def test_cascade_merge_states_rejects_bad_arguments():
+    dev = torch.device("cuda")
+    v = torch.zeros((4, 8, 80), dtype=torch.float32, device=dev)
+    lse = torch.zeros((4, 8), dtype=torch.float32, device=dev)
+    desc = torch.tensor([[0, 0, -1]] * 2, dtype=torch.int32, device=dev)
+    oi = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
+    out = torch.zeros((2, 8, 80), dtype=torch.float32, device=dev)
+    lo = torch.zeros((2, 8), dtype=torch.float32, device=dev)
+    with pytest.raises(B.PagedDecodeError) as e:      # 80 is not a multiple of 32
+        B.paged_cascade_merge_states(v, lse, 1, desc, v, lse, oi, 2, 8, 2, 80, out, lo)
+    assert e.value.name == "PD_E_UNSUPPORTED"
+    with pytest.raises(B.PagedDecodeError) as e:      # 8 query heads over 3 KV heads
+        B.paged_cascade_merge_states(v, lse, 1, desc, v, lse, oi, 2, 8, 3, 64, out, lo)
+    assert e.value.name == "PD_E_ARG"
 
 
 def test_cascade_without_sharing_is_flat(orc):
