@@ -241,9 +241,12 @@ class CascadeDecode:
             pos += sub.size
         rows = int(oi[-1])
         self.q0 = [None] * len(self.subgroups)
-        self.v_cat = torch.empty((rows, num_qo_heads, head_dim), dtype=torch.float32,
-                                 device=self.device)
-        self.lse_cat = torch.empty((rows, num_qo_heads), dtype=torch.float32, device=self.device)
+        self.v_cat = self.lse_cat = None            # the gathered merge input
+        if self.rows0 is None:
+            self.v_cat = torch.empty((rows, num_qo_heads, head_dim), dtype=torch.float32,
+                                     device=self.device)
+            self.lse_cat = torch.empty((rows, num_qo_heads), dtype=torch.float32,
+                                       device=self.device)
         self.out = torch.empty((self.batch, num_qo_heads, head_dim), dtype=torch.float32,
                                device=self.device)
         self.lse = torch.empty((self.batch, num_qo_heads), dtype=torch.float32,

@@ -578,8 +578,8 @@ def test_cascade_member_major_stacking_is_wrong(orc):
     """Negative control: stacking heads member-major (a plain reshape) launches
     fine and reads the wrong KV heads, so it must not match."""
     w = workloads.cascade_fp16(seed=6, prefix_tokens=1024, suffix_lo=64, suffix_hi=128)
-    cas = _cascade(w)
-    assert cas.active and len(cas.subgroups) == 1
+    cas = _cascade(w, merge_in_place=False)
+    assert cas.active and len(cas.subgroups) == 1 and cas.v_cat is not None
     q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
     good, _ = cas.run(q, k, v, w.sm_scale)
     good = good.cpu().numpy().copy()
