@@ -11,6 +11,7 @@ and -inf LSEs (empty chunks, empty requests) must match exactly.
 Unused pool rows are NaN in the random cases, so a read outside the page
 table shows up as NaN.
 """
+import dataclasses
 import os
 import sys
 
@@ -561,6 +562,25 @@ def test_cascade_merge_states_rejects_bad_arguments():
     with pytest.raises(B.PagedDecodeError) as e:      # 8 query heads over 3 KV heads
         B.paged_cascade_merge_states(v, lse, 1, desc, v, lse, oi, 2, 8, 3, 64, out, lo)
     assert e.value.name == "PD_E_ARG"
+
+
+def test_cascade_fp32_pools(orc):
+    """The cascade on fp32 pools (head dim 64; the stacked level 0 splits into
+    launches the fp32 kernels support), merged in place, against the oracle
+    at the fp32 tolerance."""
+    w16 = workloads.cascade_fp16(seed=12, members=3, prefix_tokens=1024, suffix_lo=40,
+                                 suffix_hi=300, hq=8, hkv=2, d=64, poison_unused=True)
+    w = dataclasses.replace(w16, dtype=workloads.FP32, q=w16.q.astype(np.float32),
+                            k_pool=w16.k_pool.astype(np.float32),
+                            v_pool=w16.v_pool.astype(np.float32))
+    cas = _cascade(w, dtype=torch.float32)
+    say("case cascade fp32 plan=%s" % cas.plan_summary())
+    assert cas.active and cas.rows0 is not None
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    out, lse = cas.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ref_v, ref_l = _oracle_flat(orc, w)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "fp32 cascade")
 
 
 def test_cascade_without_sharing_is_flat(orc):
