@@ -164,8 +164,8 @@ class CascadeDecode:
     def __init__(self, csr: dict, *, page_size: int, num_pool_pages: int, num_qo_heads: int,
                  num_kv_heads: int, head_dim: int, members=None, shared_pages: int = 0,
                  min_shared_pages: int = 16, min_members: int = 2, target_wgs: int = 0,
-                 target_wgs_level0: int = 0, merge_in_place: bool = True,
-                 dtype=torch.float16, device="cuda"):
+                 target_wgs_level0: int = 0, min_level0_tokens: int = 64,
+                 merge_in_place: bool = True, dtype=torch.float16, device="cuda"):
         indptr = np.asarray(csr["indptr"], np.int32)
         indices = np.asarray(csr["indices"], np.int32)
         lpl = np.asarray(csr["last_page_len"], np.int32)
@@ -202,10 +202,24 @@ class CascadeDecode:
         self.subgroups = [self.member_req[i:i + per] for i in range(0, self.member_req.size, per)]
         self.level0 = []
         fixed = 0
+        # Level 0's chunks hold at least min_level0_tokens tokens unless its
+        # target is given: a stacked chunk writes M*G partial rows per KV head,
+        # so the occupancy plan's smallest chunks (2 pages of 16 at 8K shared
+        # tokens) write half as many bytes as they read.  Measured on MI355X
+        # (graph-replayed steps): 4-page chunks took 4 x 8K from 34.4 to 33.4 us
+        # and 16 x 8K from 68.8 to 67.0 us; from 32K shared tokens on the plan's
+        # chunks are larger anyway.
+        floor = 0 if target_wgs_level0 else min(self.shared_pages,
+                                                  -(-min_level0_tokens // page_size))
         for sub in self.subgroups:
             lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads,
                              target_wgs=target_wgs_level0 or target_wgs,
                              fixed_pages_per_chunk=fixed, **kw)
+            if not fixed and lv.info.pages_per_chunk < floor:
+                fixed = floor
+                lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads,
+                                 target_wgs=target_wgs_level0 or target_wgs,
+                                 fixed_pages_per_chunk=fixed, **kw)
             fixed = fixed or lv.info.pages_per_chunk      # one level-0 chunking for all
             self.level0.append(lv)
         self.level1 = PagedDecode(csr1, num_qo_heads=num_qo_heads, target_wgs=target_wgs, **kw)
