@@ -181,8 +181,11 @@ int paged_decode_plan(int32_t batch, const int32_t *indptr,
  * multiples of 16 bytes.  indices/indptr/last_page_len/first_page_offset
  * are the (validated) CSR; request_indices/kv_tile_indices the plan's.
  * Outputs: v_partial [num_chunks, Hq, D] fp32 and lse_partial [num_chunks,
- * Hq] fp32.  Supported: D in {64, 128}; G in {1, 2, 4, 8, 12, 16}; other
- * shapes return PD_E_UNSUPPORTED before any launch.
+ * Hq] fp32.  Supported: D in {64, 128} with G in {1, 2, 4, 8, 12, 16};
+ * and G in {24, 32} for fp16, D = 128 and a page size that is a power-of-two
+ * multiple of 16 (the MFMA kernel; paged_decode_kernel_kind() tells which
+ * kernel serves a shape).  Other shapes return PD_E_UNSUPPORTED before any
+ * launch.
  * ---------------------------------------------------------------------- */
 int paged_decode_partial(const void *q, const void *k_pool, const void *v_pool,
                          int64_t page_stride, int64_t token_stride, int64_t head_stride,
@@ -450,15 +453,24 @@ int paged_decode_q_heads_per_wg(int32_t group_size, int32_t head_dim, int32_t dt
 int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t head_dim,
                                     int32_t dtype, int32_t num_kv_heads);
 
-/* Which partial kernel serves a shape: 1 = page kernel (256-byte K/V rows,
- * group 4, 8 or 16, page_size a power-of-two multiple of 64/group slots),
- * 0 = token kernel (every other supported shape), negative = unsupported. */
+/* Which partial kernel paged_decode_partial launches for a shape:
+ * 2 = MFMA kernel (fp16, head_dim 128, group 8, 12, 16, 24 or 32, page_size a
+ *     power-of-two multiple of 16);
+ * 1 = page kernel (256-byte K/V rows, group 4, 8 or 16, page_size a
+ *     power-of-two multiple of the 64/group slots of one step), for the
+ *     shapes the MFMA kernel does not take;
+ * 0 = token kernel (every other supported shape);
+ * negative = unsupported (PD_E_UNSUPPORTED).
+ * The answer follows paged_decode_set_kernel_choice().  Host only: no device
+ * is touched. */
 int paged_decode_kernel_kind(int32_t dtype, int32_t head_dim, int32_t group_size,
                              int32_t page_size, int64_t token_stride);
 
-/* Testing hook: nonzero routes every later launch in this process to the
- * token kernel (so both kernels can be checked on the same shapes); 0
- * restores the normal choice.  Not thread-safe with concurrent launches. */
+/* Testing hook: 1 routes every later launch in this process to the token
+ * kernel, 2 keeps every launch off the MFMA kernel (page or token kernel),
+ * 0 restores the normal choice; so every kernel can be checked on the same
+ * shapes.  Other values return PD_E_ARG.  Not thread-safe with concurrent
+ * launches. */
 int paged_decode_set_kernel_choice(int32_t force_token_kernel);
 
 /* Host evaluation of the kernels' invariant-integer division by d

@@ -78,6 +78,13 @@ union Row16 {
     float f[4];
 };
 
+// Waits until every vector memory operation this thread issued, stores
+// included, has completed (on gfx9 stores are counted by vmcnt).
+__device__ __forceinline__ void wait_stores()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 struct PartialArgs {
     const void *q;
     const void *k;
@@ -343,20 +350,23 @@ __device__ __forceinline__ void epilogue(const PartialArgs &a, EpilogueSmem<G, D
     }
     if constexpr (FUSED) {
         if (direct) return;
-        // Every wave waits for its coherent stores to complete (a workgroup
-        // fence is a plain vmcnt wait here, not a cache writeback), then one
-        // thread counts the chunk.  The workgroup that brings the count to
-        // ntiles merges rows n - t .. n - t + ntiles - 1, reading them with
-        // coherent loads, and resets the counter for the next launch.
+        // Every thread waits until its own coherent stores have completed
+        // (vmcnt counts stores on gfx9), then the barrier, then one thread
+        // counts the chunk.  A workgroup-scope fence would not do: on gfx950
+        // it emits no vmcnt wait, so another wave's rows could still be in
+        // flight when the count is added.  The workgroup that brings the
+        // count to ntiles merges rows n - t .. n - t + ntiles - 1, reading
+        // them with coherent loads, and resets the counter for the next
+        // launch.
         //
         // Ordering: the rows and LSEs are written and read only with
-        // agent-scope atomics, so no cache holds a stale copy; the writers'
-        // stores have completed before their count is added, and the
+        // agent-scope atomics, so no cache holds a stale copy; every
+        // writer's stores have completed before the count is added, and the
         // merging workgroup's loads are issued after (and only because of)
         // the count it read.  The counter therefore needs no acquire or
         // release of its own, which on gfx950 would write back and
         // invalidate the whole L2 of the XCD.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        wait_stores();
         __syncthreads();
         int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvh;
         if (tid == 0) {
@@ -725,13 +735,12 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
 
     if constexpr (FUSED) {
         if (direct) return;
-        // Every wave waits for its coherent stores to complete (a workgroup
-        // fence is a plain vmcnt wait here, not a cache writeback), then one
-        // thread counts the chunk.  The workgroup that brings the count to
-        // ntiles merges rows n - t .. n - t + ntiles - 1 for its heads,
-        // reading them with coherent loads, and resets the counter.  (The
-        // ordering argument is the one in epilogue(), above.)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        // Every thread waits until its own coherent stores have completed,
+        // then one thread counts the chunk.  The workgroup that brings the
+        // count to ntiles merges rows n - t .. n - t + ntiles - 1 for its
+        // heads, reading them with coherent loads, and resets the counter.
+        // (The ordering argument is the one in epilogue(), above.)
+        wait_stores();
         __syncthreads();
         int32_t *ctr = a.counters + int64_t(r) * a.num_kv_heads + kvg;
         if (tid == 0) {

@@ -142,6 +142,36 @@ class PagedDecode:
         return self.out, self.lse
 
 
+def cascade_members_per_launch(members: int, group_size: int, head_dim: int, pd_dtype: int,
+                               page_size: int, token_stride: int) -> int:
+    """Members stacked per level-0 launch of a cascade step.  Launches stack
+    `per` members each in member order and the last one the rest, so both
+    per * G and the remainder's stacked group must have a partial kernel
+    (for this dtype, head dim and page size).  Among the sizes that satisfy
+    that, the one with the fewest launches wins (each launch reads the shared
+    span once), then the one whose last launch stacks the most members.  A
+    single member is always a supported launch (its group is the flat
+    decode's), so some size always qualifies."""
+    lib = B.load()
+
+    def ok(k):
+        return k == 0 or lib.paged_decode_kernel_kind(pd_dtype, head_dim, k * group_size,
+                                                      page_size, token_stride) >= 0
+
+    if not ok(1):
+        raise ValueError("no partial kernel for group size %d, head_dim %d"
+                         % (group_size, head_dim))
+    best = None
+    for per in range(1, members + 1):
+        launches = -(-members // per)
+        last = members - (launches - 1) * per
+        if ok(per) and ok(last):
+            key = (launches, -last)
+            if best is None or key < best[0]:
+                best = (key, per)
+    return best[1]
+
+
 class CascadeDecode:
     """Cascade decode of one batch (cascade-attention doc).
 
@@ -179,6 +209,7 @@ class CascadeDecode:
                                                            min_shared_pages, min_members)
         self.member_req = np.asarray(members, np.int32)
         self.shared_pages = int(shared_pages)
+        self.dtype = dtype
         self.device = torch.device(device)
         kw = dict(page_size=page_size, num_pool_pages=num_pool_pages, num_kv_heads=num_kv_heads,
                   head_dim=head_dim, dtype=dtype, device=device)
@@ -195,20 +226,19 @@ class CascadeDecode:
         # subgroups of members whose stacked group size a launch supports
         g = num_qo_heads // num_kv_heads
         pd_dtype = B.PD_DTYPE_FP32 if dtype == torch.float32 else B.PD_DTYPE_FP16
-        per = 1
-        for k in range(1, self.member_req.size + 1):
-            if B.load().paged_decode_q_heads_per_wg(k * g, head_dim, pd_dtype) > 0:
-                per = k
+        per = cascade_members_per_launch(self.member_req.size, g, head_dim, pd_dtype, page_size,
+                                         num_kv_heads * head_dim)
         self.subgroups = [self.member_req[i:i + per] for i in range(0, self.member_req.size, per)]
         self.level0 = []
         fixed = 0
-        # Level 0's chunks hold at least min_level0_tokens tokens unless its
-        # target is given: a stacked chunk writes M*G partial rows per KV head,
-        # so the occupancy plan's smallest chunks (2 pages of 16 at 8K shared
-        # tokens) write half as many bytes as they read.  Measured on MI355X
-        # (graph-replayed steps): 4-page chunks took 4 x 8K from 34.4 to 33.4 us
-        # and 16 x 8K from 68.8 to 67.0 us; from 32K shared tokens on the plan's
-        # chunks are larger anyway.
+        # Level 0's chunks hold at least min_level0_tokens tokens unless a
+        # level-0 target (target_wgs_level0) is given; a target_wgs given for
+        # the whole step still gets the floor.  A stacked chunk writes M*G
+        # partial rows per KV head, so the occupancy plan's smallest chunks
+        # (2 pages of 16 at 8K shared tokens) write half as many bytes as they
+        # read.  Measured on MI355X (graph-replayed steps): 4-page chunks took
+        # 4 x 8K from 34.4 to 33.4 us and 16 x 8K from 68.8 to 67.0 us; from
+        # 32K shared tokens on the plan's chunks are larger anyway.
         floor = 0 if target_wgs_level0 else min(self.shared_pages,
                                                   -(-min_level0_tokens // page_size))
         for sub in self.subgroups:
@@ -282,6 +312,12 @@ class CascadeDecode:
         if self.flat is not None:
             return self.flat.run(q, k_pool, v_pool, sm_scale, stream)
         hq, d, hkv = self.num_qo_heads, self.head_dim, self.num_kv_heads
+        if q.shape != (self.batch, hq, d) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, D] tensor")
+        if q.dtype != self.dtype or k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+            raise TypeError("q and pools must share the dtype the cascade was planned for")
+        if not (q.is_cuda and k_pool.is_cuda and v_pool.is_cuda):
+            raise ValueError("q and pools must be device tensors")
         for j, sub in enumerate(self.subgroups):
             if self.q0[j] is None or self.q0[j].dtype != q.dtype:
                 self.q0[j] = torch.empty((1, sub.size * hq, d), dtype=q.dtype, device=q.device)

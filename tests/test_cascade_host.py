@@ -207,3 +207,33 @@ def test_merge_layout_rejects_bad_members():
     with pytest.raises(B.PagedDecodeError) as e:
         B.paged_cascade_merge_layout(4, [0, 1], 2, 1 << 20, 1 << 12)   # rows past int32
     assert e.value.name == "PD_E_ARG"
+
+
+@pytest.mark.parametrize("dtype,head_dim,g", [
+    (B.PD_DTYPE_FP16, 128, 1), (B.PD_DTYPE_FP16, 128, 2), (B.PD_DTYPE_FP16, 128, 4),
+    (B.PD_DTYPE_FP16, 128, 8), (B.PD_DTYPE_FP16, 128, 12), (B.PD_DTYPE_FP16, 128, 16),
+    (B.PD_DTYPE_FP16, 64, 2), (B.PD_DTYPE_FP16, 64, 4), (B.PD_DTYPE_FP32, 128, 4),
+    (B.PD_DTYPE_FP32, 64, 4), (B.PD_DTYPE_FP32, 64, 8)])
+def test_cascade_subgroup_sizes_all_have_a_kernel(dtype, head_dim, g):
+    """Every level-0 launch of a cascade step (per members stacked, the last
+    launch the rest) has a partial kernel, for 2 to 32 members and page sizes
+    1, 8, 16 and 64; and no other launch size needs fewer launches.  Before
+    the remainder was checked, 13 members at G = 4 left a 5-member launch
+    (stacked G = 20), which no kernel serves."""
+    from paged_attention_decode_amd.decode import cascade_members_per_launch
+    lib = B.load()
+    kv_heads = 8
+
+    def ok(k, ps):
+        return lib.paged_decode_kernel_kind(dtype, head_dim, k * g, ps, kv_heads * head_dim) >= 0
+
+    for ps in (1, 8, 16, 64):
+        for m in range(2, 33):
+            per = cascade_members_per_launch(m, g, head_dim, dtype, ps, kv_heads * head_dim)
+            sizes = [min(per, m - i) for i in range(0, m, per)]
+            assert sum(sizes) == m
+            assert all(ok(s, ps) for s in sizes), (ps, m, per, sizes)
+            for other in range(1, m + 1):
+                n = -(-m // other)
+                if ok(other, ps) and ok(m - (n - 1) * other, ps):
+                    assert n >= len(sizes), (ps, m, per, other)
