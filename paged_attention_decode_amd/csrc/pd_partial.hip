@@ -943,7 +943,11 @@ constexpr int token_rows_per_step()
 // queries is S^T [16 tokens x 16 heads] = K [16 x 128] . Q^T [128 x 16]:
 // four v_mfma_f32_16x16x32_f16.  The value sum is taken transposed,
 // O^T [16 dims x 16 heads] += V^T [16 dims x 16 tokens] . P^T [16 tokens x
-// 16 heads]: one v_mfma_f32_16x16x16_f16 per 16 dims.
+// 16 heads]: one v_mfma_f32_16x16x32_f16 per 16 dims, whose K = 32 holds
+// each token twice -- once with p rounded to fp16, once with the rounding's
+// remainder -- so that P enters the product with about 22 bits, not fp16's
+// 11 (the softmax weights stay fp32 arithmetic, as the fp16 path's
+// products and sums are).
 //
 // Lane layouts of the 16x16xK products (checked on gfx950): A [M x K] --
 // lane l holds row l%16, k = (K/4)*(l/16) + e; B [K x N] -- lane l holds
@@ -1135,19 +1139,30 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) acc[ht][dt] *= alpha;
                 }
-                half4_t pb;
+                // P^T in two fp16 parts: k = 8*(l/16) + e holds, for token
+                // 4*(l/16) + e%4, p rounded to fp16 (e < 4) or the remainder
+                // p - that, rounded to fp16 (e >= 4); the A operand repeats
+                // the token's V^T for both.  The product then carries p to
+                // about 22 bits, the sum takes p itself, and the K = 32 product
+                // takes as long as the K = 16 one it replaces.
+                half8_t pb;
                 float ls = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const _Float16 ph = _Float16(fast_exp2(x[i] - m_run[ht]));
+                    const float p = fast_exp2(x[i] - m_run[ht]);
+                    const _Float16 ph = _Float16(p);
                     pb[i] = ph;
-                    ls += float(ph);        // the sum takes the weights the products use
+                    pb[4 + i] = _Float16(p - float(ph));
+                    ls += p;
                 }
                 l_part[ht] += ls;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-                    acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vtr[dt], pb, acc[ht][dt],
-                                                                        0, 0, 0);
+                for (int dt = 0; dt < 8; ++dt) {
+                    const half8_t va = __builtin_shufflevector(vtr[dt], vtr[dt], 0, 1, 2, 3, 0, 1,
+                                                               2, 3);
+                    acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ht][dt], 0,
+                                                                         0, 0);
+                }
             }
         };
 
