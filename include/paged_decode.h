@@ -228,6 +228,34 @@ int paged_decode_fused(const void *q, const void *k_pool, const void *v_pool,
                        float *out, float *lse_out, void *stream);
 
 /* ------------------------------------------------------------------------
+ * paged_decode_fused_noalloc -- paged_decode_fused for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, semantics and outputs as paged_decode_fused, without the
+ * v_partial, lse_partial and counters buffers: the library keeps that
+ * workspace in a file-scope device array of 16 MiB (one copy per GPU, held
+ * until the process ends).  The call allocates nothing and frees nothing.
+ * The workspace needs N*Hq*D*4 + N*Hq*4 + B*Hkv*4 bytes (each part rounded
+ * up to 256); a plan that needs more returns PD_E_CAPACITY before any launch
+ * (use paged_decode_fused with caller-owned buffers then).  Each call first
+ * zeroes the counters on the caller's stream with a small kernel, so it does
+ * not depend on what an earlier call left.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (two streams, two threads)
+ * race and give wrong results; calls on one stream are ordered and safe.
+ * ---------------------------------------------------------------------- */
+int paged_decode_fused_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                               int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                               int32_t dtype,
+                               const int32_t *indices, const int32_t *indptr,
+                               const int32_t *last_page_len, const int32_t *first_page_offset,
+                               const int32_t *request_indices, const int32_t *kv_tile_indices,
+                               int32_t num_chunks, int32_t pages_per_chunk, int32_t batch,
+                               int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, float sm_scale, float *out, float *lse_out,
+                               void *stream);
+
+/* ------------------------------------------------------------------------
  * paged_merge_states -- PR #984 body item 3; issue #898 item 3;
  * cascade-attention doc "Softmax states compose".
  *

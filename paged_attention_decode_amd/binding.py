@@ -30,7 +30,7 @@ CODES = {v: k for k, v in ERRORS.items()}
 
 EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_decode_plan", "paged_decode_partial", "paged_decode_fused",
-            "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
+            "paged_decode_fused_noalloc", "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
             "paged_cascade_detect", "paged_cascade_split", "paged_cascade_layout",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
             "paged_cascade_merge_layout", "paged_cascade_merge_states",
@@ -71,6 +71,9 @@ _SIGS = {
     "paged_decode_fused": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp,
                                  i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                  vp]),
+    "paged_decode_fused_noalloc": (i32, [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp,
+                                         vp, i32, i32, i32, i32, i32, i32, i32, f32, vp, vp,
+                                         vp]),
     "paged_merge_states": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, vp]),
     "paged_mla_decode_partial": (i32, [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp,
                                        vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp,
@@ -259,6 +262,20 @@ def paged_decode_fused(q, k_pool, v_pool, page_stride, token_stride, head_stride
         _dev(request_indices), _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch,
         num_qo_heads, num_kv_heads, head_dim, page_size, float(sm_scale), _dev(v_partial),
         _dev(lse_partial), _dev(counters), _dev(out), _dev(lse_out), _stream(stream)))
+
+
+def paged_decode_fused_noalloc(q, k_pool, v_pool, page_stride, token_stride, head_stride,
+                               dtype, indices, indptr, last_page_len, first_page_offset,
+                               request_indices, kv_tile_indices, num_chunks, pages_per_chunk,
+                               batch, num_qo_heads, num_kv_heads, head_dim, page_size, sm_scale,
+                               out, lse_out, stream=None):
+    lib = load()
+    _check(lib.paged_decode_fused_noalloc(
+        _dev(q), _dev(k_pool), _dev(v_pool), page_stride, token_stride, head_stride, dtype,
+        _dev(indices), _dev(indptr), _dev(last_page_len), _dev(first_page_offset),
+        _dev(request_indices), _dev(kv_tile_indices), num_chunks, pages_per_chunk, batch,
+        num_qo_heads, num_kv_heads, head_dim, page_size, float(sm_scale), _dev(out),
+        _dev(lse_out), _stream(stream)))
 
 
 def paged_decode_kernel_kind(dtype, head_dim, group_size, page_size, token_stride):

@@ -48,6 +48,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pd_device.h"
 #include "pd_internal.h"
@@ -1485,6 +1486,112 @@ extern "C" int paged_decode_fused(const void *q, const void *k_pool, const void 
     const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
                           true, !g_force_token_kernel, num_kv_heads);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_fused: no kernel for this (dtype, D, group)");
+    a.o_final = out;
+    a.lse_final = lse_out;
+    a.counters = counters;
+    return launch(c, a, num_chunks, stream, who);
+}
+
+// ------------------------------------------------------ no-allocation entry
+// paged_decode_fused_noalloc keeps the fused launch's workspace -- the
+// partial rows, their LSEs and the arrival counters -- in this array instead
+// of caller-owned buffers.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` only names the symbol:
+// kernels get the device address that hipGetSymbolAddress returns for the
+// current device.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace pd {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_base(char **base, const char *who)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(PD_E_HIP, std::string(who) + ": no current device");
+    if (dev >= kMaxDevices)
+        return fail(PD_E_UNSUPPORTED, std::string(who) + ": device index beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(PD_E_HIP, std::string(who) + ": cannot resolve the scratch array: " +
+                                      hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<char *>(ptr);
+    }
+    *base = g_scratch_ptr[dev];
+    return PD_OK;
+}
+
+__global__ void __launch_bounds__(256) zero_i32_kernel(int32_t *p, int32_t n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+int64_t round_up256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+}  // namespace
+}  // namespace pd
+
+extern "C" int paged_decode_fused_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                          int64_t page_stride, int64_t token_stride,
+                                          int64_t head_stride, int32_t dtype,
+                                          const int32_t *indices, const int32_t *indptr,
+                                          const int32_t *last_page_len,
+                                          const int32_t *first_page_offset,
+                                          const int32_t *request_indices,
+                                          const int32_t *kv_tile_indices, int32_t num_chunks,
+                                          int32_t pages_per_chunk, int32_t batch,
+                                          int32_t num_qo_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t page_size, float sm_scale,
+                                          float *out, float *lse_out, void *stream)
+{
+    const char *who = "paged_decode_fused_noalloc";
+    if (num_chunks < 0 || batch < 1 || num_qo_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+        return fail(PD_E_ARG, std::string(who) + ": bad sizes");
+    // workspace layout in the scratch array: partial rows [N, Hq, D], their
+    // LSEs [N, Hq], counters [B, Hkv], each at a 256-byte boundary
+    const int64_t lse_off = round_up256(int64_t(num_chunks) * num_qo_heads * head_dim * 4);
+    const int64_t ctr_off = round_up256(lse_off + int64_t(num_chunks) * num_qo_heads * 4);
+    const int64_t need = ctr_off + int64_t(batch) * num_kv_heads * 4;
+    if (need > kScratchBytes)
+        return fail(PD_E_CAPACITY,
+                    std::string(who) + ": the workspace needs " + std::to_string(need) +
+                        " bytes, more than the library's " + std::to_string(kScratchBytes) +
+                        "-byte scratch array (use paged_decode_fused with caller-owned buffers)");
+    char *base = nullptr;
+    int rc = scratch_base(&base, who);
+    if (rc) return rc;
+    float *v_partial = reinterpret_cast<float *>(base);
+    float *lse_partial = reinterpret_cast<float *>(base + lse_off);
+    int32_t *counters = reinterpret_cast<int32_t *>(base + ctr_off);
+    PartialArgs a;
+    rc = check_and_fill(a, q, k_pool, v_pool, page_stride, token_stride, head_stride, dtype,
+                        indices, indptr, last_page_len, first_page_offset, request_indices,
+                        kv_tile_indices, num_chunks, pages_per_chunk, batch, num_qo_heads,
+                        num_kv_heads, head_dim, page_size, sm_scale, v_partial, lse_partial, who);
+    if (rc) return rc;
+    if (!out || !lse_out) return fail(PD_E_NULL, std::string(who) + ": null pointer");
+    if (num_chunks < batch) return fail(PD_E_ARG, std::string(who) + ": fewer chunks than requests");
+    const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
+                          true, !g_force_token_kernel, num_kv_heads);
+    if (!c.fn) return fail(PD_E_UNSUPPORTED, std::string(who) + ": no kernel for this (dtype, D, group)");
+    // the counters start at zero on every call, whatever an earlier call left
+    // (a fill kernel, not a memset: the call may be captured in a HIP graph)
+    const int32_t nctr = batch * num_kv_heads;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(uint32_t((nctr + 255) / 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), counters, nctr);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(PD_E_HIP, std::string(who) + ": launch failed: " + hipGetErrorString(err));
     a.o_final = out;
     a.lse_final = lse_out;
     a.counters = counters;

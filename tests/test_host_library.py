@@ -266,3 +266,17 @@ def test_kernel_wrappers_refuse_host_tensors():
     oi = torch.zeros(2, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU tensors"):
         B.paged_merge_states(v, lse, oi, 1, 1, 4, v[:1], lse[:1], stream=0)
+
+
+def test_fused_noalloc_refuses_before_touching_the_device(lib):
+    """Size errors of the no-allocation entry point come back before any
+    device call: a workspace larger than the library's 16 MiB array is
+    PD_E_CAPACITY, bad sizes PD_E_ARG."""
+    f = lib.paged_decode_fused_noalloc
+    args = [None] * 3 + [0, 0, 0, 0] + [None] * 6
+    tail = [None, None, None]
+    # 4096 chunks x 32 heads x 128 dims x 4 B = 64 MiB of partial rows
+    rc = f(*args, 4096, 1, 4, 32, 8, 128, 16, 0.1, *tail)
+    assert rc == -8 and b"scratch" in lib.pd_last_error()
+    rc = f(*args, 4096, 1, 0, 32, 8, 128, 16, 0.1, *tail)
+    assert rc == -2
