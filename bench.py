@@ -89,6 +89,16 @@ def parse():
                    help="cascade workload: requests sharing the prefix")
     p.add_argument("--cascade-prefix", type=int, default=8192,
                    help="cascade workload: shared prefix tokens")
+    p.add_argument("--cascade-separate", action="store_true",
+                   help="cascade workload: launch the shared and the per-request level "
+                        "separately instead of as one grid")
+    p.add_argument("--cascade-hpw", type=int, default=0,
+                   help="cascade workload: KV heads per workgroup of the one-grid launch "
+                        "(0: automatic)")
+    p.add_argument("--cascade-l0-pages", type=int, default=0,
+                   help="cascade workload: pages per chunk of the shared level (0: plan)")
+    p.add_argument("--cascade-l1-pages", type=int, default=0,
+                   help="cascade workload: pages per chunk of the per-request level (0: plan)")
     p.add_argument("--group-size", type=int, default=4,
                    help="long_context_fp16: query heads per KV head (8 KV heads; the metric "
                         "config is 4)")
@@ -146,7 +156,11 @@ def main():
         # detection over the page table picks the members and the shared span
         runner = PD.CascadeDecode(csr, page_size=w.page_size, num_pool_pages=pool_pages,
                                   num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
-                                  head_dim=w.head_dim, target_wgs=args.target_wgs, device=dev)
+                                  head_dim=w.head_dim, target_wgs=args.target_wgs,
+                                  pair_launch=not args.cascade_separate,
+                                  heads_per_workgroup=args.cascade_hpw,
+                                  fixed_pages_level0=args.cascade_l0_pages,
+                                  fixed_pages_level1=args.cascade_l1_pages, device=dev)
         plan = runner.plan_summary()
         partial_only = None
         row_bytes = w.num_kv_heads * w.head_dim * 2 * 2

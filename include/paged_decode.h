@@ -349,6 +349,54 @@ int paged_merge_states(const float *v_in, const float *lse_in, const int32_t *o_
  *   head_dim % 32 == 0 and 16-byte aligned V buffers, else
  *   PD_E_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
+/* ------------------------------------------------------------------------
+ * paged_cascade_partial -- the cascade step's partial work (cascade-attention
+ * doc, head stacking; the partial itself is paged_decode_partial's).
+ *
+ * Level 0 attends the shared span once for all `members` requests with
+ * their query heads stacked, in L = ceil(members / members_per_launch)
+ * tables: table j stacks members [j*per, min(members, (j+1)*per)) (per =
+ * members_per_launch; S_j of them), and its stacked head h0 = kv*(S_j*G) +
+ * m*G + g is query head kv*G + g of request member_req[j*per + m], read
+ * straight from q [batch, Hq, D] (no stacked copy of q is made).  Table j's
+ * rows are [level0[j].num_chunks, S_j*Hq, D], exactly what
+ * paged_decode_partial would write for those stacked queries.  Level 1
+ * (nullable) is the per-request level: every request's own pages, queries q
+ * as they are, rows [level1->num_chunks, Hq, D].  Each table brings its
+ * validated page table and its plan (paged_decode_plan with num_qo_heads =
+ * S_j*Hq for level 0).  When every stacked group runs on the MFMA kernel
+ * (fp16, head_dim 128, S_j*G in {8, 12, 16, 24, 32}, page_size a
+ * power-of-two multiple of 16) and G <= 16, all tables run in one grid
+ * (up to 8 tables per launch), workgroups [W_{i-1}, W_i) on table i, so
+ * that no level's grid has to fill the GPU alone; otherwise each table is
+ * one launch of the kernel paged_decode_partial would pick.
+ * heads_per_workgroup: KV heads per workgroup of the one-grid form (1, 2, 4
+ * or 8 dividing num_kv_heads), or 0 for two (one if num_kv_heads is odd):
+ * the shared level has few chunks, and narrow workgroups spread it over
+ * more CUs.
+ * DEVICE: q, pools (strides, dtype and alignment as paged_decode_partial),
+ * member_req [members] (requests in [0, batch)), and every pointer inside
+ * the level structs.  HOST: the structs themselves (level0 is an array of
+ * L), read before the call returns.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    const int32_t *indices, *indptr, *last_page_len, *first_page_offset;
+    const int32_t *request_indices, *kv_tile_indices;
+    int32_t batch;            /* requests of this table's page table */
+    int32_t num_chunks, pages_per_chunk;
+    float *v_partial;         /* [num_chunks, heads, D] fp32 */
+    float *lse_partial;       /* [num_chunks, heads] fp32, log2 */
+} paged_cascade_level;
+
+int paged_cascade_partial(const void *q, int32_t batch, const int32_t *member_req,
+                          int32_t members, int32_t members_per_launch, const void *k_pool,
+                          const void *v_pool, int64_t page_stride, int64_t token_stride,
+                          int64_t head_stride, int32_t dtype, int32_t num_qo_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                          float sm_scale, const paged_cascade_level *level0,
+                          const paged_cascade_level *level1, int32_t heads_per_workgroup,
+                          void *stream);
+
 int paged_cascade_detect(int32_t batch, const int32_t *indptr, const int32_t *indices,
                          const int32_t *first_page_offset, int32_t min_shared_pages,
                          int32_t min_members, int32_t *member_req, int32_t *num_members,

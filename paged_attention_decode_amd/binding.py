@@ -32,6 +32,7 @@ EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_decode_plan", "paged_decode_partial", "paged_decode_fused",
             "paged_decode_fused_noalloc", "paged_merge_states", "paged_decode_kernel_kind", "paged_decode_set_kernel_choice",
             "paged_cascade_detect", "paged_cascade_split", "paged_cascade_layout",
+            "paged_cascade_partial",
             "paged_cascade_stack_q", "paged_cascade_gather_states",
             "paged_cascade_merge_layout", "paged_cascade_merge_states",
             "paged_sparse_csr", "paged_sparse_expand_blocks", "paged_mla_decode_partial",
@@ -51,6 +52,15 @@ class PlanInfo(ctypes.Structure):
                 ("num_wgs", ctypes.c_int32), ("q_groups", ctypes.c_int32),
                 ("needs_merge", ctypes.c_int32), ("target_wgs", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64)]
+
+
+class CascadeLevel(ctypes.Structure):
+    _fields_ = [("indices", ctypes.c_void_p), ("indptr", ctypes.c_void_p),
+                ("last_page_len", ctypes.c_void_p), ("first_page_offset", ctypes.c_void_p),
+                ("request_indices", ctypes.c_void_p), ("kv_tile_indices", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("pages_per_chunk", ctypes.c_int32), ("v_partial", ctypes.c_void_p),
+                ("lse_partial", ctypes.c_void_p)]
 
 
 i32p = ctypes.POINTER(ctypes.c_int32)
@@ -85,6 +95,9 @@ _SIGS = {
                                   i32p, i32p, i32p]),
     "paged_cascade_layout": (i32, [i32, i32p, i32, i32, i32p, i32p, i32p, i32p]),
     "paged_cascade_stack_q": (i32, [vp, i32, vp, i32, i32, i32, i32, vp, vp]),
+    "paged_cascade_partial": (i32, [vp, i32, vp, i32, i32, vp, vp, i64, i64, i64, i32, i32, i32,
+                                    i32, i32, f32, ctypes.POINTER(CascadeLevel),
+                                    ctypes.POINTER(CascadeLevel), i32, vp]),
     "paged_cascade_gather_states": (i32, [vp, vp, i32, i32, vp, vp, vp, i32, vp, i32, i32, i32,
                                           vp, vp, vp]),
     "paged_cascade_merge_layout": (i32, [i32, i32p, i32, i32, i32, i32, i32p]),
@@ -352,6 +365,33 @@ def paged_cascade_stack_q(q, dtype, member_req, members, num_qo_heads, num_kv_he
                           q0, stream=None):
     _check(load().paged_cascade_stack_q(_dev(q), dtype, _dev(member_req), members, num_qo_heads,
                                         num_kv_heads, head_dim, _dev(q0), _stream(stream)))
+
+
+def cascade_level(indices, indptr, last_page_len, first_page_offset, request_indices,
+                  kv_tile_indices, batch, num_chunks, pages_per_chunk, v_partial, lse_partial):
+    """A paged_cascade_level struct of device addresses (the tensors must
+    outlive every call that uses it)."""
+    return CascadeLevel(_dev(indices), _dev(indptr), _dev(last_page_len),
+                        _dev(first_page_offset), _dev(request_indices), _dev(kv_tile_indices),
+                        batch, num_chunks, pages_per_chunk, _dev(v_partial), _dev(lse_partial))
+
+
+def cascade_levels(levels):
+    """A ctypes array of paged_cascade_level structs (level 0's tables)."""
+    return (CascadeLevel * len(levels))(*levels)
+
+
+def paged_cascade_partial(q, batch, member_req, members, members_per_launch, k_pool, v_pool,
+                          page_stride, token_stride, head_stride, dtype, num_qo_heads,
+                          num_kv_heads, head_dim, page_size, sm_scale, level0, level1=None,
+                          heads_per_workgroup=0, stream=None):
+    """level0: the array from cascade_levels(); level1: a CascadeLevel or None."""
+    _check(load().paged_cascade_partial(
+        _dev(q), batch, _dev(member_req), members, members_per_launch, _dev(k_pool),
+        _dev(v_pool), page_stride, token_stride, head_stride, dtype, num_qo_heads, num_kv_heads,
+        head_dim, page_size, float(sm_scale), level0,
+        ctypes.byref(level1) if level1 is not None else None, int(heads_per_workgroup),
+        _stream(stream)))
 
 
 def paged_cascade_gather_states(v0, lse0, n0, members, dst0, v1, lse1, n1, dst1, num_qo_heads,

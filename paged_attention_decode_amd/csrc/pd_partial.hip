@@ -48,7 +48,9 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "pd_device.h"
 #include "pd_internal.h"
@@ -98,11 +100,31 @@ struct PartialArgs {
     float scale_log2;
     float *v_out;        // partial rows [N, Hq, D]
     float *lse_out;      // [N, Hq]
+    int32_t group;       // query heads per KV head of this launch (G = Hq / Hkv)
+    // stacked launches (the cascade's shared level): the queries are read
+    // where they lie in q [B, Hkv * q_group, D]; stacked head m*q_group + g
+    // of KV head kv is query head kv*q_group + g of request q_members[m].
+    // NULL: query head h of request r is row r*Hq + h.
+    const int32_t *q_members;
+    int32_t q_group;
     // fused mode
     float *o_final;      // [B, Hq, D]
     float *lse_final;    // [B, Hq]
     int32_t *counters;   // [B, Hkv], zero between launches
 };
+
+// Row of q (in D-element rows) holding query head h (0 <= h < G) of KV head
+// kvh for request r of the launch.
+__device__ __forceinline__ int64_t q_row(const PartialArgs &a, int r, int kvh, int G, int h)
+{
+    if (a.q_members) {
+        const int m = h / a.q_group;
+        const int g = h - m * a.q_group;
+        return int64_t(a.q_members[m]) * (int64_t(a.num_kv_heads) * a.q_group) +
+               int64_t(kvh) * a.q_group + g;
+    }
+    return int64_t(r) * a.num_qo_heads + int64_t(kvh) * G + h;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
@@ -493,11 +515,11 @@ __global__ void __launch_bounds__(64 * HPW * WPH) partial_page_kernel(PartialArg
     // loads then wait for the page ids alone
     int32_t idv = load_ids(cp0);
 
-    const T *qp = static_cast<const T *>(a.q) +
-                  (int64_t(r) * a.num_qo_heads + int64_t(kvh) * G) * D + li * VEC;
     Row16 qv[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[h].u = *reinterpret_cast<const uint4 *>(qp + h * D);
+    for (int h = 0; h < G; ++h)
+        qv[h].u = *reinterpret_cast<const uint4 *>(static_cast<const T *>(a.q) +
+                                                   q_row(a, r, kvh, G, h) * D + li * VEC);
 
     constexpr int ESZ = sizeof(T);
     const char *kb = static_cast<const char *>(a.k) + int64_t(kvh) * a.head_stride * ESZ;
@@ -831,11 +853,11 @@ __global__ void __launch_bounds__(kThreads) partial_token_kernel(PartialArgs a)
     const int cp0 = t * a.pages_per_chunk;
     const int cp1 = min(npages, cp0 + a.pages_per_chunk);
 
-    const T *qp = static_cast<const T *>(a.q) +
-                  (int64_t(r) * a.num_qo_heads + int64_t(kvh) * G) * D + li * VEC;
     Row16 qv[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[h].u = *reinterpret_cast<const uint4 *>(qp + h * D);
+    for (int h = 0; h < G; ++h)
+        qv[h].u = *reinterpret_cast<const uint4 *>(static_cast<const T *>(a.q) +
+                                                   q_row(a, r, kvh, G, h) * D + li * VEC);
 
     const T *kbase = static_cast<const T *>(a.k) + int64_t(kvh) * a.head_stride + li * VEC;
     const T *vbase = static_cast<const T *>(a.v) + int64_t(kvh) * a.head_stride + li * VEC;
@@ -967,18 +989,19 @@ constexpr int token_rows_per_step()
 // bytes against bank conflicts.
 constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per V row of the tile
 
-template <int G, int HPW>
-__global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
+// The group size G = a.group is a run-time value up to 16 * HT (heads past
+// G are zero columns of the 16-head tiles), so one instantiation serves
+// every group of its tile count, and a pair launch can run two tables of
+// different groups.
+template <int HT, int HPW>
+__device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
+                                          char (&s_v)[HPW][16 * kMfmaRowBytes])
 {
-    constexpr int HT = (G + 15) / 16;   // 16-head tiles
     constexpr int D = 128;
     constexpr int ESZ = 2;
-    static_assert(G >= 8 && G <= 32, "group");
-
-    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    const int G = a.group;
 
     const int groups = a.num_kv_heads / HPW;
-    const int wg = blockIdx.x;
     const int n = wg / groups;
     const int kvg = wg - n * groups;
     const int tid = threadIdx.x;
@@ -1014,8 +1037,7 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
     for (int ht = 0; ht < HT; ++ht) {
         const int h = ht * 16 + col;
         const _Float16 *qp = static_cast<const _Float16 *>(a.q) +
-                             (int64_t(r) * a.num_qo_heads + int64_t(kvh) * G + min(h, G - 1)) * D +
-                             8 * grp;
+                             q_row(a, r, kvh, G, min(h, G - 1)) * D + 8 * grp;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
             const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * kc);
@@ -1209,6 +1231,38 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
     }
 }
 
+template <int HT, int HPW>
+__global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
+{
+    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    mfma_body<HT, HPW>(a, blockIdx.x, s_v);
+}
+
+// Several tables in one grid: workgroups [wg_end[i-1], wg_end[i]) work on
+// table i's chunks.  The cascade runs every launch of its shared level
+// (stacked heads) and its per-request level this way, so that no level's
+// grid alone has to fill the GPU.  The tables share the pools, strides, KV
+// heads and page size; each has its own page table, plan, queries, group
+// and outputs.  The table is picked by a workgroup-uniform index into the
+// kernel arguments, so the body is compiled once.
+constexpr int kMaxTables = 8;
+struct PartialTables {
+    PartialArgs t[kMaxTables];
+    int32_t wg_end[kMaxTables];
+    int32_t count;
+};
+
+template <int HT, int HPW>
+__global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTables tabs)
+{
+    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    const int wg = blockIdx.x;
+    int i = 0;
+    while (i < tabs.count - 1 && wg >= tabs.wg_end[i]) ++i;
+    const int base = i > 0 ? tabs.wg_end[i - 1] : 0;
+    mfma_body<HT, HPW>(tabs.t[i], wg - base, s_v);
+}
+
 template <typename T, int D, bool FUSED>
 KernelFn pick_token(int g)
 {
@@ -1272,25 +1326,25 @@ struct Choice {
     int kind;           // 0 token kernel, 1 page kernel, 2 MFMA kernel
 };
 
-template <int G>
+template <int HT>
 KernelFn pick_mfma_shape(int hpw)
 {
     switch (hpw) {
-    case 8: return partial_mfma_kernel<G, 8>;
-    case 4: return partial_mfma_kernel<G, 4>;
-    case 2: return partial_mfma_kernel<G, 2>;
-    default: return partial_mfma_kernel<G, 1>;
+    case 8: return partial_mfma_kernel<HT, 8>;
+    case 4: return partial_mfma_kernel<HT, 4>;
+    case 2: return partial_mfma_kernel<HT, 2>;
+    default: return partial_mfma_kernel<HT, 1>;
     }
 }
 
 KernelFn pick_mfma(int g, int hpw)
 {
     switch (g) {
-    case 8: return pick_mfma_shape<8>(hpw);
-    case 12: return pick_mfma_shape<12>(hpw);
-    case 16: return pick_mfma_shape<16>(hpw);
-    case 24: return pick_mfma_shape<24>(hpw);
-    case 32: return pick_mfma_shape<32>(hpw);
+    case 8:
+    case 12:
+    case 16: return pick_mfma_shape<1>(hpw);
+    case 24:
+    case 32: return pick_mfma_shape<2>(hpw);
     default: return nullptr;
     }
 }
@@ -1403,6 +1457,9 @@ int check_and_fill(PartialArgs &a, const void *q, const void *k_pool, const void
     a.spp_log2 = 0;
     a.fd = make_fastdiv(uint32_t(page_size));
     a.scale_log2 = float(double(sm_scale) * 1.4426950408889634074);   // log2(e)
+    a.group = num_qo_heads / num_kv_heads;
+    a.q_members = nullptr;
+    a.q_group = 0;
     a.v_out = v_partial;
     a.lse_out = lse_partial;
     a.o_final = nullptr;
@@ -1490,6 +1547,141 @@ extern "C" int paged_decode_fused(const void *q, const void *k_pool, const void 
     a.lse_final = lse_out;
     a.counters = counters;
     return launch(c, a, num_chunks, stream, who);
+}
+
+// ------------------------------------------------------------ cascade partial
+namespace pd {
+namespace {
+
+using MultiFn = void (*)(PartialTables);
+
+template <int HT>
+MultiFn pick_mfma_multi(int hpw)
+{
+    switch (hpw) {
+    case 8: return partial_mfma_multi_kernel<HT, 8>;
+    case 4: return partial_mfma_multi_kernel<HT, 4>;
+    case 2: return partial_mfma_multi_kernel<HT, 2>;
+    default: return partial_mfma_multi_kernel<HT, 1>;
+    }
+}
+
+int check_level(const paged_cascade_level *lv, const char *who)
+{
+    if (!lv->indices || !lv->indptr || !lv->last_page_len || !lv->first_page_offset ||
+        !lv->request_indices || !lv->kv_tile_indices || !lv->v_partial || !lv->lse_partial)
+        return fail(PD_E_NULL, std::string(who) + ": null pointer in a level");
+    if (lv->batch < 1 || lv->num_chunks < 0 || lv->pages_per_chunk < 1)
+        return fail(PD_E_ARG, std::string(who) + ": bad level sizes");
+    return PD_OK;
+}
+
+}  // namespace
+}  // namespace pd
+
+extern "C" int paged_cascade_partial(const void *q, int32_t batch, const int32_t *member_req,
+                                     int32_t members, int32_t members_per_launch,
+                                     const void *k_pool, const void *v_pool, int64_t page_stride,
+                                     int64_t token_stride, int64_t head_stride, int32_t dtype,
+                                     int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t page_size, float sm_scale,
+                                     const paged_cascade_level *level0,
+                                     const paged_cascade_level *level1,
+                                     int32_t heads_per_workgroup, void *stream)
+{
+    const char *who = "paged_cascade_partial";
+    if (!q || !member_req || !level0) return fail(PD_E_NULL, std::string(who) + ": null pointer");
+    if (batch < 1 || members < 1 || members > batch || members_per_launch < 1 ||
+        num_kv_heads < 1 || num_qo_heads < 1 || num_qo_heads % num_kv_heads != 0 ||
+        int64_t(members_per_launch) * num_qo_heads > (1 << 20))
+        return fail(PD_E_ARG, std::string(who) + ": bad sizes");
+    if (heads_per_workgroup != 0 &&
+        ((heads_per_workgroup & (heads_per_workgroup - 1)) != 0 || heads_per_workgroup > 8 ||
+         heads_per_workgroup < 1 || num_kv_heads % heads_per_workgroup != 0))
+        return fail(PD_E_ARG, std::string(who) + ": heads_per_workgroup must be 0 or a power of "
+                                                 "two up to 8 dividing num_kv_heads");
+    const int g = num_qo_heads / num_kv_heads;
+    const int launches0 = (members + members_per_launch - 1) / members_per_launch;
+    // every table: level-0 launch j stacks members [j*per, min(M, (j+1)*per)),
+    // level 1 (if given) comes last
+    const int ntab = launches0 + (level1 ? 1 : 0);
+    std::vector<PartialArgs> args(ntab);
+    std::vector<Choice> choice(ntab);
+    std::vector<int32_t> chunks(ntab);
+    bool all_mfma = g <= 16;
+    for (int j = 0; j < ntab; ++j) {
+        const bool is0 = j < launches0;
+        const paged_cascade_level *lv = is0 ? &level0[j] : level1;
+        int rc = check_level(lv, who);
+        if (rc) return rc;
+        if (!is0 && lv->batch != batch)
+            return fail(PD_E_ARG, std::string(who) + ": level 1 must hold every request");
+        const int sj = is0 ? std::min(members_per_launch, members - j * members_per_launch) : 1;
+        const int gj = is0 ? sj * g : g;
+        rc = check_and_fill(args[j], q, k_pool, v_pool, page_stride, token_stride, head_stride,
+                            dtype, lv->indices, lv->indptr, lv->last_page_len,
+                            lv->first_page_offset, lv->request_indices, lv->kv_tile_indices,
+                            lv->num_chunks, lv->pages_per_chunk, lv->batch, gj * num_kv_heads,
+                            num_kv_heads, head_dim, page_size, sm_scale, lv->v_partial,
+                            lv->lse_partial, who);
+        if (rc) return rc;
+        if (is0) {
+            args[j].q_members = member_req + int64_t(j) * members_per_launch;
+            args[j].q_group = g;
+        }
+        choice[j] = pick(dtype, head_dim, gj, page_size, token_stride, false,
+                         !g_force_token_kernel, num_kv_heads, !g_no_mfma);
+        if (!choice[j].fn)
+            return fail(PD_E_UNSUPPORTED, std::string(who) + ": no kernel for stacked group " +
+                                              std::to_string(gj));
+        chunks[j] = lv->num_chunks;
+        if (is0 && choice[j].kind != 2) all_mfma = false;
+    }
+    if (!all_mfma) {
+        // one launch per table, each on the kernel paged_decode_partial picks
+        for (int j = 0; j < ntab; ++j) {
+            if (chunks[j] == 0) continue;
+            const int rc = launch(choice[j], args[j], chunks[j], stream, who);
+            if (rc) return rc;
+        }
+        return PD_OK;
+    }
+    // every stacked launch runs on the MFMA kernel: the tables share grids of
+    // up to kMaxTables tables, the per-request level on the same kernel with
+    // its group as a run-time value.  Default width: two KV heads per
+    // workgroup (one for an odd count): the shared level has few chunks, so
+    // narrow workgroups spread it over many CUs.  In sweeps on MI355X (4 to
+    // 16 members, 8K to 32K shared tokens) two heads per workgroup was the
+    // best width or within a few percent of it, and eight up to 2x slower.
+    const int hpw = heads_per_workgroup ? heads_per_workgroup : (num_kv_heads % 2 ? 1 : 2);
+    int ht = 1;
+    for (int j = 0; j < ntab; ++j)
+        if (args[j].group > 16) ht = 2;
+    const MultiFn fn = ht == 1 ? pick_mfma_multi<1>(hpw) : pick_mfma_multi<2>(hpw);
+    const int groups = num_kv_heads / hpw;
+    int j = 0;
+    while (j < ntab) {
+        PartialTables tabs;
+        tabs.count = 0;
+        int64_t wgs = 0;
+        for (; j < ntab && tabs.count < kMaxTables; ++j) {
+            if (chunks[j] == 0) continue;
+            PartialArgs b = args[j];
+            b.spp_log2 = choice[0].spp_log2;   // one page size: tiles per page alike
+            wgs += int64_t(chunks[j]) * groups;
+            tabs.t[tabs.count] = b;
+            tabs.wg_end[tabs.count] = int32_t(wgs);
+            ++tabs.count;
+        }
+        if (tabs.count == 0) break;
+        if (wgs > int64_t(INT32_MAX)) return fail(PD_E_ARG, std::string(who) + ": grid too large");
+        hipLaunchKernelGGL(fn, dim3(uint32_t(wgs)), dim3(64 * hpw), 0,
+                           static_cast<hipStream_t>(stream), tabs);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return fail(PD_E_HIP, std::string(who) + ": launch failed: " + hipGetErrorString(err));
+    }
+    return PD_OK;
 }
 
 // ------------------------------------------------------ no-allocation entry

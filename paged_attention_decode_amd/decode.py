@@ -57,6 +57,7 @@ class PagedDecode:
                                                target_wgs, fixed_pages_per_chunk,
                                                dtype=pd_dtype, page_size=page_size)
         self.info, self.request_indices, self.kv_tile_indices, self.o_indptr = info, ri, ti, oi
+        self.fixed_pages_per_chunk = fixed_pages_per_chunk
         self.device = torch.device(device)
         idx = np.asarray(csr["indices"], np.int32)
         self.d_indices = _dev_i32(idx if idx.size else np.zeros(1, np.int32), self.device)
@@ -195,7 +196,9 @@ class CascadeDecode:
                  num_kv_heads: int, head_dim: int, members=None, shared_pages: int = 0,
                  min_shared_pages: int = 16, min_members: int = 2, target_wgs: int = 0,
                  target_wgs_level0: int = 0, min_level0_tokens: int = 64,
-                 merge_in_place: bool = True, dtype=torch.float16, device="cuda"):
+                 merge_in_place: bool = True, pair_launch: bool = True,
+                 heads_per_workgroup: int = 0, fixed_pages_level0: int = 0,
+                 fixed_pages_level1: int = 0, dtype=torch.float16, device="cuda"):
         indptr = np.asarray(csr["indptr"], np.int32)
         indices = np.asarray(csr["indices"], np.int32)
         lpl = np.asarray(csr["last_page_len"], np.int32)
@@ -229,8 +232,10 @@ class CascadeDecode:
         per = cascade_members_per_launch(self.member_req.size, g, head_dim, pd_dtype, page_size,
                                          num_kv_heads * head_dim)
         self.subgroups = [self.member_req[i:i + per] for i in range(0, self.member_req.size, per)]
+        self.pair_launch = pair_launch
+        self.heads_per_workgroup = heads_per_workgroup
         self.level0 = []
-        fixed = 0
+        fixed = fixed_pages_level0
         # Level 0's chunks hold at least min_level0_tokens tokens unless a
         # level-0 target (target_wgs_level0) is given; a target_wgs given for
         # the whole step still gets the floor.  A stacked chunk writes M*G
@@ -241,18 +246,37 @@ class CascadeDecode:
         # 32K shared tokens on the plan's chunks are larger anyway.
         floor = 0 if target_wgs_level0 else min(self.shared_pages,
                                                   -(-min_level0_tokens // page_size))
+        # When the first level-0 launch and level 1 run as one grid (pair
+        # launch: both on the MFMA kernel), they share the GPU.  By default
+        # the workgroups hold two KV heads, level 0 is planned for about one
+        # workgroup per CU (its chunks are few and long, and each adds
+        # members*Hq partial rows to the merge), and level 1 for as many
+        # units.  Sweeps on MI355X (4 to 16 members, 8K
+        # to 32K shared tokens; level-1 chunks of 1 to 33 pages) put this
+        # within about 10% of the best chunking, where either level planned
+        # for the whole GPU was up to 1.5x slower.
+        t0, t1 = target_wgs_level0 or target_wgs, target_wgs
+        g0 = self.subgroups[0].size * g
+        self.pair_eligible = pair_launch and g <= 16 and B.load().paged_decode_kernel_kind(
+            pd_dtype, head_dim, g0, page_size, num_kv_heads * head_dim) == 2
+        if self.pair_eligible and not heads_per_workgroup:
+            self.heads_per_workgroup = 1 if num_kv_heads % 2 else 2
+        if self.pair_eligible and not (target_wgs_level0 or target_wgs):
+            cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+            t0 = cus * self.heads_per_workgroup
+            t1 = t0
+        self.targets = (t0, t1)
         for sub in self.subgroups:
-            lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads,
-                             target_wgs=target_wgs_level0 or target_wgs,
+            lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads, target_wgs=t0,
                              fixed_pages_per_chunk=fixed, **kw)
             if not fixed and lv.info.pages_per_chunk < floor:
                 fixed = floor
-                lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads,
-                                 target_wgs=target_wgs_level0 or target_wgs,
+                lv = PagedDecode(csr0, num_qo_heads=sub.size * num_qo_heads, target_wgs=t0,
                                  fixed_pages_per_chunk=fixed, **kw)
             fixed = fixed or lv.info.pages_per_chunk      # one level-0 chunking for all
             self.level0.append(lv)
-        self.level1 = PagedDecode(csr1, num_qo_heads=num_qo_heads, target_wgs=target_wgs, **kw)
+        self.level1 = PagedDecode(csr1, num_qo_heads=num_qo_heads, target_wgs=t1,
+                                  fixed_pages_per_chunk=fixed_pages_level1, **kw)
         self.n0 = self.level0[0].info.num_chunks
         self.n1 = self.level1.info.num_chunks
         self.rows0 = None
@@ -273,6 +297,18 @@ class CascadeDecode:
             self.d_l0_desc = _dev_i32(
                 B.paged_cascade_merge_layout(self.batch, self.member_req, per, self.n0,
                                              num_qo_heads), self.device)
+        # the C-ABI's view of each level (device addresses of the tensors above)
+        self.l0_levels = B.cascade_levels(
+            [B.cascade_level(lv.d_indices, lv.d_indptr, lv.d_lpl, lv.d_fpo, lv.d_req, lv.d_tile,
+                             1, lv.info.num_chunks, lv.info.pages_per_chunk, lv.v_partial,
+                             lv.lse_partial) for lv in self.level0])
+        self.members_per_launch = per
+        self.d_member_req = _dev_i32(self.member_req, self.device)
+        l1 = self.level1
+        self.l1_level = B.cascade_level(l1.d_indices, l1.d_indptr, l1.d_lpl, l1.d_fpo, l1.d_req,
+                                        l1.d_tile, self.batch, l1.info.num_chunks,
+                                        l1.info.pages_per_chunk, l1.v_partial, l1.lse_partial)
+        self.page_size = page_size
         dst0, dst1, oi = B.paged_cascade_layout(self.member_req, self.n0, self.level1.o_indptr)
         self.o_indptr = oi
         self.d_oindptr = _dev_i32(oi, self.device)
@@ -284,7 +320,6 @@ class CascadeDecode:
             self.d_dst0.append(_dev_i32(dst0[pos:pos + sub.size], self.device))
             pos += sub.size
         rows = int(oi[-1])
-        self.q0 = [None] * len(self.subgroups)
         self.v_cat = self.lse_cat = None            # the gathered merge input
         if self.rows0 is None:
             self.v_cat = torch.empty((rows, num_qo_heads, head_dim), dtype=torch.float32,
@@ -305,7 +340,9 @@ class CascadeDecode:
             return dict(cascade=False, flat=self.flat.plan_summary())
         return dict(cascade=True, members=[int(x) for x in self.member_req],
                     shared_pages=self.shared_pages, subgroups=len(self.subgroups),
-                    level0=self.level0[0].plan_summary(), level1=self.level1.plan_summary())
+                    pair_launch=self.pair_launch, heads_per_workgroup=self.heads_per_workgroup,
+                    targets=list(self.targets), level0=self.level0[0].plan_summary(),
+                    level1=self.level1.plan_summary())
 
     def run(self, q, k_pool, v_pool, sm_scale, stream=None):
         """One decode step: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32)."""
@@ -318,14 +355,17 @@ class CascadeDecode:
             raise TypeError("q and pools must share the dtype the cascade was planned for")
         if not (q.is_cuda and k_pool.is_cuda and v_pool.is_cuda):
             raise ValueError("q and pools must be device tensors")
-        for j, sub in enumerate(self.subgroups):
-            if self.q0[j] is None or self.q0[j].dtype != q.dtype:
-                self.q0[j] = torch.empty((1, sub.size * hq, d), dtype=q.dtype, device=q.device)
-        for j, sub in enumerate(self.subgroups):
-            B.paged_cascade_stack_q(q, _pd_dtype(q), self.d_members[j], sub.size, hq, hkv, d,
-                                    self.q0[j], stream)
-            self.level0[j].partial(self.q0[j], k_pool, v_pool, sm_scale, stream)
-        self.level1.partial(q, k_pool, v_pool, sm_scale, stream)
+        ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
+        # level 0 reads the members' queries in place (stacked heads, no
+        # copy); one grid carries every level-0 launch and level 1 unless
+        # pair_launch is off
+        B.paged_cascade_partial(q, self.batch, self.d_member_req, self.member_req.size,
+                                self.members_per_launch, k_pool, v_pool, ps_, ts_, hs_,
+                                _pd_dtype(q), hq, hkv, d, self.page_size, sm_scale,
+                                self.l0_levels, self.l1_level if self.pair_launch else None,
+                                self.heads_per_workgroup, stream)
+        if not self.pair_launch:
+            self.level1.partial(q, k_pool, v_pool, sm_scale, stream)
         if self.rows0 is not None:
             B.paged_cascade_merge_states(self.rows0[0], self.rows0[1], self.n0, self.d_l0_desc,
                                          self.level1.v_partial, self.level1.lse_partial,

@@ -434,7 +434,8 @@ def _check_cascade_partials(orc, w, cas):
         check_close(lv.v_partial.cpu().numpy(), lv.lse_partial.cpu().numpy(), pv, pl, w.dtype,
                     "level-0 partials, launch %d (%d members, stacked G=%d)" % (j, n_m, n_m * g))
     l1 = cas.level1
-    oplan = orc.plan(csr1["indptr"], hkv, l1.info.target_wgs)
+    oplan = orc.plan(csr1["indptr"], hkv, l1.info.target_wgs,
+                     fixed_pages_per_chunk=l1.fixed_pages_per_chunk)
     assert np.array_equal(oplan["request_indices"], l1.request_indices)
     assert np.array_equal(oplan["kv_tile_indices"], l1.kv_tile_indices)
     pv, pl = orc.partial(w.q, w.k_pool, w.v_pool, csr1, ps, w.sm_scale, l1.request_indices,
@@ -472,6 +473,51 @@ def test_cascade_matches_flat_and_oracle(orc, in_place):
     torch.cuda.synchronize()
     check_close(out.cpu().numpy(), lse.cpu().numpy(), fo.cpu().numpy().astype(np.float64),
                 fl.cpu().numpy().astype(np.float64), w.dtype, "cascade-vs-flat")
+
+
+@pytest.mark.parametrize("pair,hpw,fixed0,fixed1", [
+    (True, 0, 0, 0), (True, 8, 0, 0), (True, 4, 0, 0), (True, 2, 0, 0), (True, 1, 0, 0),
+    (True, 0, 8, 1), (True, 4, 2, 4), (False, 0, 0, 0)],
+    ids=["pair-auto", "pair-hpw8", "pair-hpw4", "pair-hpw2", "pair-hpw1", "pair-c8-c1",
+         "pair-hpw4-c2-c4", "level1-separate"])
+def test_cascade_pair_launch_shapes(orc, pair, hpw, fixed0, fixed1):
+    """The shared level (stacked G0 = 16, queries read through the member
+    list) and the per-request level (G = 4) in one MFMA grid, at every
+    workgroup width and several chunkings, and with level 1 launched on its
+    own: outputs and every partial row of both levels against the oracle."""
+    w = cached("cascade_fp16", poison_unused=True)
+    cas = _cascade(w, pair_launch=pair, heads_per_workgroup=hpw, fixed_pages_level0=fixed0,
+                   fixed_pages_level1=fixed1)
+    say("case cascade pair=%s hpw=%d plan=%s" % (pair, hpw, cas.plan_summary()))
+    assert cas.active and len(cas.subgroups) == 1
+    if fixed0:
+        assert cas.level0[0].info.pages_per_chunk == fixed0
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    for it in range(2):
+        out, lse = cas.run(q, k, v, w.sm_scale)
+        torch.cuda.synchronize()
+    ref_v, ref_l = _oracle_flat(orc, w)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "cascade")
+    _check_cascade_partials(orc, w, cas)
+
+
+@pytest.mark.parametrize("choice", [1, 2], ids=["token-kernel", "valu-kernels"])
+def test_cascade_stacked_queries_off_the_mfma_kernel(orc, choice):
+    """The stacked level's queries read through the member list on the page
+    and token kernels (two launches), against the oracle."""
+    B.paged_decode_set_kernel_choice(choice)
+    try:
+        w = _mixed_batch(91, 4, hq=32)
+        cas = _cascade(w, min_shared_pages=16)
+        say("case cascade kernel-choice=%d plan=%s" % (choice, cas.plan_summary()))
+        q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+        out, lse = cas.run(q, k, v, w.sm_scale)
+        torch.cuda.synchronize()
+        ref_v, ref_l = _oracle_flat(orc, w)
+        check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "cascade")
+        _check_cascade_partials(orc, w, cas)
+    finally:
+        B.paged_decode_set_kernel_choice(0)
 
 
 def _mixed_batch(seed, members, hq=32, hkv=8, prefix_pages=40, ps=16):
