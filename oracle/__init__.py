@@ -50,7 +50,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c (the sanitizer test's)
+_LIB = os.environ.get("ORACLE_LIB", os.path.join(_HERE, "liboracle.so"))
 _lib = None
 
 MAX_CHUNKS = 65535
