@@ -108,8 +108,10 @@ def parse():
                    help="also time the step at every power-of-two pages-per-chunk up to the "
                         "longest request (plus that length and the default plan's choice)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=20.0,
-                   help="approximate CPU work budget of the oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="wall-time budget of the oracle's single-thread run")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the streaming-read ceiling measurement")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
     return p.parse_args()
@@ -397,21 +399,48 @@ def main():
                            "kernel": "cascade step (prefix and suffix partial launches, merge)",
                            "kernel_sha": kernel_sha(), "bytes_per_launch": int(kv_bytes)}
 
+    if partial_only is not None and not args.no_ceiling:
+        # the HBM read rate this GPU reaches with a plain streaming-read kernel,
+        # over the same pool copies the decode reads, back to back
+        res["roofline"]["measured_ceiling_gbs"], res["roofline"]["ceiling_probe"] = \
+            read_ceiling(torch, B, kv, settle, run_steps, args)
+        res["roofline"]["frac_of_measured_ceiling"] = round(
+            res["roofline"]["achieved"] / res["roofline"]["measured_ceiling_gbs"], 4)
+
     if not args.no_cpu_baseline:
-        # the oracle as it stands on all host cores, repeated to fill the budget
-        reps = max(1, min(20, int(args.cpu_seconds / max(1e-3, first_oracle_s * cores))))
+        # the oracle as it stands: the median of 3 runs on all host cores over
+        # the whole step (the first run is the parity check's), then one run
+        # on one thread over the whole step, or over its first requests if
+        # that would take longer than --cpu-seconds
         ts = [first_oracle_s]
-        for _ in range(reps - 1):
+        for _ in range(2):
             tc = time.time()
             oracle.attention(w.q, w.k_pool, w.v_pool, ocsr, w.page_size, w.sm_scale,
                              nthreads=cores)
             ts.append(time.time() - tc)
         med = float(np.median(ts))
+        rows = w.batch
+        per_req = w.visible_tokens.astype(np.float64)
+        est_1t = med * cores                      # single-thread estimate of the whole step
+        while rows > 1 and est_1t * per_req[:rows].sum() / per_req.sum() > args.cpu_seconds:
+            rows -= 1
+        sub = oracle_subset(w, ocsr, rows)
+        tc = time.time()
+        oracle.attention(sub["q"], w.k_pool, w.v_pool, sub["csr"], w.page_size, w.sm_scale,
+                         nthreads=1)
+        t1 = time.time() - tc
+        sub_bytes = kv_bytes * per_req[:rows].sum() / per_req.sum()
         res["cpu_baseline"] = {"value": round(kv_bytes / med / 1e9, 4), "unit": "GB/s",
                                "cores": cores, "kind": "oracle",
                                "sample": "the whole %s step (%d visible tokens, all heads), "
-                                         "f64 oracle, %d run(s), median %.3f s wall"
+                                         "f64 oracle, median of %d runs: %.3f s wall"
                                          % (w.name, total_tokens, len(ts), med),
+                               "runs_s": [round(t, 3) for t in ts],
+                               "single_thread": {
+                                   "value": round(sub_bytes / t1 / 1e9, 5), "unit": "GB/s",
+                                   "cores": 1, "seconds": round(t1, 2),
+                                   "sample": "requests 0..%d of the step (%d visible tokens)"
+                                             % (rows - 1, int(per_req[:rows].sum()))},
                                "cpu_model": cpu_model()}
 
     if args.calibrate_copy:
@@ -732,6 +761,37 @@ def block_sparse(args, torch, B, PD, workloads, dev):
                                          % (tokens // hkv, hkv, oracle_s),
                                "cpu_model": cpu_model()}
     print(json.dumps(res), flush=True)
+
+
+def read_ceiling(torch, B, kv, settle, run_steps, args):
+    """Best read rate of the streaming-read probe over the K pool copies
+    (each larger than the last-level cache), step i reading copy i mod n, at
+    a few grid sizes; returns (GB/s, per-grid-size table)."""
+    dev = kv[0][0].device
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = kv[0][0].numel() * kv[0][0].element_size()
+    table = {}
+    for nt in (True, False):
+        for per_cu in (0.5, 1, 2, 4):
+            wgs = max(1, int(cus * per_cu))
+            sink = torch.empty(wgs, dtype=torch.int32, device=dev)
+            fn = lambda i: B.paged_hbm_read_probe(kv[i % len(kv)][0], nbytes, wgs, sink, nt)  # noqa
+            settle(fn)
+            run_steps(args.warmup, fn)
+            t, _ = run_steps(args.steps, fn)
+            table["%s x%d" % ("nt" if nt else "plain", wgs)] = round(nbytes / t / 1e9, 1)
+    return max(table.values()), {"bytes_per_launch": int(nbytes), "gbs_by_launch": table,
+                                 "kernel": "paged_hbm_read_probe (16-byte loads, 512 threads, "
+                                           "one contiguous segment per workgroup)"}
+
+
+def oracle_subset(w, ocsr, rows):
+    """The first `rows` requests of the oracle's CSR and their queries."""
+    ip = np.asarray(ocsr["indptr"])
+    csr = dict(indptr=ip[:rows + 1].copy(), indices=np.asarray(ocsr["indices"])[:ip[rows]],
+               last_page_len=np.asarray(ocsr["last_page_len"])[:rows],
+               first_page_offset=np.asarray(ocsr["first_page_offset"])[:rows])
+    return {"q": np.ascontiguousarray(w.q[:rows]), "csr": csr}
 
 
 def cpu_model() -> str:

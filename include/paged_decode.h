@@ -555,6 +555,17 @@ int paged_decode_set_kernel_choice(int32_t force_token_kernel);
 int paged_fastdiv_eval(int32_t d, const uint32_t *n, int64_t count, uint32_t *q,
                        uint32_t *r);
 
+/* Measurement helper: reads `bytes` (a positive multiple of 16) of the
+ * DEVICE buffer `buf` (16-byte aligned) once with 16-byte loads
+ * (non-temporal if `nontemporal`), in `num_wgs` workgroups of 512 threads
+ * each streaming one contiguous segment, and writes one word per workgroup
+ * to the DEVICE array sink [num_wgs] (so the loads cannot be dropped).  Timed
+ * back to back over buffers larger than the last-level cache, it gives the
+ * HBM read rate the GPU actually reaches -- the ceiling against which the
+ * decode kernels' achieved bandwidth is judged. */
+int paged_hbm_read_probe(const void *buf, int64_t bytes, int32_t num_wgs, int32_t nontemporal,
+                         uint32_t *sink, void *stream);
+
 /* Library version string. */
 const char *pd_version(void);
 

@@ -37,7 +37,7 @@ EXPORTED = ["pd_last_error", "pd_version", "csr_validate", "paged_csr_build",
             "paged_cascade_merge_layout", "paged_cascade_merge_states",
             "paged_sparse_csr", "paged_sparse_expand_blocks", "paged_mla_decode_partial",
             "paged_decode_q_heads_per_wg", "paged_decode_default_target_wgs",
-            "paged_fastdiv_eval"]
+            "paged_fastdiv_eval", "paged_hbm_read_probe"]
 
 
 class PagedDecodeError(RuntimeError):
@@ -108,6 +108,7 @@ _SIGS = {
     "paged_decode_q_heads_per_wg": (i32, [i32, i32, i32]),
     "paged_decode_default_target_wgs": (i32, [i32, i32, i32, i32, i32]),
     "paged_fastdiv_eval": (i32, [i32, u32p, i64, u32p, u32p]),
+    "paged_hbm_read_probe": (i32, [vp, i64, i32, i32, vp, vp]),
 }
 
 _lib = None
@@ -465,3 +466,9 @@ def paged_fastdiv_eval(d, n):
     _check(load().paged_fastdiv_eval(d, n.ctypes.data_as(u32p), n.size, q.ctypes.data_as(u32p),
                                      r.ctypes.data_as(u32p)))
     return q, r
+
+
+def paged_hbm_read_probe(buf, nbytes, num_wgs, sink, nontemporal=True, stream=None):
+    """One read pass over nbytes of the device tensor buf (measurement)."""
+    _check(load().paged_hbm_read_probe(_dev(buf), int(nbytes), int(num_wgs), int(nontemporal),
+                                       _dev(sink), _stream(stream)))

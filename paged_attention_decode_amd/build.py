@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("PD_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pd_host.cpp", "pd_cascade_host.cpp", "pd_partial.hip", "pd_merge.hip", "pd_cascade.hip",
-           "pd_sparse.hip", "pd_mla.hip"]
+           "pd_sparse.hip", "pd_mla.hip", "pd_probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + INCLUDE, "-I" + CSRC]

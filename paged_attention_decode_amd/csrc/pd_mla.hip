@@ -24,8 +24,10 @@
 // with 18 v_mfma_f32_16x16x32_f16 (Q^T held in registers, loaded once), then
 // one softmax update over the 32 tokens and
 //   O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] . P^T [32 x 16 heads]
-// with 32 v_mfma_f32_16x16x32_f16, V^T read from the LDS tile with the
-// transpose read ds_read_b64_tr_b16.  The lane layouts are those of the
+// with 2 x 32 v_mfma_f32_16x16x32_f16 (P^T as an fp16 part and an fp16
+// remainder, so the weights enter the product with about 22 bits, not
+// fp16's 11), V^T read from the LDS tile with the transpose read
+// ds_read_b64_tr_b16.  The lane layouts are those of the
 // decode-v2 MFMA kernel: a lane owns one head's running max and sum and 128 of
 // its output dims, so a rescale is a per-lane scalar.
 //
@@ -78,6 +80,10 @@ constexpr int kOffRing = 4;                   // tiles of row offsets kept (thre
 constexpr int kKeyAhead = PD_MLA_KEY_AHEAD;   // key steps whose LDS reads run ahead of the products
 constexpr int kValueAhead = PD_MLA_VALUE_AHEAD;   // value steps likewise
 // instruction classes of __builtin_amdgcn_sched_group_barrier
+// P^T enters the value product as an fp16 part plus an fp16 remainder
+// (two products per value step), so the weights keep about 22 bits instead
+// of fp16's 11
+constexpr bool kSplitP = true;
 constexpr int kMfma = 0x008;
 constexpr int kDsRead = 0x100;
 constexpr float kMlaNoMax = -1e30f;           // finite "no score yet" running max
@@ -278,7 +284,8 @@ mla_partial_kernel(MlaArgs a)
                      16 * (((lane & 3) >> 1) ^ (tr_r >> 1)) + 8 * (lane & 1);
 
     // One tile: S^T for both 16-token subtiles, one softmax update over its
-    // 32 tokens, then O^T += V^T . P^T as 32 products with K = 32 tokens.  The
+    // 32 tokens, then O^T += V^T . P^T as 2 x 32 products with K = 32 tokens
+    // (the fp16 part of P^T and its remainder).  The
     // k order of the value product is the score layout's: lane l holds
     // tokens 4*(l/16) + e of subtile 0 as k = 8*(l/16) + e and tokens
     // 16 + 4*(l/16) + e as k = 8*(l/16) + 4 + e, so P^T needs no data
@@ -344,13 +351,22 @@ mla_partial_kernel(MlaArgs a)
 #pragma unroll
             for (int dt = 0; dt < kDim / 16; ++dt) acc[dt] *= alpha;
         }
-        half8_t pb;
+        // P^T as the B operand: p rounded to fp16 (pb) and, with kSplitP, the
+        // rounding's remainder rounded to fp16 (pl), each taken by its own
+        // value product; the sum takes the weights the products use
+        half8_t pb, pl;
         float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const _Float16 ph = _Float16(fast_exp2(x[e] - m_run));
+            const float p = fast_exp2(x[e] - m_run);
+            const _Float16 ph = _Float16(p);
             pb[e] = ph;
-            ls += float(ph);              // the sum takes the weights the products use
+            if constexpr (kSplitP) {
+                pl[e] = _Float16(p - float(ph));
+                ls += p;
+            } else {
+                ls += float(ph);
+            }
         }
         l_part += ls;
         auto vfrag = [&](int dt) -> half8_t {
@@ -363,22 +379,42 @@ mla_partial_kernel(MlaArgs a)
             return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         constexpr int VS = kDim / 16;                      // 32 value steps
-        constexpr int VD = kValueAhead + 1;                // value fragment ring
+        // The remainder's product for step dt is issued two steps later, so
+        // it does not wait on the same accumulator's previous product; the
+        // fragment ring keeps those two steps' fragments.
+        constexpr int kLag = kSplitP ? 2 : 0;
+        constexpr int VD = kValueAhead + 1 + kLag;         // value fragment ring
         half8_t fv[VD];
 #pragma unroll
-        for (int dt = 0; dt < VD - 1; ++dt) fv[dt] = vfrag(dt);
+        for (int dt = 0; dt < kValueAhead; ++dt) fv[dt] = vfrag(dt);
 #pragma unroll
         for (int dt = 0; dt < VS; ++dt) {
-            if (dt + VD - 1 < VS) fv[(dt + VD - 1) % VD] = vfrag(dt + VD - 1);
+            if (dt + kValueAhead < VS) fv[(dt + kValueAhead) % VD] = vfrag(dt + kValueAhead);
             acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fv[dt % VD], pb, acc[dt], 0, 0, 0);
+            if constexpr (kSplitP) {
+                if (dt >= kLag)
+                    acc[dt - kLag] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        fv[(dt - kLag) % VD], pl, acc[dt - kLag], 0, 0, 0);
+            }
+        }
+        if constexpr (kSplitP) {
+#pragma unroll
+            for (int dt = VS - kLag; dt < VS; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fv[dt % VD], pl, acc[dt], 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kDsRead, 2 * kValueAhead, 1);
 #pragma unroll
-        for (int dt = 0; dt < VS - kValueAhead; ++dt) {
+        for (int dt = 0; dt < kLag; ++dt) {
             __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
             __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
         }
-        __builtin_amdgcn_sched_group_barrier(kMfma, kValueAhead, 1);
+#pragma unroll
+        for (int dt = kLag; dt < VS - kValueAhead; ++dt) {
+            __builtin_amdgcn_sched_group_barrier(kMfma, kSplitP ? 2 : 1, 1);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(kMfma, kSplitP ? 2 * kValueAhead + kLag : kValueAhead,
+                                             1);
     };
 
     // Pipeline.  Before iteration i: LDS stage i%2 holds tile i, the rope

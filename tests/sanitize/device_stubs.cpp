@@ -51,3 +51,4 @@ PD_STUB(paged_sparse_csr, int32_t, int32_t, int32_t, int32_t, const int32_t *, i
         int32_t *, int32_t *)
 PD_STUB(paged_sparse_expand_blocks, const int32_t *, int32_t, int32_t, const int32_t *, int32_t,
         const int32_t *, const int32_t *, int32_t, int32_t *, void *)
+PD_STUB(paged_hbm_read_probe, const void *, int64_t, int32_t, int32_t, uint32_t *, void *)

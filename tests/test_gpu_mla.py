@@ -95,6 +95,28 @@ def run_mla(orc, w, *, fixed=0, target=0, heads=None, partial_rows=True):
     return dec
 
 
+def test_mla_peaked_scores(orc):
+    """Queries and rope queries scaled by 8: a few tokens carry most of each
+    head's weight, where rounding the probabilities to fp16 for the value
+    product would cost the most.  The kernel carries them as an fp16 part
+    plus an fp16 remainder; partial rows must stay within a quarter of the
+    fp16 tolerance."""
+    w = workloads.mla_paged("mla_peaked", seed=321, logical_start=[0, 5], written_len=[900, 700],
+                            num_qo_heads=128, page_size=16)
+    w.q[:] = (w.q.astype(np.float32) * 8).astype(np.float16)
+    w.q_extra[:] = (w.q_extra.astype(np.float32) * 8).astype(np.float16)
+    dec = run_mla(orc, w, fixed=4)
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len, 16)
+    pv, pl = orc.attention_mla(w.q, w.q_extra, w.k_pool, w.k_extra_pool, ocsr, 16, w.sm_scale,
+                               chunks=(dec.request_indices, dec.kv_tile_indices,
+                                       dec.info.pages_per_chunk), nthreads=NTHREADS)
+    dv = float(np.max(np.abs(dec.v_partial.cpu().numpy() - pv)))
+    fin = np.isfinite(pl)
+    dl = float(np.max(np.abs(dec.lse_partial.cpu().numpy()[fin] - pl[fin])))
+    say("  peaked scores: partial rows max|dv|=%.3g max|dlse|=%.3g" % (dv, dl))
+    assert dv <= TOL_V / 4 and dl <= TOL_L / 4
+
+
 @pytest.mark.parametrize("hq", [16, 32, 64, 128])
 @pytest.mark.parametrize("ps", [1, 16, 64, 128])
 def test_mla_ragged_poisoned(orc, hq, ps):
