@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KV GB/s and % of HBM peak, paged decode B=4 ctx=32k GQA fp16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, AMD published
+LLC_BYTES = 256 << 20           # MI355X Infinity Cache: a read ceiling needs larger buffers
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "partial_long_context_fp16_counters.md")
 PARTIAL_SRC = os.path.join(ROOT, "paged_attention_decode_amd", "csrc", "pd_partial.hip")
 
@@ -399,7 +400,8 @@ def main():
                            "kernel": "cascade step (prefix and suffix partial launches, merge)",
                            "kernel_sha": kernel_sha(), "bytes_per_launch": int(kv_bytes)}
 
-    if partial_only is not None and not args.no_ceiling:
+    if partial_only is not None and not args.no_ceiling and \
+            kv[0][0].numel() * kv[0][0].element_size() > LLC_BYTES:
         # the HBM read rate this GPU reaches with a plain streaming-read kernel,
         # over the same pool copies the decode reads, back to back
         res["roofline"]["measured_ceiling_gbs"], res["roofline"]["ceiling_probe"] = \
