@@ -79,11 +79,11 @@ constexpr int kOffRing = 4;                   // tiles of row offsets kept (thre
 #endif
 constexpr int kKeyAhead = PD_MLA_KEY_AHEAD;   // key steps whose LDS reads run ahead of the products
 constexpr int kValueAhead = PD_MLA_VALUE_AHEAD;   // value steps likewise
-// instruction classes of __builtin_amdgcn_sched_group_barrier
 // P^T enters the value product as an fp16 part plus an fp16 remainder
 // (two products per value step), so the weights keep about 22 bits instead
 // of fp16's 11
 constexpr bool kSplitP = true;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kMfma = 0x008;
 constexpr int kDsRead = 0x100;
 constexpr float kMlaNoMax = -1e30f;           // finite "no score yet" running max
