@@ -280,3 +280,43 @@ def test_fused_noalloc_refuses_before_touching_the_device(lib):
     assert rc == -8 and b"scratch" in lib.pd_last_error()
     rc = f(*args, 4096, 1, 0, 32, 8, 128, 16, 0.1, *tail)
     assert rc == -2
+
+
+def test_cascade_partial_argument_errors_before_launch():
+    """paged_cascade_partial refuses bad arguments before any launch (no
+    device needed: every case below fails a host-side check)."""
+    import ctypes
+    lib = B.load()
+    one = 16  # any non-null, 16-byte aligned address: nothing is dereferenced
+
+    def level(batch, chunks, v=one):
+        return B.CascadeLevel(one, one, one, one, one, one, batch, chunks, 2, v, one)
+
+    def call(q=one, batch=4, members=4, per=4, dtype=B.PD_DTYPE_FP16, d=128, hpw=0,
+             l0=None, l1=None):
+        l0 = B.cascade_levels([level(1, 4)]) if l0 is None else l0
+        l1 = level(batch, 8) if l1 is None else l1
+        return lib.paged_cascade_partial(q, batch, one, members, per, one, one, 16 * 8 * d,
+                                         8 * d, d, dtype, 32, 8, d, 16, 0.088, l0,
+                                         ctypes.byref(l1), hpw, None)
+
+    assert call(q=None) == B.CODES["PD_E_NULL"]
+    assert call(members=5) == B.CODES["PD_E_ARG"]                 # more members than requests
+    assert call(hpw=3) == B.CODES["PD_E_ARG"]
+    assert call(l1=level(3, 8)) == B.CODES["PD_E_ARG"]            # level 1 misses a request
+    assert call(l0=B.cascade_levels([level(1, 4, v=None)])) == B.CODES["PD_E_NULL"]
+    assert call(l0=B.cascade_levels([level(1, -1)])) == B.CODES["PD_E_ARG"]
+    assert call(dtype=7) == B.CODES["PD_E_UNSUPPORTED"]
+    assert call(d=96) == B.CODES["PD_E_UNSUPPORTED"]              # no kernel for this head dim
+    # with 2 members per table the call reads two level-0 tables: the second
+    # one is checked too
+    two = B.cascade_levels([level(1, 4), level(1, 4, v=None)])
+    assert call(per=2, l0=two) == B.CODES["PD_E_NULL"]
+
+
+def test_read_probe_argument_errors_before_launch():
+    lib = B.load()
+    assert lib.paged_hbm_read_probe(None, 1024, 4, 1, 16, None) == B.CODES["PD_E_NULL"]
+    assert lib.paged_hbm_read_probe(16, 1000, 4, 1, 16, None) == B.CODES["PD_E_ARG"]
+    assert lib.paged_hbm_read_probe(16, 1024, 0, 1, 16, None) == B.CODES["PD_E_ARG"]
+    assert lib.paged_hbm_read_probe(8, 1024, 4, 1, 16, None) == B.CODES["PD_E_UNSUPPORTED"]
