@@ -141,12 +141,11 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
 // rows), and the 256 threads are 256 / DL row lanes x DL dim lanes (lane =
 // DL * row lane + dim lane within each wave).  Row lane k merges rows k, k +
 // 256 / DL, ... of the group into a partial state (max, weight sum, weighted
-// V) with the loads of up to kSplitUnroll rows in flight.  The row states of a
+// V) with the loads of up to UNROLL rows in flight.  The row states of a
 // wave are combined by a butterfly of lane swaps (xor DL ... 32), the 4 wave
 // states through LDS.  Slicing the dims spreads one (row, head) over several
 // CUs; the merge runs right after the partial kernel and is bound by load
 // latency, not bandwidth.
-constexpr int kSplitUnroll = 4;
 // 512-wide rows (the paged MLA latent): 256-dim slices, one row lane per
 // wave.  Measured on MI355X with 128 heads: 7.1 us against 8.7 us for
 // 128-dim slices at 8 rows x 16 partials, the same 7.3-7.4 us at 4 x 32.

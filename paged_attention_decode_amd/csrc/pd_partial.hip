@@ -1420,6 +1420,7 @@ int check_and_fill(PartialArgs &a, const void *q, const void *k_pool, const void
                    int32_t page_size, float sm_scale, float *v_partial, float *lse_partial,
                    const char *who)
 {
+    (void)head_dim;   // the kernel choice checks it
     if (!q || !k_pool || !v_pool || !indices || !indptr || !last_page_len ||
         !first_page_offset || !request_indices || !kv_tile_indices || !v_partial ||
         !lse_partial)
