@@ -559,13 +559,16 @@ def _mixed_batch(seed, members, hq=32, hkv=8, prefix_pages=40, ps=16):
 
 
 @pytest.mark.parametrize("in_place", [True, False], ids=["in-place-merge", "gathered-merge"])
-@pytest.mark.parametrize("members,hq", [(3, 32), (6, 32), (5, 16), (9, 32)])
+@pytest.mark.parametrize("members,hq", [(3, 32), (6, 32), (5, 16), (9, 32), (2, 64), (3, 64),
+                                        (2, 128)])
 def test_cascade_mixed_batch_and_subgroups(orc, members, hq, in_place):
     """Members, a mid-page window over the same pages, and unrelated requests in
     one batch.  Stacked groups of 12 and 24 query heads per KV head run on the
     MFMA kernel; 9 members at G = 4 split into launches of 6 + 3 members (24 + 12
-    heads), 5 members at G = 2 into 4 + 1 (8 + 2).  Every level-0 and level-1
-    partial row is checked as well as the outputs."""
+    heads), 5 members at G = 2 into 4 + 1 (8 + 2).  At G = 8 and 16 the level-1
+    group runs on the one-grid MFMA kernel too (2 or 3 members stack 16, 24 or
+    32 heads).  Every level-0 and level-1 partial row is checked as well as the
+    outputs."""
     w = _mixed_batch(80 + members, members, hq=hq)
     cas = _cascade(w, min_shared_pages=16, merge_in_place=in_place)
     say("case mixed cascade members=%d hq=%d plan=%s" % (members, hq, cas.plan_summary()))
