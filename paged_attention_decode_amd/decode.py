@@ -58,6 +58,7 @@ class PagedDecode:
                                                dtype=pd_dtype, page_size=page_size)
         self.info, self.request_indices, self.kv_tile_indices, self.o_indptr = info, ri, ti, oi
         self.fixed_pages_per_chunk = fixed_pages_per_chunk
+        self.num_pool_pages = num_pool_pages
         self.device = torch.device(device)
         idx = np.asarray(csr["indices"], np.int32)
         self.d_indices = _dev_i32(idx if idx.size else np.zeros(1, np.int32), self.device)
@@ -105,7 +106,25 @@ class PagedDecode:
             self.out, self.lse = v_partial, lse_partial
         self.v_partial, self.lse_partial = v_partial, lse_partial
 
+    def check_step(self, q, k_pool, v_pool):
+        """The shapes the kernels index by: q a contiguous [B, Hq, D] tensor
+        and pools [>= num_pool_pages, page_size, Hkv, D] (strided views
+        allowed), all of one dtype.  The C-ABI sees only addresses, so a
+        mis-shaped tensor is refused here rather than read out of bounds."""
+        if tuple(q.shape) != (self.batch, self.num_qo_heads, self.head_dim) or \
+                not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, D] = [%d, %d, %d] tensor (got %s)"
+                             % (self.batch, self.num_qo_heads, self.head_dim, tuple(q.shape)))
+        if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
+            raise TypeError("q and pools must share a dtype")
+        if k_pool.dim() != 4 or k_pool.shape[0] < self.num_pool_pages or \
+                tuple(k_pool.shape[1:]) != (self.page_size, self.num_kv_heads, self.head_dim):
+            raise ValueError("pools must be [>= %d pages, %d, %d, %d] (got %s)"
+                             % (self.num_pool_pages, self.page_size, self.num_kv_heads,
+                                self.head_dim, tuple(k_pool.shape)))
+
     def partial(self, q, k_pool, v_pool, sm_scale, stream=None):
+        self.check_step(q, k_pool, v_pool)
         ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
         B.paged_decode_partial(q, k_pool, v_pool, ps_, ts_, hs_, _pd_dtype(q), self.d_indices,
                                self.d_indptr, self.d_lpl, self.d_fpo, self.d_req, self.d_tile,
@@ -120,6 +139,7 @@ class PagedDecode:
                                  self.num_qo_heads, self.head_dim, self.out, self.lse, stream)
 
     def fused_step(self, q, k_pool, v_pool, sm_scale, stream=None):
+        self.check_step(q, k_pool, v_pool)
         ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
         B.paged_decode_fused(q, k_pool, v_pool, ps_, ts_, hs_, _pd_dtype(q), self.d_indices,
                              self.d_indptr, self.d_lpl, self.d_fpo, self.d_req, self.d_tile,
@@ -131,10 +151,6 @@ class PagedDecode:
     def run(self, q, k_pool, v_pool, sm_scale, stream=None):
         """One decode step: returns (out [B, Hq, D] fp32, lse [B, Hq] fp32,
         log2 units); the tensors are this object's buffers."""
-        if q.shape != (self.batch, self.num_qo_heads, self.head_dim) or not q.is_contiguous():
-            raise ValueError("q must be a contiguous [B, Hq, D] tensor")
-        if q.dtype != k_pool.dtype or q.dtype != v_pool.dtype:
-            raise TypeError("q and pools must share a dtype")
         if self.fused:
             self.fused_step(q, k_pool, v_pool, sm_scale, stream)
         else:
@@ -355,6 +371,7 @@ class CascadeDecode:
             raise TypeError("q and pools must share the dtype the cascade was planned for")
         if not (q.is_cuda and k_pool.is_cuda and v_pool.is_cuda):
             raise ValueError("q and pools must be device tensors")
+        self.level1.check_step(q, k_pool, v_pool)       # level 1 holds every request's q
         ps_, ts_, hs_ = pool_strides(k_pool, v_pool)
         # level 0 reads the members' queries in place (stacked heads, no
         # copy); one grid carries every level-0 launch and level 1 unless
@@ -554,7 +571,24 @@ class MlaDecode:
                     num_wgs=i.num_wgs, q_groups=i.q_groups, needs_merge=bool(i.needs_merge),
                     target_wgs=i.target_wgs, workspace_bytes=i.workspace_bytes)
 
+    def check_step(self, q, q_extra, k_pool, k_extra_pool):
+        """Shapes and dtypes the kernel indexes by (the C-ABI sees only
+        addresses)."""
+        if q.shape != (self.batch, self.num_qo_heads, self.dim) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B, Hq, dim] tensor")
+        if q_extra.shape != (self.batch, self.num_qo_heads, self.extra_dim) or \
+                not q_extra.is_contiguous():
+            raise ValueError("q_extra must be a contiguous [B, Hq, extra_dim] tensor")
+        if not (q.dtype == q_extra.dtype == k_pool.dtype == k_extra_pool.dtype == torch.float16):
+            raise TypeError("paged MLA decode takes fp16 queries and pools")
+        for pool, width in ((k_pool, self.dim), (k_extra_pool, self.extra_dim)):
+            if pool.dim() != 3 or pool.shape[0] < self.num_pool_pages or \
+                    pool.shape[1] != self.page_size or pool.shape[2] < width:
+                raise ValueError("pools must be [>= %d pages, %d, >= row width] (got %s)"
+                                 % (self.num_pool_pages, self.page_size, tuple(pool.shape)))
+
     def partial(self, q, q_extra, k_pool, k_extra_pool, sm_scale, stream=None):
+        self.check_step(q, q_extra, k_pool, k_extra_pool)
         kps, kts = _row_pool_strides(k_pool)
         xps, xts = _row_pool_strides(k_extra_pool)
         B.paged_mla_decode_partial(q, q_extra, k_pool, k_extra_pool, kps, kts, xps, xts,
@@ -572,18 +606,6 @@ class MlaDecode:
     def run(self, q, q_extra, k_pool, k_extra_pool, sm_scale, stream=None):
         """One decode step: returns (out [B, Hq, dim] fp32, lse [B, Hq] fp32,
         log2 units); the tensors are this object's buffers."""
-        if q.shape != (self.batch, self.num_qo_heads, self.dim) or not q.is_contiguous():
-            raise ValueError("q must be a contiguous [B, Hq, dim] tensor")
-        if q_extra.shape != (self.batch, self.num_qo_heads, self.extra_dim) or \
-                not q_extra.is_contiguous():
-            raise ValueError("q_extra must be a contiguous [B, Hq, extra_dim] tensor")
-        if not (q.dtype == q_extra.dtype == k_pool.dtype == k_extra_pool.dtype == torch.float16):
-            raise TypeError("paged MLA decode takes fp16 queries and pools")
-        for pool, width in ((k_pool, self.dim), (k_extra_pool, self.extra_dim)):
-            if pool.dim() != 3 or pool.shape[0] < self.num_pool_pages or \
-                    pool.shape[1] != self.page_size or pool.shape[2] < width:
-                raise ValueError("pools must be [>= %d pages, %d, >= row width] (got %s)"
-                                 % (self.num_pool_pages, self.page_size, tuple(pool.shape)))
         self.partial(q, q_extra, k_pool, k_extra_pool, sm_scale, stream)
         self.merge(stream)
         return self.out, self.lse

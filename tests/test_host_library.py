@@ -320,3 +320,56 @@ def test_read_probe_argument_errors_before_launch():
     assert lib.paged_hbm_read_probe(16, 1000, 4, 1, 16, None) == B.CODES["PD_E_ARG"]
     assert lib.paged_hbm_read_probe(16, 1024, 0, 1, 16, None) == B.CODES["PD_E_ARG"]
     assert lib.paged_hbm_read_probe(8, 1024, 4, 1, 16, None) == B.CODES["PD_E_UNSUPPORTED"]
+
+
+def test_decode_objects_refuse_mis_shaped_step_inputs():
+    """The decode objects check q and the pools against the shapes they were
+    planned for before any launch: the C-ABI sees only addresses, so a
+    mis-shaped or mistyped tensor would be read out of bounds.  Built on the
+    host (device='cpu'); every call below raises before the binding's
+    device-pointer check would."""
+    torch = pytest.importorskip("torch")
+    from paged_attention_decode_amd import decode as PD
+
+    w = workloads.generic("shape_checks", seed=5, dtype=workloads.FP16, page_size=8,
+                          num_qo_heads=8, num_kv_heads=2, head_dim=64,
+                          logical_start=[0, 3], written_len=[40, 29])
+    pages = w.k_pool.shape[0]
+    csr = B.paged_csr_build(w.block_tables, w.logical_start, w.written_len, 8, pages)
+    dec = PD.PagedDecode(csr, page_size=8, num_pool_pages=pages, num_qo_heads=8,
+                         num_kv_heads=2, head_dim=64, target_wgs=8, device="cpu")
+    q = torch.from_numpy(w.q)
+    k, v = torch.from_numpy(w.k_pool), torch.from_numpy(w.v_pool)
+    dec.check_step(q, k, v)                                   # the planned shapes pass
+    bad = [
+        ((q[:1], k, v), ValueError),                          # batch
+        ((q[:, :4], k, v), ValueError),                       # heads
+        ((q.transpose(0, 1).contiguous().transpose(0, 1), k, v), ValueError),   # not contiguous
+        ((q.float(), k, v), TypeError),                       # dtype against the pools
+        ((q, k[: pages - 1], v[: pages - 1]), ValueError),    # fewer pages than the table names
+        ((q, k[:, :4], v[:, :4]), ValueError),                # page size
+        ((q, k[:, :, :1], v[:, :, :1]), ValueError),          # KV heads
+        ((q, k[..., :32], v[..., :32]), ValueError),          # head dim
+    ]
+    for call in (dec.partial, dec.fused_step, dec.run):
+        for args, err in bad:
+            with pytest.raises(err):
+                call(*args, w.sm_scale)
+
+    m = workloads.mla_paged("shape_checks_mla", seed=6, logical_start=[0], written_len=[70],
+                            num_qo_heads=16)
+    mcsr = B.paged_csr_build(m.block_tables, m.logical_start, m.written_len, m.page_size,
+                             m.k_pool.shape[0])
+    mdec = PD.MlaDecode(mcsr, page_size=m.page_size, num_pool_pages=m.k_pool.shape[0],
+                        num_qo_heads=16, target_wgs=8, device="cpu")
+    mq, mqx = torch.from_numpy(m.q), torch.from_numpy(m.q_extra)
+    mk, mkx = torch.from_numpy(m.k_pool), torch.from_numpy(m.k_extra_pool)
+    mdec.check_step(mq, mqx, mk, mkx)
+    for args, err in [((mq[:, :8], mqx, mk, mkx), ValueError),
+                      ((mq, mqx[..., :32], mk, mkx), ValueError),
+                      ((mq.float(), mqx, mk, mkx), TypeError),
+                      ((mq, mqx, mk[..., :256], mkx), ValueError),
+                      ((mq, mqx, mk, mkx[:1]), ValueError)]:
+        for call in (mdec.partial, mdec.run):
+            with pytest.raises(err):
+                call(*args, m.sm_scale)
