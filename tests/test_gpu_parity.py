@@ -185,6 +185,19 @@ def test_long_context_fp16_full_size(orc, target, mode):
         assert dec.info.needs_merge
 
 
+@pytest.mark.parametrize("tokens,chunks", [(65535, 65535), (65536, 32768)])
+def test_plan_at_the_chunk_limit(orc, tokens, chunks, mode):
+    """The largest grid a plan may launch: at page size 1, 65535 pages split
+    one page per chunk give exactly PD_MAX_CHUNKS chunks (every partial row
+    compared, and one merge of 65535 rows); one page more forces two pages per
+    chunk."""
+    w = workloads.generic("chunk_limit_%d" % tokens, seed=71, dtype=workloads.FP16,
+                          page_size=1, num_qo_heads=4, num_kv_heads=1, head_dim=128,
+                          logical_start=[0], written_len=[tokens], poison_unused=True)
+    dec = run_flat(orc, w, target=10 ** 9, fused=mode["fused"])
+    assert dec.info.num_chunks == chunks and dec.info.needs_merge
+
+
 def test_token_sparse_page_size_one(orc):
     s = workloads.token_sparse_fp16()
     hkv, cap, d = s.k_dense.shape[1], s.k_dense.shape[2], s.k_dense.shape[3]
