@@ -185,16 +185,25 @@ def test_long_context_fp16_full_size(orc, target, mode):
         assert dec.info.needs_merge
 
 
-@pytest.mark.parametrize("tokens,chunks", [(65535, 65535), (65536, 32768)])
-def test_plan_at_the_chunk_limit(orc, tokens, chunks, mode):
-    """The largest grid a plan may launch: at page size 1, 65535 pages split
-    one page per chunk give exactly PD_MAX_CHUNKS chunks (every partial row
-    compared, and one merge of 65535 rows); one page more forces two pages per
+_LIMIT = {}
+
+
+@pytest.mark.parametrize("page_size,pages,chunks", [(1, 65535, 65535), (1, 65536, 32768),
+                                                    (16, 65535, 65535)],
+                         ids=["ps1-65535", "ps1-65536", "ps16-65535"])
+def test_plan_at_the_chunk_limit(orc, page_size, pages, chunks, mode):
+    """The largest grid a plan may launch: 65535 pages split one page per
+    chunk give exactly PD_MAX_CHUNKS chunks (every partial row compared, and
+    one merge of 65535 rows), at page size 1 (the token kernel) and at page
+    size 16 (the page kernel, 1M tokens); one page more forces two pages per
     chunk."""
-    w = workloads.generic("chunk_limit_%d" % tokens, seed=71, dtype=workloads.FP16,
-                          page_size=1, num_qo_heads=4, num_kv_heads=1, head_dim=128,
-                          logical_start=[0], written_len=[tokens], poison_unused=True)
-    dec = run_flat(orc, w, target=10 ** 9, fused=mode["fused"])
+    key = (page_size, pages)
+    if key not in _LIMIT:
+        _LIMIT[key] = workloads.generic(
+            "chunk_limit_ps%d_%d" % key, seed=71, dtype=workloads.FP16, page_size=page_size,
+            num_qo_heads=4, num_kv_heads=1, head_dim=128, logical_start=[0],
+            written_len=[pages * page_size], pool_slack=1.25, poison_unused=True)
+    dec = run_flat(orc, _LIMIT[key], target=10 ** 9, fused=mode["fused"])
     assert dec.info.num_chunks == chunks and dec.info.needs_merge
 
 
