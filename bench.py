@@ -121,7 +121,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the decode path has no "
+        print("bench.py: measures one GPU only (the decode path has no "
               "cross-GPU exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

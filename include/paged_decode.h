@@ -562,7 +562,7 @@ int paged_fastdiv_eval(int32_t d, const uint32_t *n, int64_t count, uint32_t *q,
  * to the DEVICE array sink [num_wgs] (so the loads cannot be dropped).  Timed
  * back to back over buffers larger than the last-level cache, it gives the
  * HBM read rate the GPU actually reaches -- the ceiling against which the
- * decode kernels' achieved bandwidth is judged. */
+ * decode kernels' achieved bandwidth is compared. */
 int paged_hbm_read_probe(const void *buf, int64_t bytes, int32_t num_wgs, int32_t nontemporal,
                          uint32_t *sink, void *stream);
 

@@ -2,7 +2,7 @@
 // loads and folds what it read into one word per workgroup (so
 // the loads cannot be dropped).  Timed next to the decode kernels, it gives
 // the read rate this GPU actually reaches, against which the decode's
-// achieved bandwidth is judged.
+// achieved bandwidth is compared.
 
 #include <hip/hip_runtime.h>
 
