@@ -157,19 +157,18 @@ __global__ void __launch_bounds__(256) merge_kernel(const float *__restrict__ v_
 #endif
 constexpr int kWideDL = PD_MERGE_WIDE_DL;     // dim lanes per slice for 512-wide rows
 constexpr int kWideUnroll = PD_MERGE_WIDE_UNROLL;
-// Other widths divisible by 32: 32-dim slices.  At 4 rows x 79 partials, 32
-// heads of 128 dims, 32-, 64- and 128-dim slices with 4 or 8 rows in flight
-// per lane all took 3.5-4.1 us of GPU time (HIP-graph replay); a merge of
-// 4 x 8 partials took 3.1 us: the kernel is bound by its fixed latency chain
-// (row bounds, one round of loads, the combine), not by its slice shape.
-#ifndef PD_MERGE_NARROW_DL
-#define PD_MERGE_NARROW_DL 8
-#endif
-#ifndef PD_MERGE_NARROW_UNROLL
-#define PD_MERGE_NARROW_UNROLL 4
-#endif
-constexpr int kNarrowDL = PD_MERGE_NARROW_DL;     // dim lanes per slice, other widths
-constexpr int kNarrowUnroll = PD_MERGE_NARROW_UNROLL;
+// Other widths divisible by 32: 32-dim slices.  The merge is bound by its
+// fixed latency chain (row bounds, one round of loads, the combine), not by
+// its slice shape: at 4 rows x 79 partials, 32 heads of 128 dims, 32-, 64-
+// and 128-dim slices of four waves all took 3.5-4.1 us of GPU time.  The flat
+// merge takes each slice in one wave (merge_wave_kernel below): without the
+// cross-wave LDS combine and its barrier the long-context step went from
+// 69.2 to 68.6-68.8 us on MI355X with 8 row lanes x 10 rows in flight; 16 x 5,
+// 4 x 20 and 8 x 16 measured no better.  The cascade merge, whose groups are
+// longer, keeps four waves of row lanes.
+constexpr int kNarrowDL = 8;          // float4 dim lanes per slice, other widths
+constexpr int kWaveUnroll = 10;       // one-wave kernel: rows in flight per row lane
+constexpr int kSliceUnroll = 4;       // four-wave kernel: rows in flight per row lane
 
 // State of a partial merge: running max m (NaN once a NaN lse was seen),
 // weight sum w relative to m, weighted sum a relative to m.
@@ -373,6 +372,88 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const Rows rows, int32
     if (lse_lane) lse_out[oh] = st.m + __builtin_amdgcn_logf(st.w);
 }
 
+// One wave per (output row, head, 4*DL-dim slice): DL float4 dim lanes x
+// 64/DL row lanes (lane = DL * row lane + dim lane).  Row lane k merges rows
+// k, k + 64/DL, ... with UNROLL rows' loads in flight, and the row lanes'
+// states are combined by the butterfly alone: no LDS and no barrier.
+template <int DL, int UNROLL, typename Rows>
+__global__ void __launch_bounds__(64) merge_wave_kernel(const Rows rows, int32_t num_heads,
+                                                        int32_t head_dim,
+                                                        float *__restrict__ v_out,
+                                                        float *__restrict__ lse_out)
+{
+    using V = float4;
+    constexpr int SPLIT = 64 / DL;               // row lanes
+    const int slices = head_dim / (4 * DL);      // a multiple of 4 * DL, checked by the launcher
+    const int lane = threadIdx.x;
+    const int dl_i = lane & (DL - 1);
+    const int k = lane / DL;                     // row lane
+    const int64_t ohs = blockIdx.x;              // (o * num_heads + h) * slices + slice
+    const int64_t oh = ohs / slices;
+    const int dv = int(ohs - oh * slices) * DL + dl_i;
+    const int h = int(oh % num_heads);
+    const int64_t o = oh / num_heads;
+    const typename Rows::Group grp = rows.bind(o, h, num_heads, head_dim);
+    const int b = grp.b;
+    const int e = grp.e;
+
+    MState<V> st;
+    st.m = -INFINITY;
+    st.w = 0.f;
+    st.a = filled<V>(0.f);
+    bool nan_seen = false;
+    for (int i0 = b + k; i0 < e; i0 += SPLIT * UNROLL) {
+        float x[UNROLL];
+        V vi[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int i = min(i0 + u * SPLIT, e - 1);
+            x[u] = grp.lse(i);
+            vi[u] = reinterpret_cast<const V *>(grp.v(i))[dv];
+        }
+        float mb = st.m;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            nan_seen |= x[u] != x[u];
+            mb = fmaxf(mb, x[u]);
+        }
+        if (mb == -INFINITY) continue;              // nothing finite yet
+        const float sc = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - mb);
+        st.w *= sc;
+        st.a = scaled(st.a, sc);
+        st.m = mb;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            // a row past the group end or with lse = -inf (empty chunk) has no
+            // weight, and its V (possibly not finite) is never multiplied in
+            const bool live = i0 + u * SPLIT < e && x[u] != -INFINITY;
+            const float w = live ? __builtin_amdgcn_exp2f(x[u] - st.m) : 0.f;
+            st.w += w;
+            fma_live(st.a, live, w, vi[u]);
+        }
+    }
+    if (nan_seen) st.m = NAN;
+#pragma unroll
+    for (int mask = DL; mask < 64; mask <<= 1) {
+        MState<V> y;
+        y.m = __shfl_xor(st.m, mask);
+        y.w = __shfl_xor(st.w, mask);
+        y.a = shfl_xor4(st.a, mask);
+        st = combine(st, y);
+    }
+    if (lane >= DL) return;
+    V *dst = reinterpret_cast<V *>(v_out + oh * head_dim) + dv;
+    const bool lse_lane = dv == 0;
+    if (st.m != st.m || st.m == -INFINITY) {
+        const bool nan = st.m != st.m;
+        *dst = filled<V>(nan ? NAN : 0.f);
+        if (lse_lane) lse_out[oh] = nan ? NAN : -INFINITY;
+        return;
+    }
+    *dst = scaled(st.a, 1.f / st.w);
+    if (lse_lane) lse_out[oh] = st.m + __builtin_amdgcn_logf(st.w);
+}
+
 // One workgroup per (output row, head), for any other head size: its 256
 // threads are `split` row lanes x D/W dim lanes; row lane k merges rows k,
 // k + split, ... of the group and the split states are combined through LDS.
@@ -499,8 +580,8 @@ extern "C" int paged_merge_states(const float *v_in, const float *lse_in,
         // one workgroup per (output row, head, 4*kNarrowDL-dim slice)
         const int64_t nblk = int64_t(num_out_rows) * num_heads * (head_dim / (4 * kNarrowDL));
         if (nblk > 0x7fffffff) return fail(PD_E_ARG, "paged_merge_states: too large");
-        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kNarrowUnroll, FlatRows>),
-                           dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_heads, head_dim,
+        hipLaunchKernelGGL((merge_wave_kernel<kNarrowDL, kWaveUnroll, FlatRows>),
+                           dim3(uint32_t(nblk)), dim3(64), 0, s, rows, num_heads, head_dim,
                            v_out, lse_out);
     } else if (head_dim / w <= 256) {
         // one workgroup per (output row, head), rows split across lanes
@@ -545,9 +626,10 @@ extern "C" int paged_cascade_merge_states(const float *v0, const float *lse0, in
     const CascadeRows rows{v0, lse0, v1, lse1, l0_desc, o_indptr1, n0,
                            num_qo_heads / num_kv_heads};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // The slice widths of paged_merge_states.  At 4 members x 8192 shared
-    // tokens (about 300 rows per group), 16- and 8-dim slices, or 8 rows in
-    // flight per lane, were as fast or slower (MI355X).
+    // 32-dim slices of four waves.  At 4 members x 8192 shared tokens (about
+    // 300 rows per group), 16- and 8-dim slices, or 8 rows in flight per lane,
+    // were as fast or slower (MI355X); the flat merge's one-wave kernel took
+    // the step from 20.6 to 21.2 us.
     const bool wide = head_dim % (4 * kWideDL) == 0;
     const int64_t nblk =
         int64_t(batch) * num_qo_heads * (head_dim / (4 * (wide ? kWideDL : kNarrowDL)));
@@ -557,7 +639,7 @@ extern "C" int paged_cascade_merge_states(const float *v0, const float *lse0, in
                            dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_qo_heads, head_dim,
                            v_out, lse_out);
     else
-        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kNarrowUnroll, CascadeRows>),
+        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kSliceUnroll, CascadeRows>),
                            dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_qo_heads, head_dim,
                            v_out, lse_out);
     const hipError_t err = hipGetLastError();

@@ -608,10 +608,12 @@ def test_cascade_mixed_batch_and_subgroups(orc, members, hq, in_place):
 
 @pytest.mark.parametrize("members,hq,d", [(9, 32, 128), (5, 16, 128), (4, 32, 64)])
 def test_cascade_in_place_merge_equals_gathered_merge(orc, members, hq, d):
-    """The merge that reads the stacked level-0 rows in place visits each
-    group's rows in the order the gathered copy lays them out, so the two
-    compositions agree bit for bit (several stacked launches included), and
-    both match the oracle."""
+    """The merge that reads the stacked level-0 rows in place and the merge
+    of the gathered copy see the same rows (several stacked launches
+    included): they agree to rounding (the in-place merge folds a group with
+    four waves of row lanes, the flat merge with one), and both match the
+    oracle.  A row read from the wrong place would differ at the scale of the
+    values themselves."""
     w = workloads.cascade_fp16(seed=90 + members, members=members, prefix_tokens=1024,
                                suffix_lo=16, suffix_hi=400, hq=hq, hkv=hq // 4, d=d,
                                poison_unused=True)
@@ -624,7 +626,13 @@ def test_cascade_in_place_merge_equals_gathered_merge(orc, members, hq, d):
     oa, la = (t.clone() for t in a.run(q, k, v, w.sm_scale))
     ob, lb = b.run(q, k, v, w.sm_scale)
     torch.cuda.synchronize()
-    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    assert torch.equal(torch.isneginf(la), torch.isneginf(lb))
+    dv = float((oa - ob).abs().max())
+    dl = float((la - lb)[torch.isfinite(la)].abs().max())
+    say("  in-place vs gathered: max|dv|=%.3g max|dlse|=%.3g" % (dv, dl))
+    # a few fp32 ulps (the LSEs are O(10) in log2 units)
+    lmax = float(la[torch.isfinite(la)].abs().max())
+    assert dv <= 1e-6 and dl <= 1e-6 * max(1.0, lmax)
     ref_v, ref_l = _oracle_flat(orc, w)
     check_close(oa.cpu().numpy(), la.cpu().numpy(), ref_v, ref_l, w.dtype, "in-place cascade")
 
