@@ -117,6 +117,32 @@ def test_mla_peaked_scores(orc):
     assert dv <= TOL_V / 4 and dl <= TOL_L / 4
 
 
+@pytest.mark.parametrize("hq", [64, 128])
+def test_mla_scores_ramp_rescale_every_tile(orc, hq):
+    """Rope keys rewritten so that head 0's scores rise by 0.6 log2 units per
+    token (K_extra[t] = lambda_t * q_extra / |q_extra|; the latent rows, which
+    are also the values, stay N(0,1)): its running max passes the lazy-rescale
+    margin on every 32-token tile, so the accumulators are rescaled every
+    time, over about 540 log2 units; the other heads see the same keys at
+    random angles.  Outputs and every partial row against the oracle."""
+    w = workloads.mla_paged("mla_ramp", seed=331, logical_start=[0, 5], written_len=[900, 700],
+                            num_qo_heads=hq, page_size=16)
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len, 16)
+    scale_log2 = w.sm_scale / np.log(2.0)
+    kx = w.k_extra_pool.astype(np.float32)
+    for r in range(w.batch):
+        n = int(ocsr["seq_lens"][r])
+        slots = ocsr["first_page_offset"][r] + np.arange(n)
+        pages = ocsr["indices"][ocsr["indptr"][r] + slots // 16]
+        qx = w.q_extra[r, 0].astype(np.float64)
+        lam = 0.6 * np.arange(n) / (scale_log2 * np.linalg.norm(qx))
+        row = (lam[:, None] * (qx / np.linalg.norm(qx))[None, :]).astype(np.float32)
+        assert np.abs(row).max() < 6e4                       # inside the fp16 range
+        kx[pages, slots % 16] = row
+    w.k_extra_pool[:] = kx.astype(np.float16)
+    run_mla(orc, w, fixed=4)
+
+
 @pytest.mark.parametrize("hq", [16, 32, 64, 128])
 @pytest.mark.parametrize("ps", [1, 16, 64, 128])
 def test_mla_ragged_poisoned(orc, hq, ps):

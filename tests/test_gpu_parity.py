@@ -846,6 +846,45 @@ def test_mfma_kernel_peaked_scores(orc, g):
     assert dv <= 5e-4 and dl <= 2.5e-4
 
 
+def ramp_keys(orc, w, slope_log2):
+    """Rewrites the visible K rows of workload w so that the scores of the
+    first query head of every KV head rise by slope_log2 (log2 units) per
+    token: K[t] = lambda_t * q / |q|.  Every step of every chunk then raises
+    that head's running max past the lazy-rescale margin, so the rescale path
+    runs on every step, over a score range of hundreds of log2 units."""
+    ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len,
+                                     w.page_size)
+    g = w.num_qo_heads // w.num_kv_heads
+    scale_log2 = w.sm_scale / np.log(2.0)
+    k = w.k_pool.astype(np.float32)
+    for r in range(w.batch):
+        n = int(ocsr["seq_lens"][r])
+        slots = ocsr["first_page_offset"][r] + np.arange(n)
+        pages = ocsr["indices"][ocsr["indptr"][r] + slots // w.page_size]
+        entries = slots % w.page_size
+        for kvh in range(w.num_kv_heads):
+            q = w.q[r, kvh * g].astype(np.float64)
+            u = q / np.linalg.norm(q)
+            lam = slope_log2 * np.arange(n) / (scale_log2 * np.linalg.norm(q))
+            row = (lam[:, None] * u[None, :]).astype(np.float32)
+            assert np.abs(row).max(initial=0.0) < 6e4          # inside the fp16 range
+            k[pages, entries, kvh] = row
+    w.k_pool[:] = k.astype(w.k_pool.dtype)
+
+
+@pytest.mark.parametrize("g", [4, 16])
+def test_scores_ramp_rescale_every_step(orc, g, mode):
+    """Scores that rise by 0.6 log2 units per token for one head of every KV
+    head (and fall or wander for the others): the running max grows past the
+    lazy margin on every step and the accumulators are rescaled each time,
+    over a score range of about 900 log2 units.  Every kernel mode, every
+    partial row and the merge against the oracle at the usual tolerances."""
+    w = workloads.random_geometry(730 + g, batch=3, page_size=16, max_len=1500,
+                                  num_qo_heads=g * 4, num_kv_heads=4, p_empty=0.0, p_trim=0.5)
+    ramp_keys(orc, w, 0.6)
+    run_flat(orc, w, target=0, fixed=16, fused=mode["fused"])
+
+
 def test_kernel_choice():
     kk = B.paged_decode_kernel_kind
     assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1024) == 1
