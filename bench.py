@@ -388,7 +388,7 @@ def main():
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "traffic": counter_traffic() if default_run else None,
-                           "kernel_kind": {0: "token", 1: "page", 2: "mfma"}[kind],
+                           "kernel_kind": {0: "token", 1: "page", 2: "mfma", 3: "mfma-any-page"}[kind],
                            "kernel": "paged_decode_partial", "kernel_sha": kernel_sha(),
                            "bytes_per_launch": int(kv_bytes)}
     else:

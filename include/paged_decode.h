@@ -182,10 +182,9 @@ int paged_decode_plan(int32_t batch, const int32_t *indptr,
  * are the (validated) CSR; request_indices/kv_tile_indices the plan's.
  * Outputs: v_partial [num_chunks, Hq, D] fp32 and lse_partial [num_chunks,
  * Hq] fp32.  Supported: D in {64, 128} with G in {1, 2, 4, 8, 12, 16};
- * and G in {24, 32} for fp16, D = 128 and a page size that is a power-of-two
- * multiple of 16 (the MFMA kernel; paged_decode_kernel_kind() tells which
- * kernel serves a shape).  Other shapes return PD_E_UNSUPPORTED before any
- * launch.
+ * and G in {24, 32} for fp16 and D = 128, at any page size (the MFMA
+ * kernels; paged_decode_kernel_kind() tells which kernel serves a shape).
+ * Other shapes return PD_E_UNSUPPORTED before any launch.
  * ---------------------------------------------------------------------- */
 int paged_decode_partial(const void *q, const void *k_pool, const void *v_pool,
                          int64_t page_stride, int64_t token_stride, int64_t head_stride,
@@ -202,7 +201,9 @@ int paged_decode_partial(const void *q, const void *k_pool, const void *v_pool,
  * paged_decode_fused -- the partial and the merge in one launch (PR #984 body
  * item 5 "write O directly" for single-chunk requests; issue #898 items 2-3).
  *
- * Same inputs as paged_decode_partial.  A request with one chunk writes its
+ * Same inputs as paged_decode_partial; the fused launch runs the page and
+ * token kernels only, so G in {24, 32} returns PD_E_UNSUPPORTED here.  A
+ * request with one chunk writes its
  * result straight to out[r] / lse_out[r].  A request with several chunks
  * writes its partial rows to v_partial / lse_partial (as paged_decode_partial
  * would), then the last of its workgroups to finish -- counted per (request,
@@ -531,7 +532,9 @@ int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t 
 
 /* Which partial kernel paged_decode_partial launches for a shape:
  * 2 = MFMA kernel (fp16, head_dim 128, group 8, 12, 16, 24 or 32, page_size a
- *     power-of-two multiple of 16);
+ *     power-of-two multiple of 16, in-page offsets below 2^31 bytes);
+ * 3 = any-page MFMA kernel (the same dtype, head_dim and groups at every
+ *     other page size: a 16-token tile may span 16 pages);
  * 1 = page kernel (256-byte K/V rows, group 4, 8 or 16, page_size a
  *     power-of-two multiple of the 64/group slots of one step), for the
  *     shapes the MFMA kernel does not take;

@@ -1263,6 +1263,251 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTab
     mfma_body<HT, HPW>(tabs.t[i], wg - base, s_v);
 }
 
+// ----------------------------------------------------- MFMA kernel, any page
+// The MFMA kernel above reads a 16-token tile from one page.  This variant
+// serves page sizes it cannot (page size 1 -- token-sparse selections --
+// and sizes that are not a power-of-two multiple of 16): the tile's 16
+// tokens may lie on 16 pages.  Each wave keeps the byte offsets of 64
+// consecutive tokens of its chunk in a register (lane t: token w0 + t,
+// from the page id and in-page slot of the PR #984 page-table walk,
+// fast-divided by the page size) and gathers a tile's offsets from it with
+// ds_bpermute: lane l loads K of token l % 16 and V rows l / 16 + 4j, as
+// the page variant does within a page.  The products, the softmax and the
+// epilogue are the page variant's.  Tokens past the chunk take the last
+// token's offset (valid rows) and are masked: -inf scores, zero V rows.
+template <int HT, int HPW>
+__device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
+                                              char (&s_v)[HPW][16 * kMfmaRowBytes])
+{
+    constexpr int D = 128;
+    constexpr int ESZ = 2;
+    const int G = a.group;
+
+    const int groups = a.num_kv_heads / HPW;
+    const int n = wg / groups;
+    const int kvg = wg - n * groups;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kvh = kvg * HPW + wave;
+    const int lane = tid & 63;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+
+    const int r = ld_uniform(a.req_idx + n);
+    const int t = ld_uniform(a.tile_idx + n);
+    const int pbeg = ld_uniform(a.indptr + r);
+    const int npages = ld_uniform(a.indptr + r + 1) - pbeg;
+    const int fpo = ld_uniform(a.fpo + r);
+    const int lpl = ld_uniform(a.lpl + r);
+    const int ps = a.page_size;
+    // the chunk's visible tokens, request-relative: pages [t*c, (t+1)*c)
+    const int64_t n_r = npages > 0 ? int64_t(npages - 1) * ps + lpl - fpo : 0;
+    const int64_t span = int64_t(a.pages_per_chunk) * ps;
+    const int64_t tok0 = max(int64_t(0), int64_t(t) * span - fpo);
+    const int64_t tok1 = min(n_r, int64_t(t + 1) * span - fpo);
+    const int ntok = tok1 > tok0 ? int(tok1 - tok0) : 0;
+
+    const int64_t page_bytes = a.page_stride * ESZ;
+    const int64_t tsb = a.token_stride * ESZ;
+    // page id and in-page slot of chunk token w0 + lane (clamped to the last)
+    auto load_pid = [&](int w0, uint32_t &slot_e) -> int32_t {
+        const int tk = min(w0 + lane, max(ntok - 1, 0));
+        const uint32_t slot = uint32_t(fpo + tok0 + tk);
+        const uint32_t pi = fastdiv_q(a.fd, slot);
+        slot_e = slot - pi * uint32_t(ps);
+        return a.indices[pbeg + min(int(pi), npages - 1)];
+    };
+
+    half8_t qb[HT][4];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int h = ht * 16 + col;
+        const _Float16 *qp = static_cast<const _Float16 *>(a.q) +
+                             q_row(a, r, kvh, G, min(h, G - 1)) * D + 8 * grp;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * kc);
+            qb[ht][kc] = h < G ? __builtin_bit_cast(half8_t, u) : half8_t{};
+        }
+    }
+
+    const char *kb = static_cast<const char *>(a.k) + int64_t(kvh) * a.head_stride * ESZ;
+    const char *vb = static_cast<const char *>(a.v) + int64_t(kvh) * a.head_stride * ESZ;
+
+    float m_run[HT], l_part[HT];
+    float4_t acc[HT][8];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        m_run[ht] = kNoMax;
+        l_part[ht] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    char *vt = s_v[wave];
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    const int tr_off = (4 * grp + (col >> 2)) * kMfmaRowBytes + 8 * (lane & 3);
+
+    // row offsets of the load cursor's 64-token window, split for ds_bpermute;
+    // the page ids of the window after it are loaded one window ahead
+    const int nsteps = (ntok + 15) / 16;
+    int32_t off_lo = 0, off_hi = 0;
+    uint32_t e_next = 0;
+    int32_t pid_next = 0;
+    auto set_window = [&](int32_t pid, uint32_t e) {
+        const int64_t off = int64_t(pid) * page_bytes + int64_t(e) * tsb;
+        off_lo = int32_t(uint32_t(uint64_t(off)));
+        off_hi = int32_t(uint32_t(uint64_t(off) >> 32));
+    };
+    if (ntok > 0) {
+        uint32_t e0;
+        const int32_t pid0 = load_pid(0, e0);
+        set_window(pid0, e0);
+        pid_next = load_pid(64, e_next);
+    }
+    auto gather = [&](int src) -> int64_t {         // offset of window token src
+        const uint32_t lo = uint32_t(__builtin_amdgcn_ds_bpermute(4 * src, off_lo));
+        const uint32_t hi = uint32_t(__builtin_amdgcn_ds_bpermute(4 * src, off_hi));
+        return int64_t((uint64_t(hi) << 32) | lo);
+    };
+
+    // loads run in step order, so the cursor moves to window s/4 at the
+    // first step of it; steps past the chunk reload the last one
+    auto load = [&](int s, uint4 (&kr)[4], uint4 (&vr)[4]) {
+        if (s < nsteps && s > 0 && (s & 3) == 0) {
+            set_window(pid_next, e_next);
+            // unconditional (clamped to the last token): a conditional load
+            // would be merged through a register copy that waits for it
+            pid_next = load_pid(16 * s + 64, e_next);
+        }
+        const int sl = (min(s, nsteps - 1) & 3) * 16;
+        const char *kp = kb + gather(sl + col) + 16 * grp;
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) kr[kc] = load_nt(kp + 64 * kc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vr[j] = load_nt(vb + gather(sl + grp + 4 * j) + 16 * col);
+    };
+
+    auto compute = [&](int s, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+        const int tt0 = 16 * s;                     // chunk token of the tile's first row
+        const bool edge = tt0 + 16 > ntok;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint4 v = vr[j];
+            if (edge) {
+                const bool ok = tt0 + grp + 4 * j < ntok;
+                v.x = ok ? v.x : 0u;
+                v.y = ok ? v.y : 0u;
+                v.z = ok ? v.z : 0u;
+                v.w = ok ? v.w : 0u;
+            }
+            *reinterpret_cast<uint4 *>(vt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = v;
+        }
+        float4_t sc[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            sc[ht] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(half8_t, kr[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
+        }
+        // the V rows written above are read back below by the same wave:
+        // LDS operations of a wave complete in order, so only the
+        // compiler must keep them in order
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        half4_t vtr[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+            vtr[dt] = __builtin_bit_cast(
+                half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                             (lds_short4 *)(vt + tr_off + 32 * dt)));
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            float x[4];
+            float mb = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = sc[ht][i] * a.scale_log2;
+                if (edge) v = tt0 + 4 * grp + i < ntok ? v : -INFINITY;
+                x[i] = v;
+                mb = fmaxf(mb, v);
+            }
+            mb = group_max4(mb);
+            const bool need = mb > m_run[ht] + kLazyMargin;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float m_new = need ? mb : m_run[ht];
+                const float alpha = fast_exp2(m_run[ht] - m_new);
+                m_run[ht] = m_new;
+                l_part[ht] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acc[ht][dt] *= alpha;
+            }
+            // P^T as an fp16 part and an fp16 remainder (the page variant's
+            // layout: k = 8*(l/16) + e, token 4*(l/16) + e%4)
+            half8_t pb;
+            float ls = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(x[i] - m_run[ht]);
+                const _Float16 ph = _Float16(p);
+                pb[i] = ph;
+                pb[4 + i] = _Float16(p - float(ph));
+                ls += p;
+            }
+            l_part[ht] += ls;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const half8_t va = __builtin_shufflevector(vtr[dt], vtr[dt], 0, 1, 2, 3, 0, 1,
+                                                           2, 3);
+                acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ht][dt], 0,
+                                                                     0, 0);
+            }
+        }
+    };
+
+    uint4 kbuf[kDepth][4], vbuf[kDepth][4];
+    int s = 0;
+    if (nsteps > 0) {
+#pragma unroll
+        for (int d = 0; d < kDepth - 1; ++d) load(s + d, kbuf[d], vbuf[d]);
+    }
+    const int rounds = (nsteps + kDepth - 1) / kDepth;
+    for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            load(s + kDepth - 1, kbuf[(u + kDepth - 1) % kDepth], vbuf[(u + kDepth - 1) % kDepth]);
+            if (s < nsteps) compute(s, kbuf[u], vbuf[u]);
+            ++s;
+        }
+    }
+
+    const int hq = a.num_qo_heads;
+    float *vrow = a.v_out + int64_t(n) * hq * D;
+    float *lrow = a.lse_out + int64_t(n) * hq;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const float l = group_sum4(l_part[ht]);
+        const int h = ht * 16 + col;
+        if (h >= G) continue;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int64_t qh = int64_t(kvh) * G + h;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const float4_t o = acc[ht][dt] * inv;
+            *reinterpret_cast<float4 *>(vrow + qh * D + 16 * dt + 4 * grp) =
+                make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (grp == 0) lrow[qh] = l > 0.f ? m_run[ht] + fast_log2(l) : -INFINITY;
+    }
+}
+template <int HT, int HPW>
+__global__ void __launch_bounds__(64 * HPW) partial_mfma_tok_kernel(PartialArgs a)
+{
+    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    mfma_tok_body<HT, HPW>(a, blockIdx.x, s_v);
+}
+
 template <typename T, int D, bool FUSED>
 KernelFn pick_token(int g)
 {
@@ -1323,7 +1568,7 @@ struct Choice {
     int spp_log2;
     int heads_per_wg;   // KV heads one workgroup covers
     int threads;
-    int kind;           // 0 token kernel, 1 page kernel, 2 MFMA kernel
+    int kind;           // 0 token kernel, 1 page kernel, 2 MFMA kernel, 3 MFMA kernel, any page
 };
 
 template <int HT>
@@ -1349,11 +1594,44 @@ KernelFn pick_mfma(int g, int hpw)
     }
 }
 
+template <int HT>
+KernelFn pick_mfma_tok_shape(int hpw)
+{
+    switch (hpw) {
+    case 8: return partial_mfma_tok_kernel<HT, 8>;
+    case 4: return partial_mfma_tok_kernel<HT, 4>;
+    case 2: return partial_mfma_tok_kernel<HT, 2>;
+    default: return partial_mfma_tok_kernel<HT, 1>;
+    }
+}
+
+KernelFn pick_mfma_tok(int g, int hpw)
+{
+    switch (g) {
+    case 8:
+    case 12:
+    case 16: return pick_mfma_tok_shape<1>(hpw);
+    case 24:
+    case 32: return pick_mfma_tok_shape<2>(hpw);
+    default: return nullptr;
+    }
+}
+
+// KV heads per MFMA workgroup: the largest power of two up to 8 that divides
+// the KV head count
+int mfma_heads_per_wg(int hkv)
+{
+    for (int h = 8; h > 1; h >>= 1)
+        if (hkv % h == 0) return h;
+    return 1;
+}
+
 // The MFMA kernel serves fp16 with D = 128, G in {8, 12, 16, 24, 32} and page
-// sizes that are a power-of-two multiple of 16 (two-launch mode); the page
-// kernel 256-byte rows, G in {4, 8, 16}, and page sizes that are a
+// sizes that are a power-of-two multiple of 16 (two-launch mode), its
+// any-page variant the same heads and groups at every other page size; the
+// page kernel 256-byte rows, G in {4, 8, 16}, and page sizes that are a
 // power-of-two multiple of its 64/G slots per step; every other shape takes
-// the token kernel.  All need 32-bit in-page offsets.
+// the token kernel.  The page kernels need 32-bit in-page offsets.
 Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
             bool allow_page = true, int hkv = 1, bool allow_mfma = true)
 {
@@ -1366,12 +1644,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
         if ((tiles & (tiles - 1)) == 0) {
             int lg = 0;
             while ((1 << lg) < tiles) ++lg;
-            int hpw = 1;
-            for (int h = 8; h > 1; h >>= 1)
-                if (hkv % h == 0) {
-                    hpw = h;
-                    break;
-                }
+            const int hpw = mfma_heads_per_wg(hkv);
             c.fn = pick_mfma(g, hpw);
             c.spp_log2 = lg;
             c.heads_per_wg = hpw;
@@ -1379,6 +1652,15 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
             c.kind = 2;
             return c;
         }
+    }
+    if (allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 && d == 128 &&
+        (g == 8 || g == 12 || g == 16 || g == 24 || g == 32)) {
+        const int hpw = mfma_heads_per_wg(hkv);
+        c.fn = pick_mfma_tok(g, hpw);
+        c.heads_per_wg = hpw;
+        c.threads = 64 * hpw;
+        c.kind = 3;
+        return c;
     }
     const bool row256 = (dtype == PD_DTYPE_FP16 && d == 128) || (dtype == PD_DTYPE_FP32 && d == 64);
     if (allow_page && row256 && (g == 4 || g == 8 || g == 16)) {
