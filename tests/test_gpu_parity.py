@@ -547,6 +547,26 @@ def test_cascade_stacked_queries_off_the_mfma_kernel(orc, choice):
         B.paged_decode_set_kernel_choice(0)
 
 
+@pytest.mark.parametrize("ps", [5, 48, 1])
+def test_cascade_on_the_any_page_mfma_kernel(orc, ps):
+    """Page sizes the page-tiled MFMA kernel cannot take: the stacked level's
+    groups (S*G from 8 to 16 here) run on the any-page MFMA kernel, one launch
+    per table, reading the members' queries through the member list; the
+    per-request level (G = 4) runs on the page or token kernel.  The output
+    and every partial row of both levels against the oracle."""
+    w = _mixed_batch(95 + ps, 4, hq=32, ps=ps, prefix_pages=max(40, 640 // ps))
+    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, 128, 16, ps, 8 * 128) == 3
+    cas = _cascade(w, min_shared_pages=16)
+    say("case cascade any-page ps=%d plan=%s" % (ps, cas.plan_summary()))
+    assert cas.plan_summary()["cascade"]
+    q, k, v = to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool)
+    out, lse = cas.run(q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    ref_v, ref_l = _oracle_flat(orc, w)
+    check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "cascade")
+    _check_cascade_partials(orc, w, cas)
+
+
 def _mixed_batch(seed, members, hq=32, hkv=8, prefix_pages=40, ps=16):
     """A batch in which `members` requests share a prefix of pages, one more
     request holds the same pages but starts mid-page (so detection leaves it
