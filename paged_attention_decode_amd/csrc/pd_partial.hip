@@ -1480,6 +1480,13 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
             if (s < nsteps) compute(s, kbuf[u], vbuf[u]);
             ++s;
         }
+        // the workgroup's KV heads share every token's row of the pool: in
+        // lockstep their loads of a step meet in the same DRAM pages (every
+        // wave of the workgroup has the same chunk, so the same round count)
+        if constexpr (kLockstep > 0 && HPW > 1) {
+            constexpr int every = kLockstep > 0 ? kLockstep : 1;
+            if (rd % every == every - 1) __builtin_amdgcn_s_barrier();
+        }
     }
 
     const int hq = a.num_qo_heads;
