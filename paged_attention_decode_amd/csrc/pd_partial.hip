@@ -980,14 +980,25 @@ constexpr int token_rows_per_step()
 // layout puts the same head in lane l.  So a lane owns one head's running
 // max and sum and 32 of its output dims, and a rescale is a per-lane scalar.
 //
-// K rows go straight from memory into the A operand (lane l: token l%16, 16
-// bytes at dims 8*(l/16) + 32*kc).  V^T's A operand (4 tokens of one dim per
-// lane) is read from an LDS copy of the V tile with the gfx950 transpose
-// read ds_read_b64_tr_b16: in each 16-lane group, lanes 4r..4r+3 name 4
+// K and V are loaded by rows: each load instruction reads 4 whole 256-byte
+// rows (16 lanes per row), and the rows go to the wave's LDS tiles.  K's A
+// operand (lane l: token l%16, 16 bytes at dims 8*(l/16) + 32*kc) is read
+// back with ds_read_b128.  Loading it straight into the operand layout reads
+// 16 rows x 64 bytes per instruction, twice the cache lines per request:
+// measured on MI355X at G = 8 that took the long-context partial from 65.6
+// to 67.1 us, and the any-page variant at page size 1 from 68.7 to 72.5 us
+// (PD_MFMA_K_LDS=0 builds that form).  V^T's A operand (4 tokens of one dim
+// per lane) is read from the V tile with the gfx950 transpose read
+// ds_read_b64_tr_b16: in each 16-lane group, lanes 4r..4r+3 name 4
 // consecutive halves each (together row r of a 4 x 16 tile) and lane c
-// receives column c.  Each wave has its own LDS tile, rows padded by 16
+// receives column c.  Each wave has its own LDS tiles, rows padded by 16
 // bytes against bank conflicts.
-constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per V row of the tile
+constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per row of a tile
+#ifndef PD_MFMA_K_LDS
+#define PD_MFMA_K_LDS 1
+#endif
+constexpr bool kKviaLds = PD_MFMA_K_LDS != 0;
+constexpr int kMfmaTileBytes = (kKviaLds ? 32 : 16) * kMfmaRowBytes;   // V tile, then K tile
 
 // The group size G = a.group is a run-time value up to 16 * HT (heads past
 // G are zero columns of the 16-head tiles), so one instantiation serves
@@ -995,7 +1006,7 @@ constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per V row of the til
 // different groups.
 template <int HT, int HPW>
 __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
-                                          char (&s_v)[HPW][16 * kMfmaRowBytes])
+                                          char (&s_v)[HPW][kMfmaTileBytes])
 {
     constexpr int D = 128;
     constexpr int ESZ = 2;
@@ -1092,7 +1103,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
             const int soff = int(sub * tile_bytes);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * j, soff, kLoadNT));
+                kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rk, kKviaLds ? v_off + 4 * j * tsb : k_off + 64 * j, soff, kLoadNT));
                 vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + 4 * j * tsb, soff, kLoadNT));
             }
         };
@@ -1118,6 +1130,23 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
                 }
                 *reinterpret_cast<uint4 *>(vt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = v;
             }
+            // K operand fragments: lane l takes token l % 16 at dims
+            // 8*(l/16) + 32*kc, straight from the load or through the LDS
+            // copy of the tile (written in the V rows' layout)
+            uint4 kf[4];
+            if constexpr (kKviaLds) {
+                char *kt = vt + 16 * kMfmaRowBytes;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<uint4 *>(kt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = kr[j];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc)
+                    kf[kc] = *reinterpret_cast<const uint4 *>(kt + col * kMfmaRowBytes + 16 * grp + 64 * kc);
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < 4; ++kc) kf[kc] = kr[kc];
+            }
             // scores S^T = K . Q^T, per 16-head tile
             float4_t sc[HT];
 #pragma unroll
@@ -1126,7 +1155,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
 #pragma unroll
                 for (int kc = 0; kc < 4; ++kc)
                     sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(half8_t, kr[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
+                        __builtin_bit_cast(half8_t, kf[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
             }
             // the V rows written above are read back below by the same wave:
             // LDS operations of a wave complete in order, so only the
@@ -1234,7 +1263,7 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
 template <int HT, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
 {
-    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    __shared__ __align__(16) char s_v[HPW][kMfmaTileBytes];
     mfma_body<HT, HPW>(a, blockIdx.x, s_v);
 }
 
@@ -1255,7 +1284,7 @@ struct PartialTables {
 template <int HT, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTables tabs)
 {
-    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    __shared__ __align__(16) char s_v[HPW][kMfmaTileBytes];
     const int wg = blockIdx.x;
     int i = 0;
     while (i < tabs.count - 1 && wg >= tabs.wg_end[i]) ++i;
@@ -1271,13 +1300,13 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTab
 // consecutive tokens of its chunk in a register (lane t: token w0 + t,
 // from the page id and in-page slot of the PR #984 page-table walk,
 // fast-divided by the page size) and gathers a tile's offsets from it with
-// ds_bpermute: lane l loads K of token l % 16 and V rows l / 16 + 4j, as
-// the page variant does within a page.  The products, the softmax and the
-// epilogue are the page variant's.  Tokens past the chunk take the last
+// ds_bpermute: lane l loads the K and V rows of tokens l / 16 + 4j, as the
+// page variant does within a page (the row offsets of 4 tokens per lane and
+// step).  The products, the softmax and the epilogue are the page variant's.  Tokens past the chunk take the last
 // token's offset (valid rows) and are masked: -inf scores, zero V rows.
 template <int HT, int HPW>
 __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
-                                              char (&s_v)[HPW][16 * kMfmaRowBytes])
+                                              char (&s_v)[HPW][kMfmaTileBytes])
 {
     constexpr int D = 128;
     constexpr int ESZ = 2;
@@ -1381,11 +1410,21 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
             pid_next = load_pid(16 * s + 64, e_next);
         }
         const int sl = (min(s, nsteps - 1) & 3) * 16;
-        const char *kp = kb + gather(sl + col) + 16 * grp;
+        if constexpr (kKviaLds) {
+            // K and V rows of tokens grp + 4j, 256 contiguous bytes per 16 lanes
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) kr[kc] = load_nt(kp + 64 * kc);
+            for (int j = 0; j < 4; ++j) {
+                const int64_t o = gather(sl + grp + 4 * j) + 16 * col;
+                kr[j] = load_nt(kb + o);
+                vr[j] = load_nt(vb + o);
+            }
+        } else {
+            const char *kp = kb + gather(sl + col) + 16 * grp;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vr[j] = load_nt(vb + gather(sl + grp + 4 * j) + 16 * col);
+            for (int kc = 0; kc < 4; ++kc) kr[kc] = load_nt(kp + 64 * kc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vr[j] = load_nt(vb + gather(sl + grp + 4 * j) + 16 * col);
+        }
     };
 
     auto compute = [&](int s, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
@@ -1403,6 +1442,22 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
             }
             *reinterpret_cast<uint4 *>(vt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = v;
         }
+        // K operand fragments (lane l: token l % 16, dims 8*(l/16) + 32*kc),
+        // through the LDS copy of the tile when K was loaded by rows
+        uint4 kf[4];
+        if constexpr (kKviaLds) {
+            char *kt = vt + 16 * kMfmaRowBytes;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint4 *>(kt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = kr[j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+                kf[kc] = *reinterpret_cast<const uint4 *>(kt + col * kMfmaRowBytes + 16 * grp + 64 * kc);
+        } else {
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc) kf[kc] = kr[kc];
+        }
         float4_t sc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
@@ -1410,7 +1465,7 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc)
                 sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    __builtin_bit_cast(half8_t, kr[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
+                    __builtin_bit_cast(half8_t, kf[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
         }
         // the V rows written above are read back below by the same wave:
         // LDS operations of a wave complete in order, so only the
@@ -1511,7 +1566,7 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
 template <int HT, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_tok_kernel(PartialArgs a)
 {
-    __shared__ __align__(16) char s_v[HPW][16 * kMfmaRowBytes];
+    __shared__ __align__(16) char s_v[HPW][kMfmaTileBytes];
     mfma_tok_body<HT, HPW>(a, blockIdx.x, s_v);
 }
 
