@@ -1647,6 +1647,9 @@ KernelFn pick_mfma_shape(int hpw)
 KernelFn pick_mfma(int g, int hpw)
 {
     switch (g) {
+    case 1:
+    case 2:
+    case 4:
     case 8:
     case 12:
     case 16: return pick_mfma_shape<1>(hpw);
@@ -1670,6 +1673,9 @@ KernelFn pick_mfma_tok_shape(int hpw)
 KernelFn pick_mfma_tok(int g, int hpw)
 {
     switch (g) {
+    case 1:
+    case 2:
+    case 4:
     case 8:
     case 12:
     case 16: return pick_mfma_tok_shape<1>(hpw);
@@ -1688,19 +1694,23 @@ int mfma_heads_per_wg(int hkv)
     return 1;
 }
 
-// The MFMA kernel serves fp16 with D = 128, G in {8, 12, 16, 24, 32} and page
-// sizes that are a power-of-two multiple of 16 (two-launch mode), its
-// any-page variant the same heads and groups at every other page size; the
-// page kernel 256-byte rows, G in {4, 8, 16}, and page sizes that are a
-// power-of-two multiple of its 64/G slots per step; every other shape takes
-// the token kernel.  The page kernels need 32-bit in-page offsets.
+// In the two-launch mode, fp16 with D = 128 runs on the MFMA kernels for
+// every group they take (1, 2, 4, 8, 12, 16, 24, 32; groups under 16 as
+// zero-padded 16-head tiles): the page-tiled one at page sizes that are a
+// power-of-two multiple of 16, the any-page one at every other.  The page
+// kernel takes 256-byte rows, G in {4, 8, 16} and page sizes that are a
+// power-of-two multiple of its 64/G slots per step, for the shapes off the
+// MFMA kernels (fp32 with D = 64, the fused launch, the VALU-only choice).
+// Every other shape takes the token kernel.  The page-tiled kernels need
+// 32-bit in-page offsets.
 Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
             bool allow_page = true, int hkv = 1, bool allow_mfma = true)
 {
     Choice c{nullptr, 0, 1, kThreads, 0};
     const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
-    if (allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 && d == 128 &&
-        (g == 8 || g == 12 || g == 16 || g == 24 || g == 32) && page_size % 16 == 0 &&
+    const bool mfma_ok = allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 &&
+                         d == 128 && pick_mfma(g, 1) != nullptr;
+    if (mfma_ok && page_size % 16 == 0 &&
         token_stride * esz * page_size < (int64_t(1) << 31)) {
         const int tiles = page_size / 16;
         if ((tiles & (tiles - 1)) == 0) {
@@ -1715,17 +1725,8 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
             return c;
         }
     }
-    if (allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 && d == 128 &&
-        (g == 8 || g == 12 || g == 16 || g == 24 || g == 32)) {
-        const int hpw = mfma_heads_per_wg(hkv);
-        c.fn = pick_mfma_tok(g, hpw);
-        c.heads_per_wg = hpw;
-        c.threads = 64 * hpw;
-        c.kind = 3;
-        return c;
-    }
     const bool row256 = (dtype == PD_DTYPE_FP16 && d == 128) || (dtype == PD_DTYPE_FP32 && d == 64);
-    if (allow_page && row256 && (g == 4 || g == 8 || g == 16)) {
+    if (allow_page && row256 && (g == 4 || g == 8 || g == 16) && !mfma_ok) {
         const int sps = 64 / g;
         if (page_size % sps == 0) {
             const int spp = page_size / sps;
@@ -1742,6 +1743,14 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
                 return c;
             }
         }
+    }
+    if (mfma_ok) {
+        const int hpw = mfma_heads_per_wg(hkv);
+        c.fn = pick_mfma_tok(g, hpw);
+        c.heads_per_wg = hpw;
+        c.threads = 64 * hpw;
+        c.kind = 3;
+        return c;
     }
     if (dtype == PD_DTYPE_FP16) {
         if (d == 64) c.fn = fused ? pick_token<_Float16, 64, true>(g) : pick_token<_Float16, 64, false>(g);

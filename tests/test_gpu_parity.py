@@ -834,7 +834,7 @@ def test_page_kernel_shapes_ragged(orc, g, ps, mode):
     run_flat(orc, w, target=48, fused=mode["fused"])
 
 
-@pytest.mark.parametrize("g", [8, 12, 16, 24, 32])
+@pytest.mark.parametrize("g", [1, 2, 8, 12, 16, 24, 32])
 @pytest.mark.parametrize("ps,hkv", [(16, 8), (32, 2), (64, 1)])
 def test_mfma_kernel_ragged(orc, g, ps, hkv):
     """The MFMA kernel over ragged windows, mid-page starts, partial last
@@ -848,7 +848,7 @@ def test_mfma_kernel_ragged(orc, g, ps, hkv):
         run_flat(orc, w, target=target, fixed=fixed)
 
 
-@pytest.mark.parametrize("g", [8, 12, 24, 32])
+@pytest.mark.parametrize("g", [1, 4, 8, 12, 24, 32])
 @pytest.mark.parametrize("ps,hkv", [(1, 2), (3, 8), (48, 1), (4, 4)])
 def test_mfma_any_page_kernel_ragged(orc, g, ps, hkv):
     """The any-page MFMA kernel, at page sizes the page-tiled one cannot take
@@ -866,12 +866,14 @@ def test_mfma_any_page_kernel_ragged(orc, g, ps, hkv):
         run_flat(orc, w, target=target, fixed=fixed)
 
 
-@pytest.mark.parametrize("g,ps", [(12, 1), (16, 5), (8, 16), (4, 16), (2, 3)])
-def test_pool_pages_past_4gib(orc, g, ps):
+@pytest.mark.parametrize("g,ps,choice", [(12, 1, 0), (16, 5, 0), (8, 16, 0), (4, 16, 2), (2, 3, 0),
+                                         (2, 3, 2)])
+def test_pool_pages_past_4gib(orc, g, ps, choice):
     """Every visible page lies past byte 2^32 of the K and V pools (the
     pools are 5 GiB, NaN everywhere but the copied pages): each kernel forms
-    64-bit page offsets (any-page MFMA at page sizes 1 and 5, page-tiled
-    MFMA, page and token kernels).  A truncated offset reads NaN."""
+    64-bit page offsets (any-page MFMA at page sizes 1, 3 and 5, page-tiled
+    MFMA, the page kernel, and the token kernel with the MFMA kernels switched
+    off).  A truncated offset reads NaN."""
     hkv, d = 2, 128
     w = workloads.random_geometry(780 + g + ps, batch=4, page_size=ps, max_len=1200,
                                   num_qo_heads=g * hkv, num_kv_heads=hkv, p_empty=0.0,
@@ -880,16 +882,18 @@ def test_pool_pages_past_4gib(orc, g, ps):
     page_bytes = ps * hkv * d * 2
     shift = -(-(5 << 30) // page_bytes) - pages
     assert shift * page_bytes > (1 << 32)
-    kind = B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, d, g, ps, hkv * d)
-    say("case past-4GiB g=%d ps=%d kernel %s shift=%d pages" % (g, ps, KIND[kind], shift))
     tables = [np.where(t >= 0, t + shift, -1).astype(np.int32) for t in w.block_tables]
     csr = B.paged_csr_build(tables, w.logical_start, w.written_len, ps, shift + pages)
-    dec = PD.PagedDecode(csr, page_size=ps, num_pool_pages=shift + pages,
-                         num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d, target_wgs=64)
     ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len, ps)
     ref_v, ref_l = orc.attention(w.q, w.k_pool, w.v_pool, ocsr, ps, w.sm_scale,
                                  nthreads=NTHREADS)
+    kbig = vbig = None
+    B.paged_decode_set_kernel_choice(choice)
     try:
+        kind = B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, d, g, ps, hkv * d)
+        say("case past-4GiB g=%d ps=%d kernel %s shift=%d pages" % (g, ps, KIND[kind], shift))
+        dec = PD.PagedDecode(csr, page_size=ps, num_pool_pages=shift + pages,
+                             num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d, target_wgs=64)
         kbig = torch.full((shift + pages, ps, hkv, d), float("nan"), dtype=torch.float16,
                           device=DEV)
         vbig = torch.full_like(kbig, float("nan"))
@@ -899,6 +903,7 @@ def test_pool_pages_past_4gib(orc, g, ps):
         torch.cuda.synchronize()
         check_close(out.cpu().numpy(), lse.cpu().numpy(), ref_v, ref_l, w.dtype, "past 4 GiB")
     finally:
+        B.paged_decode_set_kernel_choice(0)
         kbig = vbig = None
         torch.cuda.empty_cache()
 
@@ -971,8 +976,8 @@ def test_scores_ramp_rescale_every_step(orc, g, ps, mode):
 
 def test_kernel_choice():
     kk = B.paged_decode_kernel_kind
-    assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1024) == 1
-    assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 2    # MFMA from G = 8
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1024) == 2    # fp16, D = 128: MFMA for every G
+    assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 2
     assert kk(B.PD_DTYPE_FP16, 128, 12, 32, 1024) == 2
     assert kk(B.PD_DTYPE_FP16, 128, 16, 16, 1024) == 2
     assert kk(B.PD_DTYPE_FP16, 128, 32, 64, 1024) == 2
@@ -986,19 +991,27 @@ def test_kernel_choice():
     assert kk(B.PD_DTYPE_FP32, 64, 4, 16, 128) == 1
     B.paged_decode_set_kernel_choice(2)
     try:
+        assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1024) == 1
         assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1024) == 1
         assert kk(B.PD_DTYPE_FP16, 128, 12, 16, 1024) == 0
         assert kk(B.PD_DTYPE_FP16, 128, 16, 4, 1024) == 1
         assert kk(B.PD_DTYPE_FP16, 128, 12, 1, 128) == 0
+        assert kk(B.PD_DTYPE_FP16, 128, 1, 16, 1024) == 0
+        assert kk(B.PD_DTYPE_FP16, 128, 4, 1, 128) == 0
         with pytest.raises(B.PagedDecodeError):            # G = 32 needs an MFMA kernel
             kk(B.PD_DTYPE_FP16, 128, 32, 1, 128)
     finally:
         B.paged_decode_set_kernel_choice(0)
-    assert kk(B.PD_DTYPE_FP16, 128, 4, 8, 1024) == 0     # page smaller than a step
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 8, 1024) == 3     # page smaller than a step
     assert kk(B.PD_DTYPE_FP16, 128, 12, 1, 128) == 3     # token-sparse page_size 1
-    assert kk(B.PD_DTYPE_FP16, 128, 2, 1, 128) == 0      # below the MFMA kernels' groups
+    assert kk(B.PD_DTYPE_FP16, 128, 1, 16, 1024) == 2    # G = 1 and 2: padded MFMA tiles
+    assert kk(B.PD_DTYPE_FP16, 128, 2, 1, 128) == 3
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 1, 128) == 3
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1 << 27) == 3  # in-page offsets past 2^31 bytes
     assert kk(B.PD_DTYPE_FP16, 64, 4, 16, 512) == 0      # 128-byte rows
-    assert kk(B.PD_DTYPE_FP16, 128, 4, 48, 1024) == 0    # 3 steps per page
+    assert kk(B.PD_DTYPE_FP16, 64, 1, 1, 64) == 0
+    assert kk(B.PD_DTYPE_FP32, 128, 1, 16, 1024) == 0
+    assert kk(B.PD_DTYPE_FP16, 128, 4, 48, 1024) == 3    # 3 steps per page
 
 
 def test_empty_requests_do_not_poison_neighbours(orc):
