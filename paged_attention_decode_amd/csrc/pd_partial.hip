@@ -65,10 +65,16 @@ constexpr int kPageWindow = 1024;     // token kernel: page ids staged in LDS pe
 #define PD_PIPELINE_DEPTH 2
 #endif
 constexpr int kDepth = PD_PIPELINE_DEPTH;   // page kernel: steps per wave in the load pipeline
+// rounds of the load pipeline between the workgroup barriers that keep its
+// waves (one per KV head) in lockstep, 0 for none.  Measured on MI355X with
+// the MFMA kernel on the long-context geometry: every 2 or 3 rounds 63.96-
+// 64.08 us, every round 64.19-64.26, every 4 rounds 64.10-64.23, never
+// 65.47; G = 4 at page size 1 on the any-page kernel 68.07-68.14 against
+// 68.47-68.70 every round.
 #ifndef PD_LOCKSTEP_ROUNDS
-#define PD_LOCKSTEP_ROUNDS 1
+#define PD_LOCKSTEP_ROUNDS 2
 #endif
-constexpr int kLockstep = PD_LOCKSTEP_ROUNDS;   // page kernel: rounds between wave barriers (0: none)
+constexpr int kLockstep = PD_LOCKSTEP_ROUNDS;
 constexpr float kLazyMargin = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr float kNoMax = -1e30f;      // finite "no score yet" running max
 constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer descriptor dword 3 (32-bit data)
