@@ -643,7 +643,8 @@ def mla(args, torch, B, PD, workloads, dev):
 
 def block_sparse(args, torch, B, PD, workloads, dev):
     """Block-sparse decode (a selection of KV blocks per KV head): the
-    block-granular page table timed beside the token-exact one."""
+    block-granular page table (16-row pages, the default) timed beside the
+    token-exact one and the one-page-per-block one."""
     import oracle
     w = workloads.block_sparse_fp16()
     b, hkv, cap, d = w.k_dense.shape
@@ -652,11 +653,13 @@ def block_sparse(args, torch, B, PD, workloads, dev):
     vd = torch.from_numpy(w.v_dense).to(dev)
     q = torch.from_numpy(w.q).to(dev)
     ids = torch.from_numpy(w.block_ids).to(dev)
-    runners = {exact: PD.BlockSparseDecode(kd, vd, num_qo_heads=hq, block_size=w.block_size,
-                                           blocks_per_request=w.block_ids.shape[1],
-                                           kv_len=w.kv_len, token_exact=exact,
-                                           target_wgs=args.target_wgs, device=dev)
-               for exact in (False, True)}
+    arms = {False: dict(token_exact=False), True: dict(token_exact=True),
+            "block": dict(token_exact=False, page_size=w.block_size)}
+    runners = {k: PD.BlockSparseDecode(kd, vd, num_qo_heads=hq, block_size=w.block_size,
+                                       blocks_per_request=w.block_ids.shape[1],
+                                       kv_len=w.kv_len, target_wgs=args.target_wgs, device=dev,
+                                       **kw)
+               for k, kw in arms.items()}
     # parity of both granularities against attention over the selected positions
     g = hq // hkv
     t0 = time.time()
@@ -699,8 +702,10 @@ def block_sparse(args, torch, B, PD, workloads, dev):
 
     t_block = timed(lambda: runners[False].run(q, ids, w.sm_scale))
     t_token = timed(lambda: runners[True].run(q, ids, w.sm_scale))
+    t_whole = timed(lambda: runners["block"].run(q, ids, w.sm_scale))
     g_block = PD.graph_time(lambda i: runners[False].run(q, ids, w.sm_scale), args.steps)
     g_token = PD.graph_time(lambda i: runners[True].run(q, ids, w.sm_scale), args.steps)
+    g_whole = PD.graph_time(lambda i: runners["block"].run(q, ids, w.sm_scale), args.steps)
     sweep = None
     if args.sweep_chunks:
         sweep = {}
@@ -710,8 +715,8 @@ def block_sparse(args, torch, B, PD, workloads, dev):
                                          runners[exact].dec.info.pages_per_chunk):
                 r = PD.BlockSparseDecode(kd, vd, num_qo_heads=hq, block_size=w.block_size,
                                          blocks_per_request=w.block_ids.shape[1],
-                                         kv_len=w.kv_len, token_exact=exact,
-                                         fixed_pages_per_chunk=c, device=dev)
+                                         kv_len=w.kv_len, fixed_pages_per_chunk=c, device=dev,
+                                         **arms[exact])
                 out, lse = r.run(q, ids, w.sm_scale)
                 torch.cuda.synchronize()
                 if not (float(np.max(np.abs(out.cpu().numpy() - ref_v))) <= 2e-3 and
@@ -743,10 +748,13 @@ def block_sparse(args, torch, B, PD, workloads, dev):
         "step_us": round(t_block * 1e6, 2),
         "block_vs_token": {"block_granular_step_us": round(t_block * 1e6, 2),
                            "token_exact_step_us": round(t_token * 1e6, 2),
+                           "one_page_per_block_step_us": round(t_whole * 1e6, 2),
                            "speedup": round(t_token / t_block, 3),
                            "graph_block_granular_step_us": round(g_block * 1e6, 2),
                            "graph_token_exact_step_us": round(g_token * 1e6, 2),
-                           "token_exact_plan": runners[True].plan_summary()},
+                           "graph_one_page_per_block_step_us": round(g_whole * 1e6, 2),
+                           "token_exact_plan": runners[True].plan_summary(),
+                           "one_page_per_block_plan": runners["block"].plan_summary()},
         "parity": {"max_abs_v": worst[0], "max_abs_lse2": worst[1], "tol_v": 2e-3,
                    "tol_lse2": 1e-3, "ok": True},
         # three launches per step (block-id expansion, partial, merge) over K/V

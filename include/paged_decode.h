@@ -444,31 +444,36 @@ int paged_cascade_merge_states(const float *v0, const float *lse0, int32_t n0,
  * tail[r] in [1, block_size] positions.
  *
  * paged_sparse_csr (HOST): the page table's shape, which needs no selection
- *   values.  token_exact = 1: page_size 1, request r holds (blocks-1)*block_size
- *   + tail[r] one-token pages (last_page_len 1).  token_exact = 0
- *   (block-granular): page_size = block_size, request r holds `blocks` pages,
- *   last_page_len = tail[r].  first_page_offset 0.  Out: indptr [R+1],
- *   last_page_len [R], first_page_offset [R].
+ *   values.  The table names every selected block by s = block_size /
+ *   page_size pages of page_size rows (page_size must divide block_size):
+ *   page_size = block_size is the doc's block-granular table (one page per
+ *   block), page_size = 1 the token-exact one, and sizes between read the
+ *   same whole blocks while letting the plan cut chunks smaller than a block.
+ *   Request r holds (blocks-1)*s + ceil(tail[r] / page_size) pages, the last
+ *   holding tail[r] - (that count - 1)*page_size positions (last_page_len).
+ *   first_page_offset 0.  Out: indptr [R+1], last_page_len [R],
+ *   first_page_offset [R].  A page_size that does not divide block_size, or a
+ *   tail outside [1, block_size], returns PD_E_ARG.
  *
  * paged_sparse_expand_blocks (DEVICE arrays, caller's stream): one pass over
  *   the selection.  Block j of request r (block_ids [R, blocks], int32)
  *   becomes rows base[r] + id*span + t for t < span, written from
- *   rows[out_indptr[r] + j*span]; the last block writes only tail[r] rows.
- *   span = block_size gives token rows (token_exact tables, the pool read as
- *   one-token pages); span = 1 gives page ids of block-granular tables (a pool
- *   whose rows are blocks, row of block j of request r = base[r] + j).
+ *   rows[out_indptr[r] + j*span]; the last block writes only final_rows[r]
+ *   rows.  span = block_size / page_size (pages per block) over a pool read
+ *   in pages of page_size rows, whose page of block j, piece t, of request r
+ *   is base[r] + j*span + t; final_rows[r] = ceil(tail[r] / page_size).
  *   Block ids must lie in [0, num_blocks); an id outside is clamped into it,
  *   so the rows never leave the request's region of the pool.
- *   base, tail [R]; out_indptr [R+1] (the table's indptr); rows
+ *   base, final_rows [R]; out_indptr [R+1] (the table's indptr); rows
  *   [out_indptr[R]].
  * ---------------------------------------------------------------------- */
 int paged_sparse_csr(int32_t num_requests, int32_t blocks_per_request, int32_t block_size,
-                     int32_t token_exact, const int32_t *tail, int32_t *indptr,
+                     int32_t page_size, const int32_t *tail, int32_t *indptr,
                      int32_t *last_page_len, int32_t *first_page_offset);
 
 int paged_sparse_expand_blocks(const int32_t *block_ids, int32_t num_requests,
                                int32_t blocks_per_request, const int32_t *base, int32_t span,
-                               const int32_t *tail, const int32_t *out_indptr,
+                               const int32_t *final_rows, const int32_t *out_indptr,
                                int32_t num_blocks, int32_t *rows, void *stream);
 
 /* ------------------------------------------------------------------------

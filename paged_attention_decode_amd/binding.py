@@ -424,23 +424,23 @@ def paged_cascade_merge_states(v0, lse0, n0, l0_desc, v1, lse1, o_indptr1, batch
                                              _stream(stream)))
 
 
-def paged_sparse_csr(blocks_per_request, block_size, tail, token_exact):
+def paged_sparse_csr(blocks_per_request, block_size, tail, page_size):
     """Returns dict(indptr, last_page_len, first_page_offset) of a selection's
-    page table (host arrays)."""
+    page table in pages of page_size rows (host arrays)."""
     tail = _host_i32(tail)
     r = tail.size
     indptr = np.zeros(r + 1, np.int32)
     lpl = np.zeros(r, np.int32)
     fpo = np.zeros(r, np.int32)
-    _check(load().paged_sparse_csr(r, blocks_per_request, block_size, 1 if token_exact else 0,
+    _check(load().paged_sparse_csr(r, blocks_per_request, block_size, page_size,
                                    _hp(tail), _hp(indptr), _hp(lpl), _hp(fpo)))
     return dict(indptr=indptr, last_page_len=lpl, first_page_offset=fpo)
 
 
-def paged_sparse_expand_blocks(block_ids, num_requests, blocks_per_request, base, span, tail,
-                               out_indptr, num_blocks, rows, stream=None):
+def paged_sparse_expand_blocks(block_ids, num_requests, blocks_per_request, base, span,
+                               final_rows, out_indptr, num_blocks, rows, stream=None):
     _check(load().paged_sparse_expand_blocks(_dev(block_ids), num_requests, blocks_per_request,
-                                             _dev(base), span, _dev(tail), _dev(out_indptr),
+                                             _dev(base), span, _dev(final_rows), _dev(out_indptr),
                                              num_blocks, _dev(rows), _stream(stream)))
 
 

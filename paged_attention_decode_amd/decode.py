@@ -438,9 +438,13 @@ class BlockSparseDecode:
     lists `blocks_per_request` block ids, its partially written final block
     last; that block holds kv_len - final*block_size positions.
 
-    token_exact=False (block-granular): the allocation is read as a pool of
-    Cap/block_size-row blocks (page_size = block_size, needs Cap % block_size
-    == 0) and the block ids, offset by the request's region, are the page ids.
+    token_exact=False (block-granular, needs Cap % block_size == 0): the
+    allocation is read as a pool of pages of page_size rows, page_size
+    dividing block_size, and each selected block becomes its block_size /
+    page_size pages -- the same whole blocks are read.  page_size =
+    block_size is one page per block; the default, 16 where it divides the
+    block (else the block), lets the plan cut a small selection into chunks
+    smaller than a block, so that it spreads over the GPU.
     token_exact=True: the allocation is read as one-token pages and the block
     ids are expanded into token rows.  Either way the ids are a device value
     turned into the table's rows by one device pass per step; the table's
@@ -449,7 +453,8 @@ class BlockSparseDecode:
 
     def __init__(self, k_dense, v_dense, *, num_qo_heads: int, block_size: int,
                  blocks_per_request: int, kv_len, token_exact: bool = False,
-                 target_wgs: int = 0, fixed_pages_per_chunk: int = 0, device="cuda"):
+                 page_size: int = 0, target_wgs: int = 0, fixed_pages_per_chunk: int = 0,
+                 device="cuda"):
         b, hkv, cap, d = k_dense.shape
         if v_dense.shape != k_dense.shape or not k_dense.is_contiguous() or \
                 not v_dense.is_contiguous():
@@ -466,20 +471,22 @@ class BlockSparseDecode:
         self.blocks = blocks_per_request
         self.block_size = block_size
         self.token_exact = token_exact
+        if token_exact:
+            ps = 1
+        else:
+            ps = page_size or (16 if block_size % 16 == 0 else block_size)
+            if ps < 1 or block_size % ps:
+                raise ValueError("page_size must divide block_size")
         final = (kv_len - 1) // block_size
         tail = np.repeat((kv_len - final * block_size).astype(np.int32), hkv)
-        csr = B.paged_sparse_csr(blocks_per_request, block_size, tail, token_exact)
+        csr = B.paged_sparse_csr(blocks_per_request, block_size, tail, ps)
         nnz = int(csr["indptr"][-1])
-        if token_exact:
-            self.page_size, self.span = 1, block_size
-            self.k_pool = k_dense.view(b * hkv * cap, 1, 1, d)
-            self.v_pool = v_dense.view(b * hkv * cap, 1, 1, d)
-            base = np.arange(self.requests, dtype=np.int64) * cap
-        else:
-            self.page_size, self.span = block_size, 1
-            self.k_pool = k_dense.view(b * hkv * cap // block_size, block_size, 1, d)
-            self.v_pool = v_dense.view(b * hkv * cap // block_size, block_size, 1, d)
-            base = np.arange(self.requests, dtype=np.int64) * (cap // block_size)
+        self.page_size, self.span = ps, block_size // ps
+        self.k_pool = k_dense.view(b * hkv * cap // ps, ps, 1, d)
+        self.v_pool = v_dense.view(b * hkv * cap // ps, ps, 1, d)
+        base = np.arange(self.requests, dtype=np.int64) * (cap // ps)
+        if int(base[-1]) + cap // ps > np.iinfo(np.int32).max:
+            raise ValueError("the allocation has more pages than int32 page ids can name")
         self.num_blocks = cap // block_size
         # the table's rows are written on the device every step; placeholder
         # rows (valid pool rows) let the host check the table's shape now
@@ -491,7 +498,8 @@ class BlockSparseDecode:
                                fixed_pages_per_chunk=fixed_pages_per_chunk, device=device)
         dev = self.dec.device
         self.d_base = _dev_i32(base.astype(np.int32), dev)
-        self.d_tail = _dev_i32(tail, dev)
+        # pages of the final block that hold its written positions
+        self.d_final = _dev_i32(((tail + ps - 1) // ps).astype(np.int32), dev)
 
     def plan_summary(self) -> dict:
         return dict(self.dec.plan_summary(), page_size=self.page_size,
@@ -503,7 +511,7 @@ class BlockSparseDecode:
         if block_ids.dtype != torch.int32 or block_ids.numel() != self.requests * self.blocks:
             raise ValueError("block_ids must be int32 [B*Hkv, blocks_per_request]")
         B.paged_sparse_expand_blocks(block_ids, self.requests, self.blocks, self.d_base,
-                                     self.span, self.d_tail, self.dec.d_indptr,
+                                     self.span, self.d_final, self.dec.d_indptr,
                                      self.num_blocks, self.dec.d_indices, stream)
         qf = q.reshape(self.requests, self.num_qo_heads // self.num_kv_heads, self.head_dim)
         out, lse = self.dec.run(qf, self.k_pool, self.v_pool, sm_scale, stream)

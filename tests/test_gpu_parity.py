@@ -256,27 +256,33 @@ def test_token_sparse_page_size_one(orc):
 
 
 def test_sparse_expand_blocks_exact():
-    """Block ids -> rows, both spans, against the definition; ids outside
-    [0, num_blocks) are clamped into the request's region."""
+    """Block ids -> rows at every page size dividing the block (token rows,
+    sub-block pages, one page per block), against the definition: block j's
+    pages id*span + t, the final block only the pages that hold its written
+    positions; ids outside [0, num_blocks) are clamped into the request's
+    region."""
     rng = np.random.Generator(np.random.PCG64(90))
     r, blocks, c, nb = 5, 7, 16, 40
     ids = rng.integers(-3, nb + 3, size=(r, blocks)).astype(np.int32)
     tail = rng.integers(1, c + 1, size=r).astype(np.int32)
     base = (np.arange(r) * 1000).astype(np.int32)
-    for span, exact in ((c, True), (1, False)):
-        csr = B.paged_sparse_csr(blocks, c, tail, exact)
+    for ps in (1, 2, 4, 8, 16):
+        span = c // ps
+        final = (tail + ps - 1) // ps
+        csr = B.paged_sparse_csr(blocks, c, tail, ps)
         ip = csr["indptr"]
         rows = torch.full((int(ip[-1]),), -1, dtype=torch.int32, device=DEV)
-        B.paged_sparse_expand_blocks(to_dev(ids), r, blocks, to_dev(base), span, to_dev(tail),
+        B.paged_sparse_expand_blocks(to_dev(ids), r, blocks, to_dev(base), span, to_dev(final),
                                      to_dev(ip), nb, rows)
         torch.cuda.synchronize()
         want = []
         for i in range(r):
             for j in range(blocks):
                 cid = min(max(int(ids[i, j]), 0), nb - 1)
-                n = span if (j < blocks - 1 or not exact) else int(tail[i])
+                # pages of this block that hold selected positions
+                n = span if j < blocks - 1 else -(-int(tail[i]) // ps)
                 want.extend(int(base[i]) + cid * span + t for t in range(n))
-        assert rows.cpu().numpy().tolist() == want
+        assert rows.cpu().numpy().tolist() == want, ps
 
 
 def _block_sparse_reference(orc, w):
@@ -294,20 +300,27 @@ def _block_sparse_reference(orc, w):
     return ref_v, ref_l
 
 
-@pytest.mark.parametrize("token_exact", [False, True], ids=["block-granular", "token-exact"])
+@pytest.mark.parametrize("token_exact,page_size", [(False, 0), (False, -1), (False, 32),
+                                                   (False, 8), (True, 0)],
+                         ids=["block-granular", "one-page-per-block", "32-row-pages",
+                              "8-row-pages", "token-exact"])
 @pytest.mark.parametrize("geom", [dict(), dict(seed=8, hq=16, hkv=4, cap=8192, block_size=64,
-                                                blocks=9, kv_len=8192)],
-                         ids=["minimax-like", "g4-full-final-block"])
-def test_block_sparse_decode(orc, token_exact, geom):
-    """The selection read through either page-table granularity matches
-    attention over the selected positions of the dense allocation; the
-    positions past the live length are NaN, so reading past the final
-    block's written positions would show."""
+                                                blocks=9, kv_len=8192),
+                                  dict(seed=9, hq=8, hkv=2, cap=4096, block_size=64,
+                                       blocks=5, kv_len=4000 - 21)],
+                         ids=["minimax-like", "g4-full-final-block", "g4-mid-page-final"])
+def test_block_sparse_decode(orc, token_exact, page_size, geom):
+    """The selection read through each page-table granularity (one-token
+    pages, pages of 8 to 32 rows, one page per block, and the default 16-row
+    pages) matches attention over the selected positions of the dense
+    allocation; the positions past the live length are NaN, so reading past
+    the final block's written positions would show."""
     w = workloads.block_sparse_fp16(**geom)
     b, hkv, cap, d = w.k_dense.shape
+    ps = w.block_size if page_size == -1 else page_size
     dec = PD.BlockSparseDecode(to_dev(w.k_dense), to_dev(w.v_dense), num_qo_heads=w.q.shape[1],
                                block_size=w.block_size, blocks_per_request=w.block_ids.shape[1],
-                               kv_len=w.kv_len, token_exact=token_exact)
+                               kv_len=w.kv_len, token_exact=token_exact, page_size=ps)
     say("case block_sparse %s exact=%s plan=%s" % (geom, token_exact, dec.plan_summary()))
     ids = to_dev(w.block_ids)
     for it in range(2):
