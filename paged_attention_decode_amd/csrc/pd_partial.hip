@@ -1692,10 +1692,20 @@ KernelFn pick_mfma_tok(int g, int hpw)
 }
 
 // KV heads per MFMA workgroup: the largest power of two up to 8 that divides
-// the KV head count
-int mfma_heads_per_wg(int hkv)
+// the KV head count, or up to 2 for chunks shorter than kNarrowChunkTokens.
+// Short chunks are latency-bound: spread over more, narrower workgroups they
+// reach more CUs.  Measured on MI355X, long-context geometry (8 KV heads)
+// with chunks forced to c pages of 16 tokens, partial kernel: c = 4 87.6 ->
+// 79.6 us, c = 8 82.5 -> 74.1, c = 13 70.7 -> 69.2 with 2 heads per
+// workgroup instead of 8, but c = 16 69.2 -> 72.7 and the default c = 26
+// 64.1 -> 65.0; the batched workload's 48-token chunks: step 13.9 -> 13.4 us
+// and the shared-prefix batch's flat decode (160-token chunks) 32.0 -> 27.0 us
+// (graph-replayed).  4 heads per workgroup measured between the two or worse.
+constexpr int64_t kNarrowChunkTokens = 224;
+int mfma_heads_per_wg(int hkv, int64_t chunk_tokens = 0)
 {
-    for (int h = 8; h > 1; h >>= 1)
+    const int cap = chunk_tokens > 0 && chunk_tokens < kNarrowChunkTokens ? 2 : 8;
+    for (int h = cap; h > 1; h >>= 1)
         if (hkv % h == 0) return h;
     return 1;
 }
@@ -1710,7 +1720,8 @@ int mfma_heads_per_wg(int hkv)
 // Every other shape takes the token kernel.  The page-tiled kernels need
 // 32-bit in-page offsets.
 Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool fused,
-            bool allow_page = true, int hkv = 1, bool allow_mfma = true)
+            bool allow_page = true, int hkv = 1, bool allow_mfma = true,
+            int64_t chunk_tokens = 0)
 {
     Choice c{nullptr, 0, 1, kThreads, 0};
     const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
@@ -1722,7 +1733,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
         if ((tiles & (tiles - 1)) == 0) {
             int lg = 0;
             while ((1 << lg) < tiles) ++lg;
-            const int hpw = mfma_heads_per_wg(hkv);
+            const int hpw = mfma_heads_per_wg(hkv, chunk_tokens);
             c.fn = pick_mfma(g, hpw);
             c.spp_log2 = lg;
             c.heads_per_wg = hpw;
@@ -1751,7 +1762,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
         }
     }
     if (mfma_ok) {
-        const int hpw = mfma_heads_per_wg(hkv);
+        const int hpw = mfma_heads_per_wg(hkv, chunk_tokens);
         c.fn = pick_mfma_tok(g, hpw);
         c.heads_per_wg = hpw;
         c.threads = 64 * hpw;
@@ -1872,7 +1883,8 @@ extern "C" int paged_decode_partial(const void *q, const void *k_pool, const voi
                             who);
     if (rc) return rc;
     const Choice c = pick(dtype, head_dim, num_qo_heads / num_kv_heads, page_size, token_stride,
-                          false, !g_force_token_kernel, num_kv_heads, !g_no_mfma);
+                          false, !g_force_token_kernel, num_kv_heads, !g_no_mfma,
+                          int64_t(pages_per_chunk) * page_size);
     if (!c.fn) return fail(PD_E_UNSUPPORTED, "paged_decode_partial: no kernel for this (dtype, D, group)");
     if (num_chunks == 0) return PD_OK;
     return launch(c, a, num_chunks, stream, who);
@@ -1990,7 +2002,8 @@ extern "C" int paged_cascade_partial(const void *q, int32_t batch, const int32_t
             args[j].q_group = g;
         }
         choice[j] = pick(dtype, head_dim, gj, page_size, token_stride, false,
-                         !g_force_token_kernel, num_kv_heads, !g_no_mfma);
+                         !g_force_token_kernel, num_kv_heads, !g_no_mfma,
+                         int64_t(lv->pages_per_chunk) * page_size);
         if (!choice[j].fn)
             return fail(PD_E_UNSUPPORTED, std::string(who) + ": no kernel for stacked group " +
                                               std::to_string(gj));
