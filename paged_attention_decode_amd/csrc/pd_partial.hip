@@ -1308,8 +1308,9 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTab
 // fast-divided by the page size) and gathers a tile's offsets from it with
 // ds_bpermute: lane l loads the K and V rows of tokens l / 16 + 4j, as the
 // page variant does within a page (the row offsets of 4 tokens per lane and
-// step).  The products, the softmax and the epilogue are the page variant's.  Tokens past the chunk take the last
-// token's offset (valid rows) and are masked: -inf scores, zero V rows.
+// step).  The products, the softmax and the epilogue are the page
+// variant's.  Tokens past the chunk take the last token's offset (valid
+// rows) and are masked: -inf scores, zero V rows.
 template <int HT, int HPW>
 __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
                                               char (&s_v)[HPW][kMfmaTileBytes])
