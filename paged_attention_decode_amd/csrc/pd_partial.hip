@@ -967,16 +967,17 @@ constexpr int token_rows_per_step()
 }
 
 // ----------------------------------------------------------------- MFMA kernel
-// For large query groups (G >= 8) the scores and the value sum are real
-// dense products.  A tile of 16 tokens of one KV head against the group's
-// queries is S^T [16 tokens x 16 heads] = K [16 x 128] . Q^T [128 x 16]:
-// four v_mfma_f32_16x16x32_f16.  The value sum is taken transposed,
-// O^T [16 dims x 16 heads] += V^T [16 dims x 16 tokens] . P^T [16 tokens x
-// 16 heads]: one v_mfma_f32_16x16x32_f16 per 16 dims, whose K = 32 holds
-// each token twice -- once with p rounded to fp16, once with the rounding's
-// remainder -- so that P enters the product with about 22 bits, not fp16's
-// 11 (the softmax weights stay fp32 arithmetic, as the fp16 path's
-// products and sums are).
+// fp16 with head dim D in {64, 128}: the scores and the value sum as dense
+// products on the matrix cores.  A tile of 16 tokens of one KV head against
+// the group's queries is S^T [16 tokens x 16 heads] = K [16 x D] . Q^T
+// [D x 16]: D/32 v_mfma_f32_16x16x32_f16.  The value sum is taken
+// transposed, O^T [16 dims x 16 heads] += V^T [16 dims x 16 tokens] . P^T
+// [16 tokens x 16 heads]: one v_mfma_f32_16x16x32_f16 per 16 dims, whose
+// K = 32 holds each token twice -- once with p rounded to fp16, once with
+// the rounding's remainder -- so that P enters the product with about 22
+// bits, not fp16's 11 (the softmax weights stay fp32 arithmetic, as the
+// fp16 path's products and sums are).  Groups under 16 heads are
+// zero-padded 16-head tiles: the kernel streams K/V at the same rate.
 //
 // Lane layouts of the 16x16xK products (checked on gfx950): A [M x K] --
 // lane l holds row l%16, k = (K/4)*(l/16) + e; B [K x N] -- lane l holds
@@ -984,37 +985,200 @@ constexpr int token_rows_per_step()
 // 4*(l/16) + i.  With S^T in C layout, lane l holds head l%16 for tokens
 // 4*(l/16) + i: that is P^T's B layout for the value product, and O^T's C
 // layout puts the same head in lane l.  So a lane owns one head's running
-// max and sum and 32 of its output dims, and a rescale is a per-lane scalar.
+// max and sum and D/4 of its output dims, and a rescale is a per-lane
+// scalar.
 //
-// K and V are loaded by rows: each load instruction reads 4 whole 256-byte
-// rows (16 lanes per row), and the rows go to the wave's LDS tiles.  K's A
-// operand (lane l: token l%16, 16 bytes at dims 8*(l/16) + 32*kc) is read
-// back with ds_read_b128.  Loading it straight into the operand layout reads
-// 16 rows x 64 bytes per instruction, twice the cache lines per request:
-// measured on MI355X at G = 8 that took the long-context partial from 65.6
-// to 67.1 us, and the any-page variant at page size 1 from 68.7 to 72.5 us
-// (PD_MFMA_K_LDS=0 builds that form).  V^T's A operand (4 tokens of one dim
-// per lane) is read from the V tile with the gfx950 transpose read
-// ds_read_b64_tr_b16: in each 16-lane group, lanes 4r..4r+3 name 4
-// consecutive halves each (together row r of a 4 x 16 tile) and lane c
-// receives column c.  Each wave has its own LDS tiles, rows padded by 16
-// bytes against bank conflicts.
-constexpr int kMfmaRowBytes = 128 * 2 + 16;    // LDS bytes per row of a tile
-#ifndef PD_MFMA_K_LDS
-#define PD_MFMA_K_LDS 1
-#endif
-constexpr bool kKviaLds = PD_MFMA_K_LDS != 0;
-constexpr int kMfmaTileBytes = (kKviaLds ? 32 : 16) * kMfmaRowBytes;   // V tile, then K tile
+// K and V are loaded by rows: each load instruction reads whole rows of
+// 2*D bytes (D/8 lanes of 16 bytes per row: 4 rows at D = 128, 8 at
+// D = 64), and the rows go to the wave's LDS tiles.  K's A operand (lane l:
+// token l%16, 16 bytes at dims 8*(l/16) + 32*kc) is read back with
+// ds_read_b128.  Loading it straight into the operand layout reads 16 rows
+// x 64 bytes per instruction, twice the cache lines per request: measured
+// on MI355X at D = 128 and G = 8 that took the long-context partial from
+// 65.6 to 67.1 us, and the any-page variant at page size 1 from 68.7 to
+// 72.5 us.  V^T's A operand (4 tokens of one dim per lane) is read from the
+// V tile with the gfx950 transpose read ds_read_b64_tr_b16: in each 16-lane
+// group, lanes 4r..4r+3 name 4 consecutive halves each (together row r of a
+// 4 x 16 tile) and lane c receives column c.  Each wave has its own LDS
+// tiles, rows padded by 16 bytes against bank conflicts.
+template <int D>
+struct MfmaShape {
+    static_assert(D == 64 || D == 128, "MFMA kernels: head dim 64 or 128");
+    static constexpr int KC = D / 32;            // K-steps of the score product
+    static constexpr int DT = D / 16;            // 16-dim tiles of the value product
+    static constexpr int RB = 2 * D + 16;        // LDS bytes per tile row
+    static constexpr int LPR = D / 8;            // lanes per row of a row load
+    static constexpr int RPI = 64 / LPR;         // rows per load instruction
+    static constexpr int NJ = 16 / RPI;          // load instructions per 16-row tile
+    static constexpr int TILE_BYTES = 32 * RB;   // per wave: V tile, then K tile
+};
 
-// The group size G = a.group is a run-time value up to 16 * HT (heads past
-// G are zero columns of the 16-head tiles), so one instantiation serves
-// every group of its tile count, and a pair launch can run two tables of
-// different groups.
-template <int HT, int HPW>
-__device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
-                                          char (&s_v)[HPW][kMfmaTileBytes])
+// Q^T as the B operand of the score product: lane l holds head 16*ht + l%16
+// (zero past G) at dims 32*kc + 8*(l/16) .. + 7
+template <int D, int HT>
+__device__ __forceinline__ void mfma_load_q(const PartialArgs &a, int r, int kvh, int G,
+                                            int lane, half8_t (&qb)[HT][MfmaShape<D>::KC])
 {
-    constexpr int D = 128;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int h = ht * 16 + col;
+        const _Float16 *qp = static_cast<const _Float16 *>(a.q) +
+                             q_row(a, r, kvh, G, min(h, G - 1)) * D + 8 * grp;
+#pragma unroll
+        for (int kc = 0; kc < MfmaShape<D>::KC; ++kc) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * kc);
+            qb[ht][kc] = h < G ? __builtin_bit_cast(half8_t, u) : half8_t{};
+        }
+    }
+}
+
+// One 16-token tile of one KV head.  kr / vr: the tile's K and V rows as
+// loaded (load j, lane l: row l/(D/8) + (64/(D/8))*j, bytes 16*(l%(D/8))).
+// vis(i) says whether tile token i is visible; it is asked only on an edge
+// tile.  Hidden tokens get zero V rows (whatever they hold never reaches the
+// sum) and -inf scores.
+template <int D, int HT, typename Vis>
+__device__ __forceinline__ void mfma_tile(const uint4 (&kr)[MfmaShape<D>::NJ],
+                                          const uint4 (&vr)[MfmaShape<D>::NJ], bool edge,
+                                          Vis vis, char *vt, float scale_log2,
+                                          const half8_t (&qb)[HT][MfmaShape<D>::KC],
+                                          float (&m_run)[HT], float (&l_part)[HT],
+                                          float4_t (&acc)[HT][MfmaShape<D>::DT], int lane)
+{
+    using S = MfmaShape<D>;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+    const int lrow = lane / S::LPR;
+    const int lpc = lane % S::LPR;
+    char *kt = vt + 16 * S::RB;
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j) {
+        const int row = lrow + S::RPI * j;
+        uint4 v = vr[j];
+        if (edge) {
+            const bool ok = vis(row);
+            v.x = ok ? v.x : 0u;
+            v.y = ok ? v.y : 0u;
+            v.z = ok ? v.z : 0u;
+            v.w = ok ? v.w : 0u;
+        }
+        *reinterpret_cast<uint4 *>(vt + row * S::RB + 16 * lpc) = v;
+        *reinterpret_cast<uint4 *>(kt + row * S::RB + 16 * lpc) = kr[j];
+    }
+    // the rows written above are read back below by the same wave: LDS
+    // operations of a wave complete in order, so only the compiler must keep
+    // them in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    uint4 kf[S::KC];
+#pragma unroll
+    for (int kc = 0; kc < S::KC; ++kc)
+        kf[kc] = *reinterpret_cast<const uint4 *>(kt + col * S::RB + 16 * grp + 64 * kc);
+    // scores S^T = K . Q^T, per 16-head tile
+    float4_t sc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        sc[ht] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < S::KC; ++kc)
+            sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kf[kc]),
+                                                            qb[ht][kc], sc[ht], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // V^T, 16 dims at a time: row 4*(l/16) + (l%16)/4, halves 16*dt + 4*(l%4)
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    const int tr_off = (4 * grp + (col >> 2)) * S::RB + 8 * (lane & 3);
+    half4_t vtr[S::DT];
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+        vtr[dt] = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                  (lds_short4 *)(vt + tr_off + 32 * dt)));
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        float x[4];
+        float mb = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = sc[ht][i] * scale_log2;
+            if (edge) v = vis(4 * grp + i) ? v : -INFINITY;
+            x[i] = v;
+            mb = fmaxf(mb, v);
+        }
+        mb = group_max4(mb);                       // over the tile's 16 tokens
+        const bool need = mb > m_run[ht] + kLazyMargin;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float m_new = need ? mb : m_run[ht];
+            const float alpha = fast_exp2(m_run[ht] - m_new);
+            m_run[ht] = m_new;
+            l_part[ht] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < S::DT; ++dt) acc[ht][dt] *= alpha;
+        }
+        // P^T in two fp16 parts: k = 8*(l/16) + e holds, for token
+        // 4*(l/16) + e%4, p rounded to fp16 (e < 4) or the remainder
+        // p - that, rounded to fp16 (e >= 4); the A operand repeats the
+        // token's V^T for both.  The product then carries p to about 22
+        // bits, the sum takes p itself, and the K = 32 product takes as
+        // long as the K = 16 one it replaces.
+        half8_t pb;
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(x[i] - m_run[ht]);
+            const _Float16 ph = _Float16(p);
+            pb[i] = ph;
+            pb[4 + i] = _Float16(p - float(ph));
+            ls += p;
+        }
+        l_part[ht] += ls;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) {
+            const half8_t va = __builtin_shufflevector(vtr[dt], vtr[dt], 0, 1, 2, 3, 0, 1, 2, 3);
+            acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ht][dt], 0, 0, 0);
+        }
+    }
+}
+
+// per head: the sum over the four 16-lane groups; each group holds 4 of
+// every 16 dims, so the accumulators need no combine
+template <int D, int HT>
+__device__ __forceinline__ void mfma_epilogue(const PartialArgs &a, int n, int kvh, int G,
+                                              int lane, const float (&m_run)[HT],
+                                              const float (&l_part)[HT],
+                                              const float4_t (&acc)[HT][MfmaShape<D>::DT])
+{
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+    const int hq = a.num_qo_heads;
+    float *vrow = a.v_out + int64_t(n) * hq * D;
+    float *lrow = a.lse_out + int64_t(n) * hq;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const float l = group_sum4(l_part[ht]);
+        const int h = ht * 16 + col;
+        if (h >= G) continue;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int64_t qh = int64_t(kvh) * G + h;
+#pragma unroll
+        for (int dt = 0; dt < MfmaShape<D>::DT; ++dt) {
+            const float4_t o = acc[ht][dt] * inv;
+            *reinterpret_cast<float4 *>(vrow + qh * D + 16 * dt + 4 * grp) =
+                make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (grp == 0) lrow[qh] = l > 0.f ? m_run[ht] + fast_log2(l) : -INFINITY;
+    }
+}
+
+// The page-tiled kernel: a step is a 16-token tile of one page.  The group
+// size G = a.group is a run-time value up to 16 * HT (heads past G are zero
+// columns of the 16-head tiles), so one instantiation serves every group of
+// its tile count, and a pair launch can run two tables of different groups.
+template <int D, int HT, int HPW>
+__device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
+                                          char (&s_v)[HPW][MfmaShape<D>::TILE_BYTES])
+{
+    using S = MfmaShape<D>;
     constexpr int ESZ = 2;
     const int G = a.group;
 
@@ -1025,8 +1189,6 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kvh = kvg * HPW + wave;
     const int lane = tid & 63;
-    const int grp = lane >> 4;          // 16-lane group
-    const int col = lane & 15;          // head of a tile (C / B layouts) or token (A layout)
 
     const int r = ld_uniform(a.req_idx + n);
     const int t = ld_uniform(a.tile_idx + n);
@@ -1047,20 +1209,8 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
     };
     int32_t idv = load_ids(cp0);
 
-    // Q^T as the B operand of the score product: lane l holds head
-    // 16*ht + l%16 (zero past G) at dims 32*kc + 8*(l/16) .. + 7
-    half8_t qb[HT][4];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int h = ht * 16 + col;
-        const _Float16 *qp = static_cast<const _Float16 *>(a.q) +
-                             q_row(a, r, kvh, G, min(h, G - 1)) * D + 8 * grp;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * kc);
-            qb[ht][kc] = h < G ? __builtin_bit_cast(half8_t, u) : half8_t{};
-        }
-    }
+    half8_t qb[HT][S::KC];
+    mfma_load_q<D, HT>(a, r, kvh, G, lane, qb);
 
     const char *kb = static_cast<const char *>(a.k) + int64_t(kvh) * a.head_stride * ESZ;
     const char *vb = static_cast<const char *>(a.v) + int64_t(kvh) * a.head_stride * ESZ;
@@ -1068,34 +1218,27 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
     const int32_t tsb = int32_t(a.token_stride * ESZ);
     const uint32_t tile_bytes = uint32_t(tsb) * 16u;
     const int32_t page_span = int32_t(int64_t(ps - 1) * a.token_stride * ESZ + D * ESZ);
-    // K: lane l reads token l%16 at dims 8*(l/16) + 32*kc; V: lane l reads
-    // row l/16 + 4*j at bytes 16*(l%16) (16 lanes per whole row)
-    const int32_t k_off = col * tsb + 16 * grp;
-    const int32_t v_off = grp * tsb + 16 * col;
+    // load j, lane l: row l/(D/8) + (64/(D/8))*j at bytes 16*(l%(D/8))
+    const int32_t row_off = (lane / S::LPR) * tsb + 16 * (lane % S::LPR);
 
     // per 16-head tile: the lane's head's running max and its share of the sum
     float m_run[HT], l_part[HT];
-    float4_t acc[HT][8];
+    float4_t acc[HT][S::DT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         m_run[ht] = kNoMax;
         l_part[ht] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < S::DT; ++dt) acc[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-
     char *vt = s_v[wave];
-    typedef __attribute__((address_space(3))) short4_t lds_short4;
-    // transpose-read address of dim tile dt: row 4*(l/16) + (l%16)/4, halves
-    // 16*dt + 4*(l%4)
-    const int tr_off = (4 * grp + (col >> 2)) * kMfmaRowBytes + 8 * (lane & 3);
 
     for (int wp0 = cp0; wp0 < cp1; wp0 += 64) {
         const int wcount = min(cp1 - wp0, 64);
         const int32_t idn = load_ids(wp0 + 64);    // the next window's ids, one window ahead
         const int nsteps = wcount << spp_log2;
 
-        auto load = [&](int s, uint4 (&kr)[4], uint4 (&vr)[4]) {
+        auto load = [&](int s, uint4 (&kr)[S::NJ], uint4 (&vr)[S::NJ]) {
             const bool live = s < nsteps;
             const int p = min(s >> spp_log2, wcount - 1);
             const int sub = s & ((1 << spp_log2) - 1);
@@ -1108,123 +1251,29 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
                 const_cast<char *>(vb + base), 0, span, kBufferWord3);
             const int soff = int(sub * tile_bytes);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rk, kKviaLds ? v_off + 4 * j * tsb : k_off + 64 * j, soff, kLoadNT));
-                vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + 4 * j * tsb, soff, kLoadNT));
+            for (int j = 0; j < S::NJ; ++j) {
+                const int32_t off = row_off + S::RPI * j * tsb;
+                kr[j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, soff, kLoadNT));
+                vr[j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, soff, kLoadNT));
             }
         };
 
-        auto compute = [&](int s, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+        auto compute = [&](int s, const uint4 (&kr)[S::NJ], const uint4 (&vr)[S::NJ]) {
             const int p = wp0 + (s >> spp_log2);          // request-relative page
             const int slot0 = (s & ((1 << spp_log2) - 1)) * 16;
             const bool edge = (p == 0 && fpo > 0) || (p == npages - 1 && lpl < ps);
             const int lo = p == 0 ? fpo : 0;
             const int hi_slot = p == npages - 1 ? lpl : ps;
-            // V tile -> this wave's LDS rows (tokens outside the visible range
-            // as zeros: whatever they hold never reaches the sum)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint4 v = vr[j];
-                if (edge) {
-                    const int slot = slot0 + grp + 4 * j;
-                    const bool ok = slot >= lo && slot < hi_slot;
-                    v.x = ok ? v.x : 0u;
-                    v.y = ok ? v.y : 0u;
-                    v.z = ok ? v.z : 0u;
-                    v.w = ok ? v.w : 0u;
-                }
-                *reinterpret_cast<uint4 *>(vt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = v;
-            }
-            // K operand fragments: lane l takes token l % 16 at dims
-            // 8*(l/16) + 32*kc, straight from the load or through the LDS
-            // copy of the tile (written in the V rows' layout)
-            uint4 kf[4];
-            if constexpr (kKviaLds) {
-                char *kt = vt + 16 * kMfmaRowBytes;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<uint4 *>(kt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = kr[j];
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc)
-                    kf[kc] = *reinterpret_cast<const uint4 *>(kt + col * kMfmaRowBytes + 16 * grp + 64 * kc);
-            } else {
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc) kf[kc] = kr[kc];
-            }
-            // scores S^T = K . Q^T, per 16-head tile
-            float4_t sc[HT];
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                sc[ht] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < 4; ++kc)
-                    sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(half8_t, kf[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
-            }
-            // the V rows written above are read back below by the same wave:
-            // LDS operations of a wave complete in order, so only the
-            // compiler must keep them in order
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            half4_t vtr[8];
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                vtr[dt] = __builtin_bit_cast(
-                    half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                 (lds_short4 *)(vt + tr_off + 32 * dt)));
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                float x[4];
-                float mb = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = sc[ht][i] * a.scale_log2;
-                    if (edge) {
-                        const int slot = slot0 + 4 * grp + i;
-                        v = (slot >= lo && slot < hi_slot) ? v : -INFINITY;
-                    }
-                    x[i] = v;
-                    mb = fmaxf(mb, v);
-                }
-                mb = group_max4(mb);                       // over the tile's 16 tokens
-                const bool need = mb > m_run[ht] + kLazyMargin;
-                if (__builtin_amdgcn_ballot_w64(need)) {
-                    const float m_new = need ? mb : m_run[ht];
-                    const float alpha = fast_exp2(m_run[ht] - m_new);
-                    m_run[ht] = m_new;
-                    l_part[ht] *= alpha;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) acc[ht][dt] *= alpha;
-                }
-                // P^T in two fp16 parts: k = 8*(l/16) + e holds, for token
-                // 4*(l/16) + e%4, p rounded to fp16 (e < 4) or the remainder
-                // p - that, rounded to fp16 (e >= 4); the A operand repeats
-                // the token's V^T for both.  The product then carries p to
-                // about 22 bits, the sum takes p itself, and the K = 32 product
-                // takes as long as the K = 16 one it replaces.
-                half8_t pb;
-                float ls = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(x[i] - m_run[ht]);
-                    const _Float16 ph = _Float16(p);
-                    pb[i] = ph;
-                    pb[4 + i] = _Float16(p - float(ph));
-                    ls += p;
-                }
-                l_part[ht] += ls;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    const half8_t va = __builtin_shufflevector(vtr[dt], vtr[dt], 0, 1, 2, 3, 0, 1,
-                                                               2, 3);
-                    acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ht][dt], 0,
-                                                                         0, 0);
-                }
-            }
+            auto vis = [&](int i) {
+                const int slot = slot0 + i;
+                return slot >= lo && slot < hi_slot;
+            };
+            mfma_tile<D, HT>(kr, vr, edge, vis, vt, a.scale_log2, qb, m_run, l_part, acc, lane);
         };
 
-        uint4 kbuf[kDepth][4], vbuf[kDepth][4];
+        uint4 kbuf[kDepth][S::NJ], vbuf[kDepth][S::NJ];
         int s = 0;
 #pragma unroll
         for (int d = 0; d < kDepth - 1; ++d) load(s + d, kbuf[d], vbuf[d]);
@@ -1243,34 +1292,14 @@ __device__ __forceinline__ void mfma_body(const PartialArgs &a, int wg,
         }
         idv = idn;
     }
-
-    // per head: the sum over the four 16-lane groups; each group holds 4 of
-    // every 16 dims, so the accumulators need no combine
-    const int hq = a.num_qo_heads;
-    float *vrow = a.v_out + int64_t(n) * hq * D;
-    float *lrow = a.lse_out + int64_t(n) * hq;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const float l = group_sum4(l_part[ht]);
-        const int h = ht * 16 + col;
-        if (h >= G) continue;
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const int64_t qh = int64_t(kvh) * G + h;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const float4_t o = acc[ht][dt] * inv;
-            *reinterpret_cast<float4 *>(vrow + qh * D + 16 * dt + 4 * grp) =
-                make_float4(o[0], o[1], o[2], o[3]);
-        }
-        if (grp == 0) lrow[qh] = l > 0.f ? m_run[ht] + fast_log2(l) : -INFINITY;
-    }
+    mfma_epilogue<D, HT>(a, n, kvh, G, lane, m_run, l_part, acc);
 }
 
-template <int HT, int HPW>
+template <int D, int HT, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_kernel(PartialArgs a)
 {
-    __shared__ __align__(16) char s_v[HPW][kMfmaTileBytes];
-    mfma_body<HT, HPW>(a, blockIdx.x, s_v);
+    __shared__ __align__(16) char s_v[HPW][MfmaShape<D>::TILE_BYTES];
+    mfma_body<D, HT, HPW>(a, blockIdx.x, s_v);
 }
 
 // Several tables in one grid: workgroups [wg_end[i-1], wg_end[i]) work on
@@ -1287,15 +1316,15 @@ struct PartialTables {
     int32_t count;
 };
 
-template <int HT, int HPW>
+template <int D, int HT, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTables tabs)
 {
-    __shared__ __align__(16) char s_v[HPW][kMfmaTileBytes];
+    __shared__ __align__(16) char s_v[HPW][MfmaShape<D>::TILE_BYTES];
     const int wg = blockIdx.x;
     int i = 0;
     while (i < tabs.count - 1 && wg >= tabs.wg_end[i]) ++i;
     const int base = i > 0 ? tabs.wg_end[i - 1] : 0;
-    mfma_body<HT, HPW>(tabs.t[i], wg - base, s_v);
+    mfma_body<D, HT, HPW>(tabs.t[i], wg - base, s_v);
 }
 
 // ----------------------------------------------------- MFMA kernel, any page
@@ -1306,16 +1335,16 @@ __global__ void __launch_bounds__(64 * HPW) partial_mfma_multi_kernel(PartialTab
 // consecutive tokens of its chunk in a register (lane t: token w0 + t,
 // from the page id and in-page slot of the PR #984 page-table walk,
 // fast-divided by the page size) and gathers a tile's offsets from it with
-// ds_bpermute: lane l loads the K and V rows of tokens l / 16 + 4j, as the
-// page variant does within a page (the row offsets of 4 tokens per lane and
-// step).  The products, the softmax and the epilogue are the page
-// variant's.  Tokens past the chunk take the last token's offset (valid
-// rows) and are masked: -inf scores, zero V rows.
-template <int HT, int HPW>
+// ds_bpermute: lane l loads the K and V rows of the tokens the page variant's
+// row loads give it (l/(D/8) + (64/(D/8))*j), one gathered offset per load.
+// The tile's products, softmax and the epilogue are the page variant's.
+// Tokens past the chunk take the last token's offset (valid rows) and are
+// masked: -inf scores, zero V rows.
+template <int D, int HT, int HPW>
 __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
-                                              char (&s_v)[HPW][kMfmaTileBytes])
+                                              char (&s_v)[HPW][MfmaShape<D>::TILE_BYTES])
 {
-    constexpr int D = 128;
+    using S = MfmaShape<D>;
     constexpr int ESZ = 2;
     const int G = a.group;
 
@@ -1326,8 +1355,8 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kvh = kvg * HPW + wave;
     const int lane = tid & 63;
-    const int grp = lane >> 4;
-    const int col = lane & 15;
+    const int lrow = lane / S::LPR;
+    const int lpc = lane % S::LPR;
 
     const int r = ld_uniform(a.req_idx + n);
     const int t = ld_uniform(a.tile_idx + n);
@@ -1354,35 +1383,22 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
         return a.indices[pbeg + min(int(pi), npages - 1)];
     };
 
-    half8_t qb[HT][4];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int h = ht * 16 + col;
-        const _Float16 *qp = static_cast<const _Float16 *>(a.q) +
-                             q_row(a, r, kvh, G, min(h, G - 1)) * D + 8 * grp;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const uint4 u = *reinterpret_cast<const uint4 *>(qp + 32 * kc);
-            qb[ht][kc] = h < G ? __builtin_bit_cast(half8_t, u) : half8_t{};
-        }
-    }
+    half8_t qb[HT][S::KC];
+    mfma_load_q<D, HT>(a, r, kvh, G, lane, qb);
 
     const char *kb = static_cast<const char *>(a.k) + int64_t(kvh) * a.head_stride * ESZ;
     const char *vb = static_cast<const char *>(a.v) + int64_t(kvh) * a.head_stride * ESZ;
 
     float m_run[HT], l_part[HT];
-    float4_t acc[HT][8];
+    float4_t acc[HT][S::DT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         m_run[ht] = kNoMax;
         l_part[ht] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < S::DT; ++dt) acc[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-
     char *vt = s_v[wave];
-    typedef __attribute__((address_space(3))) short4_t lds_short4;
-    const int tr_off = (4 * grp + (col >> 2)) * kMfmaRowBytes + 8 * (lane & 3);
 
     // row offsets of the load cursor's 64-token window, split for ds_bpermute;
     // the page ids of the window after it are loaded one window ahead
@@ -1409,7 +1425,7 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
 
     // loads run in step order, so the cursor moves to window s/4 at the
     // first step of it; steps past the chunk reload the last one
-    auto load = [&](int s, uint4 (&kr)[4], uint4 (&vr)[4]) {
+    auto load = [&](int s, uint4 (&kr)[S::NJ], uint4 (&vr)[S::NJ]) {
         if (s < nsteps && s > 0 && (s & 3) == 0) {
             set_window(pid_next, e_next);
             // unconditional (clamped to the last token): a conditional load
@@ -1417,118 +1433,23 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
             pid_next = load_pid(16 * s + 64, e_next);
         }
         const int sl = (min(s, nsteps - 1) & 3) * 16;
-        if constexpr (kKviaLds) {
-            // K and V rows of tokens grp + 4j, 256 contiguous bytes per 16 lanes
+        // K and V rows of tokens lrow + RPI*j, whole rows per load
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t o = gather(sl + grp + 4 * j) + 16 * col;
-                kr[j] = load_nt(kb + o);
-                vr[j] = load_nt(vb + o);
-            }
-        } else {
-            const char *kp = kb + gather(sl + col) + 16 * grp;
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) kr[kc] = load_nt(kp + 64 * kc);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vr[j] = load_nt(vb + gather(sl + grp + 4 * j) + 16 * col);
+        for (int j = 0; j < S::NJ; ++j) {
+            const int64_t o = gather(sl + lrow + S::RPI * j) + 16 * lpc;
+            kr[j] = load_nt(kb + o);
+            vr[j] = load_nt(vb + o);
         }
     };
 
-    auto compute = [&](int s, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+    auto compute = [&](int s, const uint4 (&kr)[S::NJ], const uint4 (&vr)[S::NJ]) {
         const int tt0 = 16 * s;                     // chunk token of the tile's first row
         const bool edge = tt0 + 16 > ntok;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint4 v = vr[j];
-            if (edge) {
-                const bool ok = tt0 + grp + 4 * j < ntok;
-                v.x = ok ? v.x : 0u;
-                v.y = ok ? v.y : 0u;
-                v.z = ok ? v.z : 0u;
-                v.w = ok ? v.w : 0u;
-            }
-            *reinterpret_cast<uint4 *>(vt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = v;
-        }
-        // K operand fragments (lane l: token l % 16, dims 8*(l/16) + 32*kc),
-        // through the LDS copy of the tile when K was loaded by rows
-        uint4 kf[4];
-        if constexpr (kKviaLds) {
-            char *kt = vt + 16 * kMfmaRowBytes;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<uint4 *>(kt + (grp + 4 * j) * kMfmaRowBytes + 16 * col) = kr[j];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-                kf[kc] = *reinterpret_cast<const uint4 *>(kt + col * kMfmaRowBytes + 16 * grp + 64 * kc);
-        } else {
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc) kf[kc] = kr[kc];
-        }
-        float4_t sc[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            sc[ht] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)
-                sc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    __builtin_bit_cast(half8_t, kf[kc]), qb[ht][kc], sc[ht], 0, 0, 0);
-        }
-        // the V rows written above are read back below by the same wave:
-        // LDS operations of a wave complete in order, so only the
-        // compiler must keep them in order
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        half4_t vtr[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            vtr[dt] = __builtin_bit_cast(
-                half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                             (lds_short4 *)(vt + tr_off + 32 * dt)));
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            float x[4];
-            float mb = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v = sc[ht][i] * a.scale_log2;
-                if (edge) v = tt0 + 4 * grp + i < ntok ? v : -INFINITY;
-                x[i] = v;
-                mb = fmaxf(mb, v);
-            }
-            mb = group_max4(mb);
-            const bool need = mb > m_run[ht] + kLazyMargin;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                const float m_new = need ? mb : m_run[ht];
-                const float alpha = fast_exp2(m_run[ht] - m_new);
-                m_run[ht] = m_new;
-                l_part[ht] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[ht][dt] *= alpha;
-            }
-            // P^T as an fp16 part and an fp16 remainder (the page variant's
-            // layout: k = 8*(l/16) + e, token 4*(l/16) + e%4)
-            half8_t pb;
-            float ls = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(x[i] - m_run[ht]);
-                const _Float16 ph = _Float16(p);
-                pb[i] = ph;
-                pb[4 + i] = _Float16(p - float(ph));
-                ls += p;
-            }
-            l_part[ht] += ls;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const half8_t va = __builtin_shufflevector(vtr[dt], vtr[dt], 0, 1, 2, 3, 0, 1,
-                                                           2, 3);
-                acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, acc[ht][dt], 0,
-                                                                     0, 0);
-            }
-        }
+        auto vis = [&](int i) { return tt0 + i < ntok; };
+        mfma_tile<D, HT>(kr, vr, edge, vis, vt, a.scale_log2, qb, m_run, l_part, acc, lane);
     };
 
-    uint4 kbuf[kDepth][4], vbuf[kDepth][4];
+    uint4 kbuf[kDepth][S::NJ], vbuf[kDepth][S::NJ];
     int s = 0;
     if (nsteps > 0) {
 #pragma unroll
@@ -1550,31 +1471,13 @@ __device__ __forceinline__ void mfma_tok_body(const PartialArgs &a, int wg,
             if (rd % every == every - 1) __builtin_amdgcn_s_barrier();
         }
     }
-
-    const int hq = a.num_qo_heads;
-    float *vrow = a.v_out + int64_t(n) * hq * D;
-    float *lrow = a.lse_out + int64_t(n) * hq;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const float l = group_sum4(l_part[ht]);
-        const int h = ht * 16 + col;
-        if (h >= G) continue;
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const int64_t qh = int64_t(kvh) * G + h;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const float4_t o = acc[ht][dt] * inv;
-            *reinterpret_cast<float4 *>(vrow + qh * D + 16 * dt + 4 * grp) =
-                make_float4(o[0], o[1], o[2], o[3]);
-        }
-        if (grp == 0) lrow[qh] = l > 0.f ? m_run[ht] + fast_log2(l) : -INFINITY;
-    }
+    mfma_epilogue<D, HT>(a, n, kvh, G, lane, m_run, l_part, acc);
 }
-template <int HT, int HPW>
+template <int D, int HT, int HPW>
 __global__ void __launch_bounds__(64 * HPW) partial_mfma_tok_kernel(PartialArgs a)
 {
-    __shared__ __align__(16) char s_v[HPW][kMfmaTileBytes];
-    mfma_tok_body<HT, HPW>(a, blockIdx.x, s_v);
+    __shared__ __align__(16) char s_v[HPW][MfmaShape<D>::TILE_BYTES];
+    mfma_tok_body<D, HT, HPW>(a, blockIdx.x, s_v);
 }
 
 template <typename T, int D, bool FUSED>
@@ -1640,44 +1543,31 @@ struct Choice {
     int kind;           // 0 token kernel, 1 page kernel, 2 MFMA kernel, 3 MFMA kernel, any page
 };
 
-template <int HT>
+template <int D, int HT>
 KernelFn pick_mfma_shape(int hpw)
 {
     switch (hpw) {
-    case 8: return partial_mfma_kernel<HT, 8>;
-    case 4: return partial_mfma_kernel<HT, 4>;
-    case 2: return partial_mfma_kernel<HT, 2>;
-    default: return partial_mfma_kernel<HT, 1>;
+    case 8: return partial_mfma_kernel<D, HT, 8>;
+    case 4: return partial_mfma_kernel<D, HT, 4>;
+    case 2: return partial_mfma_kernel<D, HT, 2>;
+    default: return partial_mfma_kernel<D, HT, 1>;
     }
 }
 
-KernelFn pick_mfma(int g, int hpw)
-{
-    switch (g) {
-    case 1:
-    case 2:
-    case 4:
-    case 8:
-    case 12:
-    case 16: return pick_mfma_shape<1>(hpw);
-    case 24:
-    case 32: return pick_mfma_shape<2>(hpw);
-    default: return nullptr;
-    }
-}
-
-template <int HT>
+template <int D, int HT>
 KernelFn pick_mfma_tok_shape(int hpw)
 {
     switch (hpw) {
-    case 8: return partial_mfma_tok_kernel<HT, 8>;
-    case 4: return partial_mfma_tok_kernel<HT, 4>;
-    case 2: return partial_mfma_tok_kernel<HT, 2>;
-    default: return partial_mfma_tok_kernel<HT, 1>;
+    case 8: return partial_mfma_tok_kernel<D, HT, 8>;
+    case 4: return partial_mfma_tok_kernel<D, HT, 4>;
+    case 2: return partial_mfma_tok_kernel<D, HT, 2>;
+    default: return partial_mfma_tok_kernel<D, HT, 1>;
     }
 }
 
-KernelFn pick_mfma_tok(int g, int hpw)
+// 16-head tiles per wave for a group size, 0 for a group the MFMA kernels
+// do not take
+int mfma_head_tiles(int g)
 {
     switch (g) {
     case 1:
@@ -1685,11 +1575,24 @@ KernelFn pick_mfma_tok(int g, int hpw)
     case 4:
     case 8:
     case 12:
-    case 16: return pick_mfma_tok_shape<1>(hpw);
+    case 16: return 1;
     case 24:
-    case 32: return pick_mfma_tok_shape<2>(hpw);
-    default: return nullptr;
+    case 32: return 2;
+    default: return 0;
     }
+}
+
+// the page-tiled (any_page false) or any-page MFMA kernel for (D, G, width)
+KernelFn pick_mfma(int d, int g, int hpw, bool any_page)
+{
+    const int ht = mfma_head_tiles(g);
+    if (ht == 0 || (d != 64 && d != 128)) return nullptr;
+    if (any_page) {
+        if (d == 64) return ht == 1 ? pick_mfma_tok_shape<64, 1>(hpw) : pick_mfma_tok_shape<64, 2>(hpw);
+        return ht == 1 ? pick_mfma_tok_shape<128, 1>(hpw) : pick_mfma_tok_shape<128, 2>(hpw);
+    }
+    if (d == 64) return ht == 1 ? pick_mfma_shape<64, 1>(hpw) : pick_mfma_shape<64, 2>(hpw);
+    return ht == 1 ? pick_mfma_shape<128, 1>(hpw) : pick_mfma_shape<128, 2>(hpw);
 }
 
 // KV heads per MFMA workgroup: the largest power of two up to 8 that divides
@@ -1711,8 +1614,8 @@ int mfma_heads_per_wg(int hkv, int64_t chunk_tokens = 0)
     return 1;
 }
 
-// In the two-launch mode, fp16 with D = 128 runs on the MFMA kernels for
-// every group they take (1, 2, 4, 8, 12, 16, 24, 32; groups under 16 as
+// In the two-launch mode, fp16 with D = 64 or 128 runs on the MFMA kernels
+// for every group they take (1, 2, 4, 8, 12, 16, 24, 32; groups under 16 as
 // zero-padded 16-head tiles): the page-tiled one at page sizes that are a
 // power-of-two multiple of 16, the any-page one at every other.  The page
 // kernel takes 256-byte rows, G in {4, 8, 16} and page sizes that are a
@@ -1727,7 +1630,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
     Choice c{nullptr, 0, 1, kThreads, 0};
     const int esz = dtype == PD_DTYPE_FP16 ? 2 : 4;
     const bool mfma_ok = allow_page && allow_mfma && !fused && dtype == PD_DTYPE_FP16 &&
-                         d == 128 && pick_mfma(g, 1) != nullptr;
+                         (d == 64 || d == 128) && mfma_head_tiles(g) > 0;
     if (mfma_ok && page_size % 16 == 0 &&
         token_stride * esz * page_size < (int64_t(1) << 31)) {
         const int tiles = page_size / 16;
@@ -1735,7 +1638,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
             int lg = 0;
             while ((1 << lg) < tiles) ++lg;
             const int hpw = mfma_heads_per_wg(hkv, chunk_tokens);
-            c.fn = pick_mfma(g, hpw);
+            c.fn = pick_mfma(d, g, hpw, false);
             c.spp_log2 = lg;
             c.heads_per_wg = hpw;
             c.threads = 64 * hpw;
@@ -1764,7 +1667,7 @@ Choice pick(int dtype, int d, int g, int page_size, int64_t token_stride, bool f
     }
     if (mfma_ok) {
         const int hpw = mfma_heads_per_wg(hkv, chunk_tokens);
-        c.fn = pick_mfma_tok(g, hpw);
+        c.fn = pick_mfma(d, g, hpw, true);
         c.heads_per_wg = hpw;
         c.threads = 64 * hpw;
         c.kind = 3;
@@ -1928,15 +1831,21 @@ namespace {
 
 using MultiFn = void (*)(PartialTables);
 
-template <int HT>
-MultiFn pick_mfma_multi(int hpw)
+template <int D, int HT>
+MultiFn pick_mfma_multi_shape(int hpw)
 {
     switch (hpw) {
-    case 8: return partial_mfma_multi_kernel<HT, 8>;
-    case 4: return partial_mfma_multi_kernel<HT, 4>;
-    case 2: return partial_mfma_multi_kernel<HT, 2>;
-    default: return partial_mfma_multi_kernel<HT, 1>;
+    case 8: return partial_mfma_multi_kernel<D, HT, 8>;
+    case 4: return partial_mfma_multi_kernel<D, HT, 4>;
+    case 2: return partial_mfma_multi_kernel<D, HT, 2>;
+    default: return partial_mfma_multi_kernel<D, HT, 1>;
     }
+}
+
+MultiFn pick_mfma_multi(int d, int ht, int hpw)
+{
+    if (d == 64) return ht == 1 ? pick_mfma_multi_shape<64, 1>(hpw) : pick_mfma_multi_shape<64, 2>(hpw);
+    return ht == 1 ? pick_mfma_multi_shape<128, 1>(hpw) : pick_mfma_multi_shape<128, 2>(hpw);
 }
 
 int check_level(const paged_cascade_level *lv, const char *who)
@@ -2031,7 +1940,7 @@ extern "C" int paged_cascade_partial(const void *q, int32_t batch, const int32_t
     int ht = 1;
     for (int j = 0; j < ntab; ++j)
         if (args[j].group > 16) ht = 2;
-    const MultiFn fn = ht == 1 ? pick_mfma_multi<1>(hpw) : pick_mfma_multi<2>(hpw);
+    const MultiFn fn = pick_mfma_multi(head_dim, ht, hpw);
     const int groups = num_kv_heads / hpw;
     int j = 0;
     while (j < ntab) {

@@ -847,23 +847,25 @@ def test_page_kernel_shapes_ragged(orc, g, ps, mode):
     run_flat(orc, w, target=48, fused=mode["fused"])
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("g", [1, 2, 8, 12, 16, 24, 32])
 @pytest.mark.parametrize("ps,hkv", [(16, 8), (32, 2), (64, 1)])
-def test_mfma_kernel_ragged(orc, g, ps, hkv):
+def test_mfma_kernel_ragged(orc, g, ps, hkv, d):
     """The MFMA kernel over ragged windows, mid-page starts, partial last
-    pages, empty requests and NaN-poisoned pools, at each group size and
-    workgroup shape (8, 2 or 1 KV heads per workgroup)."""
-    w = workloads.random_geometry(300 + g + ps, batch=6, page_size=ps, max_len=2500,
-                                  num_qo_heads=g * hkv, num_kv_heads=hkv, p_empty=0.15,
-                                  p_trim=0.5)
-    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, 128, g, ps, hkv * 128) == 2
+    pages, empty requests and NaN-poisoned pools, at each group size, head
+    dim and workgroup shape (8, 2 or 1 KV heads per workgroup)."""
+    w = workloads.random_geometry(300 + g + ps + d, batch=6, page_size=ps, max_len=2500,
+                                  num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                  p_empty=0.15, p_trim=0.5)
+    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, d, g, ps, hkv * d) == 2
     for target, fixed in ((0, 0), (64, 0), (0, 1)):
         run_flat(orc, w, target=target, fixed=fixed)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("g", [1, 4, 8, 12, 24, 32])
 @pytest.mark.parametrize("ps,hkv", [(1, 2), (3, 8), (48, 1), (4, 4)])
-def test_mfma_any_page_kernel_ragged(orc, g, ps, hkv):
+def test_mfma_any_page_kernel_ragged(orc, g, ps, hkv, d):
     """The any-page MFMA kernel, at page sizes the page-tiled one cannot take
     (a 16-token tile spread over 16, 6 or 4 pages; three tiles per page),
     over ragged windows, mid-page starts, partial last pages, empty requests
@@ -871,10 +873,10 @@ def test_mfma_any_page_kernel_ragged(orc, g, ps, hkv):
     one page (down to a single token) to the whole request, and 37 pages,
     whose chunks start at every offset within the kernel's 64-token
     windows."""
-    w = workloads.random_geometry(760 + g + ps, batch=6, page_size=ps, max_len=2500,
-                                  num_qo_heads=g * hkv, num_kv_heads=hkv, p_empty=0.15,
-                                  p_trim=0.5)
-    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, 128, g, ps, hkv * 128) == 3
+    w = workloads.random_geometry(760 + g + ps + d, batch=6, page_size=ps, max_len=2500,
+                                  num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                  p_empty=0.15, p_trim=0.5)
+    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, d, g, ps, hkv * d) == 3
     for target, fixed in ((0, 0), (64, 0), (0, 1), (0, 37)):
         run_flat(orc, w, target=target, fixed=fixed)
 
@@ -998,8 +1000,9 @@ def test_kernel_choice():
     assert kk(B.PD_DTYPE_FP16, 128, 8, 48, 1024) == 3    # 3 MFMA tiles per page
     assert kk(B.PD_DTYPE_FP16, 128, 32, 1, 128) == 3     # G = 32 at page size 1
     assert kk(B.PD_DTYPE_FP16, 128, 8, 16, 1 << 27) == 3  # in-page offsets past 2^31 bytes
-    assert kk(B.PD_DTYPE_FP16, 64, 8, 1, 128) == 0       # the MFMA kernels take D = 128 only
-    assert kk(B.PD_DTYPE_FP32, 128, 8, 1, 128) == 0      # and fp16 only
+    assert kk(B.PD_DTYPE_FP16, 64, 8, 1, 128) == 3       # D = 64 on the MFMA kernels too
+    assert kk(B.PD_DTYPE_FP16, 64, 32, 16, 512) == 2
+    assert kk(B.PD_DTYPE_FP32, 128, 8, 1, 128) == 0      # fp16 only
     assert kk(B.PD_DTYPE_FP32, 64, 16, 16, 128) == 1
     assert kk(B.PD_DTYPE_FP32, 64, 4, 16, 128) == 1
     B.paged_decode_set_kernel_choice(2)
@@ -1011,6 +1014,7 @@ def test_kernel_choice():
         assert kk(B.PD_DTYPE_FP16, 128, 12, 1, 128) == 0
         assert kk(B.PD_DTYPE_FP16, 128, 1, 16, 1024) == 0
         assert kk(B.PD_DTYPE_FP16, 128, 4, 1, 128) == 0
+        assert kk(B.PD_DTYPE_FP16, 64, 4, 16, 512) == 0
         with pytest.raises(B.PagedDecodeError):            # G = 32 needs an MFMA kernel
             kk(B.PD_DTYPE_FP16, 128, 32, 1, 128)
     finally:
@@ -1021,8 +1025,8 @@ def test_kernel_choice():
     assert kk(B.PD_DTYPE_FP16, 128, 2, 1, 128) == 3
     assert kk(B.PD_DTYPE_FP16, 128, 4, 1, 128) == 3
     assert kk(B.PD_DTYPE_FP16, 128, 4, 16, 1 << 27) == 3  # in-page offsets past 2^31 bytes
-    assert kk(B.PD_DTYPE_FP16, 64, 4, 16, 512) == 0      # 128-byte rows
-    assert kk(B.PD_DTYPE_FP16, 64, 1, 1, 64) == 0
+    assert kk(B.PD_DTYPE_FP16, 64, 4, 16, 512) == 2      # 128-byte rows
+    assert kk(B.PD_DTYPE_FP16, 64, 1, 1, 64) == 3
     assert kk(B.PD_DTYPE_FP32, 128, 1, 16, 1024) == 0
     assert kk(B.PD_DTYPE_FP16, 128, 4, 48, 1024) == 3    # 3 steps per page
 
@@ -1070,8 +1074,8 @@ def test_many_pages_per_chunk_cross_lds_window(orc):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("g", [1, 2, 4, 8, 12, 16, 32])
 def test_group_and_head_dim_variants(orc, dtype, d, g):
-    if g == 32 and (dtype != workloads.FP16 or d != 128):
-        pytest.skip("G = 32 runs on the MFMA kernel only (fp16, D = 128)")
+    if g == 32 and dtype != workloads.FP16:
+        pytest.skip("G = 32 runs on the MFMA kernels only (fp16)")
     hkv = 2
     w = workloads.random_geometry(70 + g + d, batch=3, page_size=16, max_len=900, dtype=dtype,
                                   num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d)
