@@ -182,8 +182,8 @@ int paged_decode_plan(int32_t batch, const int32_t *indptr,
  * are the (validated) CSR; request_indices/kv_tile_indices the plan's.
  * Outputs: v_partial [num_chunks, Hq, D] fp32 and lse_partial [num_chunks,
  * Hq] fp32.  Supported: D in {64, 128} with G in {1, 2, 4, 8, 12, 16};
- * and G in {24, 32} for fp16 and D = 128, at any page size (the MFMA
- * kernels; paged_decode_kernel_kind() tells which kernel serves a shape).
+ * and G in {24, 32} for fp16, at any page size (the MFMA kernels;
+ * paged_decode_kernel_kind() tells which kernel serves a shape).
  * Other shapes return PD_E_UNSUPPORTED before any launch.
  * ---------------------------------------------------------------------- */
 int paged_decode_partial(const void *q, const void *k_pool, const void *v_pool,
@@ -536,15 +536,15 @@ int paged_decode_default_target_wgs(int32_t device, int32_t group_size, int32_t 
                                     int32_t dtype, int32_t num_kv_heads);
 
 /* Which partial kernel paged_decode_partial launches for a shape:
- * 2 = MFMA kernel (fp16, head_dim 128, group 1, 2, 4, 8, 12, 16, 24 or 32,
- *     page_size a power-of-two multiple of 16, in-page offsets below 2^31
- *     bytes);
+ * 2 = MFMA kernel (fp16, head_dim 64 or 128, group 1, 2, 4, 8, 12, 16, 24
+ *     or 32, page_size a power-of-two multiple of 16, in-page offsets below
+ *     2^31 bytes);
  * 3 = any-page MFMA kernel (the same dtype, head_dim and groups at every
  *     other page size: a 16-token tile may span 16 pages);
  * 1 = page kernel (256-byte K/V rows, group 4, 8 or 16, page_size a
  *     power-of-two multiple of the 64/group slots of one step), for the
- *     shapes the MFMA kernels do not take (fp32 with head_dim 64, or with
- *     paged_decode_set_kernel_choice(2));
+ *     shapes the MFMA kernels do not take (fp32 with head_dim 64, or fp16
+ *     with paged_decode_set_kernel_choice(2));
  * 0 = token kernel (every other supported shape);
  * negative = unsupported (PD_E_UNSUPPORTED).
  * The answer follows paged_decode_set_kernel_choice().  Host only: no device
