@@ -105,6 +105,8 @@ def parse():
                         "config is 4)")
     p.add_argument("--page-size", type=int, default=16,
                    help="long_context_fp16: tokens per page (the metric config is 16)")
+    p.add_argument("--head-dim", type=int, default=128, choices=[64, 128],
+                   help="long_context_fp16: head dim (the metric config is 128)")
     p.add_argument("--kernel-choice", type=int, default=0, choices=[0, 1, 2],
                    help="0 default kernels, 1 token kernel only, 2 no MFMA kernel")
     p.add_argument("--sweep-chunks", action="store_true",
@@ -151,7 +153,7 @@ def main():
         w = workloads.folded_sparse(workloads.token_sparse_fp16())
     elif args.workload == "long_context_fp16":
         w = workloads.long_context_fp16(num_qo_heads=8 * args.group_size,
-                                        page_size=args.page_size)
+                                        page_size=args.page_size, head_dim=args.head_dim)
     else:
         w = getattr(workloads, args.workload)()
     pool_pages = w.k_pool.shape[0]
@@ -382,7 +384,8 @@ def main():
         res["merge_and_gap_us"] = round((step_s - part_s) * 1e6, 2)
         # the committed counter summary covers the default long-context run only
         default_run = (args.workload == "long_context_fp16" and args.group_size == 4 and
-                       args.page_size == 16 and args.kernel_choice == 0)
+                       args.page_size == 16 and args.head_dim == 128 and
+                       args.kernel_choice == 0)
         kind = B.paged_decode_kernel_kind(B.PD_DTYPE_FP16 if w.dtype == workloads.FP16 else
                                           B.PD_DTYPE_FP32, w.head_dim,
                                           w.num_qo_heads // w.num_kv_heads, w.page_size,

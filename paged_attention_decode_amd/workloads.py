@@ -191,7 +191,7 @@ def batched_fp16(seed=2, poison_unused=False):
     return poison_invisible(w) if poison_unused else w
 
 
-def long_context_fp16(seed=3, poison_unused=False, num_qo_heads=32, page_size=16):
+def long_context_fp16(seed=3, poison_unused=False, num_qo_heads=32, page_size=16, head_dim=128):
     """Long-context split-KV: B=4, Hq=32, Hkv=8, D=128, page_size=16, fp16.
     Requests 0-2 see 32768 tokens from position 0.  Request 3 is a sliding
     window of 4096 visible tokens whose first visible token sits at entry 7 of
@@ -199,9 +199,10 @@ def long_context_fp16(seed=3, poison_unused=False, num_qo_heads=32, page_size=16
     the 1792 pages before the window are released.  Pool = 2x the live
     pages, drawn without replacement.  num_qo_heads other than 32 gives the
     same KV geometry with larger query groups (G = num_qo_heads / 8), and
-    page_size other than 16 the same token windows in pages of that size."""
+    page_size other than 16 the same token windows in pages of that size, and
+    head_dim other than 128 rows of that many halves."""
     rng = _rng(seed)
-    ps, hq, hkv, d = page_size, num_qo_heads, 8, 128
+    ps, hq, hkv, d = page_size, num_qo_heads, 8, head_dim
     wl = np.array([32768, 32768, 32768, 32768 + 7], np.int32)
     ls = np.array([0, 0, 0, 32768 + 7 - 4096], np.int32)
     live = sum(-(-int(w) // ps) - int(s) // ps for w, s in zip(wl, ls))
