@@ -925,7 +925,8 @@ def test_pool_pages_past_4gib(orc, g, ps, choice):
 
 @pytest.mark.parametrize("g", [8, 16, 32])
 @pytest.mark.parametrize("ps", [16, 1])
-def test_mfma_kernel_peaked_scores(orc, g, ps):
+@pytest.mark.parametrize("d", [128, 64])
+def test_mfma_kernel_peaked_scores(orc, g, ps, d):
     """Queries scaled by 8: natural-unit scores have a standard deviation of
     about 8, so a few tokens carry most of each head's weight -- the case in
     which rounding the probabilities to fp16 for the value product costs the
@@ -933,10 +934,11 @@ def test_mfma_kernel_peaked_scores(orc, g, ps):
     part plus an fp16 remainder, so its error stays far inside the fp16
     tolerance; the bound asserted here is a quarter of it.  Page size 16
     runs the page-tiled MFMA kernel, page size 1 the any-page one."""
-    w = workloads.random_geometry(700 + g, batch=4, page_size=ps, max_len=3000,
-                                  num_qo_heads=g * 8, num_kv_heads=8, p_empty=0.0, p_trim=0.5)
+    w = workloads.random_geometry(700 + g + d, batch=4, page_size=ps, max_len=3000,
+                                  num_qo_heads=g * 8, num_kv_heads=8, head_dim=d, p_empty=0.0,
+                                  p_trim=0.5)
     w.q[:] = (w.q.astype(np.float32) * 8).astype(np.float16)
-    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, 128, g, ps, 8 * 128) == (
+    assert B.paged_decode_kernel_kind(B.PD_DTYPE_FP16, d, g, ps, 8 * d) == (
         2 if ps == 16 else 3)
     dec = run_flat(orc, w, target=0, fixed=4 * 16 // ps)
     ocsr = orc.csr_from_block_tables(w.block_tables, w.logical_start, w.written_len, ps)
@@ -977,14 +979,16 @@ def ramp_keys(orc, w, slope_log2):
 
 @pytest.mark.parametrize("g", [4, 16])
 @pytest.mark.parametrize("ps", [16, 5])
-def test_scores_ramp_rescale_every_step(orc, g, ps, mode):
+@pytest.mark.parametrize("d", [128, 64])
+def test_scores_ramp_rescale_every_step(orc, g, ps, d, mode):
     """Scores that rise by 0.6 log2 units per token for one head of every KV
     head (and fall or wander for the others): the running max grows past the
     lazy margin on every step and the accumulators are rescaled each time,
     over a score range of about 900 log2 units.  Every kernel mode, every
     partial row and the merge against the oracle at the usual tolerances."""
-    w = workloads.random_geometry(730 + g + ps, batch=3, page_size=ps, max_len=1500,
-                                  num_qo_heads=g * 4, num_kv_heads=4, p_empty=0.0, p_trim=0.5)
+    w = workloads.random_geometry(730 + g + ps + d, batch=3, page_size=ps, max_len=1500,
+                                  num_qo_heads=g * 4, num_kv_heads=4, head_dim=d, p_empty=0.0,
+                                  p_trim=0.5)
     ramp_keys(orc, w, 0.6)
     run_flat(orc, w, target=0, fixed=16 * 16 // ps, fused=mode["fused"])
 
