@@ -161,9 +161,11 @@ int paged_decode_plan(int32_t batch, const int32_t *indptr,
  * paged_decode_partial -- PR #984 kernel commit and body item 2; issue #898
  * items 1 and 2; sparse-paged-decode doc "Indirection".
  *
- * One workgroup per (chunk n, KV head g): it attends the G = Hq/Hkv query
- * heads of KV head g of request r = request_indices[n] over that chunk's
- * visible tokens, reading every K and V row once for all G heads.  Visible
+ * One unit per (chunk n, KV head g): it attends the G = Hq/Hkv query heads
+ * of KV head g of request r = request_indices[n] over that chunk's visible
+ * tokens, reading every K and V row once for all G heads.  A unit is one
+ * wave (or a few, for small head counts); a workgroup takes 1 to 8 KV heads
+ * of one chunk.  Visible
  * token i of request r lives in page indices[indptr[r] + (fpo_r + i) /
  * page_size] at entry (fpo_r + i) % page_size; the chunk t =
  * kv_tile_indices[n] covers tokens [max(0, t*c*ps - fpo_r), min(n_r,
