@@ -1056,6 +1056,28 @@ def test_reverse_order_pages(orc):
     run_flat(orc, w, target=128)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(orc, seed):
+    """Shapes drawn at random over every axis the kernel choice looks at:
+    dtype, head dim, group (1 to 32), KV heads (odd counts included, which
+    give one KV head per workgroup), page size (1 to 64, powers of two and
+    not), chunk size (the plan's, one page, three pages) and ragged windows
+    -- each against the oracle, every partial row included."""
+    rng = np.random.Generator(np.random.PCG64(900 + seed))
+    dtype = workloads.FP32 if rng.random() < 0.25 else workloads.FP16
+    d = int(rng.choice([64, 128]))
+    groups = [1, 2, 4, 8, 12, 16] + ([24, 32] if dtype == workloads.FP16 else [])
+    g = int(rng.choice(groups))
+    hkv = int(rng.choice([1, 2, 3, 5, 6, 8]))
+    ps = int(rng.choice([1, 2, 3, 5, 8, 16, 32, 48, 64]))
+    fixed = int(rng.choice([0, 1, 3]))
+    w = workloads.random_geometry(910 + seed, batch=int(rng.integers(1, 6)), page_size=ps,
+                                  max_len=int(rng.integers(1, 1500)), dtype=dtype,
+                                  num_qo_heads=g * hkv, num_kv_heads=hkv, head_dim=d,
+                                  p_empty=0.1, p_trim=0.5)
+    run_flat(orc, w, target=0, fixed=fixed)
+
+
 def test_windows_start_mid_page_single_page(orc):
     # one-page windows whose first entry is not 0, plus a page-crossing window
     w = workloads.generic("midpage", seed=62, dtype=workloads.FP32, page_size=16,
