@@ -374,7 +374,7 @@ int paged_merge_states(const float *v_in, const float *lse_in, const int32_t *o_
  * that no level's grid has to fill the GPU alone; otherwise each table is
  * one launch of the kernel paged_decode_partial would pick.
  * heads_per_workgroup: KV heads per workgroup of the one-grid form (1, 2, 4
- * or 8 dividing num_kv_heads), or 0 for two (one if num_kv_heads is odd):
+ * or 8 dividing num_kv_heads), or 0 for one:
  * the shared level has few chunks, and narrow workgroups spread it over
  * more CUs.
  * DEVICE: q, pools (strides, dtype and alignment as paged_decode_partial),

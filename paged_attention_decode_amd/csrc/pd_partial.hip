@@ -1931,12 +1931,12 @@ extern "C" int paged_cascade_partial(const void *q, int32_t batch, const int32_t
     }
     // every stacked launch runs on the MFMA kernel: the tables share grids of
     // up to kMaxTables tables, the per-request level on the same kernel with
-    // its group as a run-time value.  Default width: two KV heads per
-    // workgroup (one for an odd count): the shared level has few chunks, so
-    // narrow workgroups spread it over many CUs.  In sweeps on MI355X (4 to
-    // 16 members, 8K to 32K shared tokens) two heads per workgroup was the
-    // best width or within a few percent of it, and eight up to 2x slower.
-    const int hpw = heads_per_workgroup ? heads_per_workgroup : (num_kv_heads % 2 ? 1 : 2);
+    // its group as a run-time value.  Default width: one KV head per
+    // workgroup: the shared level has few chunks, so narrow workgroups spread
+    // it over many CUs.  In sweeps on MI355X (4 to 16 members, 8K to 32K
+    // shared tokens) at the same chunking, one head per workgroup was as fast
+    // as two or faster (up to 5%), and eight up to 2x slower.
+    const int hpw = heads_per_workgroup ? heads_per_workgroup : 1;
     int ht = 1;
     for (int j = 0; j < ntab; ++j)
         if (args[j].group > 16) ht = 2;

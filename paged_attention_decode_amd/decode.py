@@ -264,22 +264,25 @@ class CascadeDecode:
                                                   -(-min_level0_tokens // page_size))
         # When the first level-0 launch and level 1 run as one grid (pair
         # launch: both on the MFMA kernel), they share the GPU.  By default
-        # the workgroups hold two KV heads, level 0 is planned for about one
-        # workgroup per CU (its chunks are few and long, and each adds
-        # members*Hq partial rows to the merge), and level 1 for as many
-        # units.  Sweeps on MI355X (4 to 16 members, 8K
-        # to 32K shared tokens; level-1 chunks of 1 to 33 pages) put this
-        # within about 10% of the best chunking, where either level planned
-        # for the whole GPU was up to 1.5x slower.
+        # level 0 is planned for about two (chunk, KV head) units per CU (its
+        # chunks are few and long, and each adds members*Hq partial rows to
+        # the merge), and level 1 for as many units.  Sweeps on MI355X (4 to
+        # 16 members, 8K to 32K shared tokens; level-1 chunks of 1 to 33
+        # pages) put this within about 10% of the best chunking, where either
+        # level planned for the whole GPU was up to 1.5x slower.  The
+        # workgroups hold one KV head each: at the same chunking that was as
+        # fast as two or faster (graph-replayed, 4 x 8K shared tokens 19.1
+        # against 20.1 us, 16 x 8K 46.9 against 47.7, 4 x 32K 36.6 against
+        # 37.8-38.4, equal at 8 x 8K and 8 x 16K).
         t0, t1 = target_wgs_level0 or target_wgs, target_wgs
         g0 = self.subgroups[0].size * g
         self.pair_eligible = pair_launch and g <= 16 and B.load().paged_decode_kernel_kind(
             pd_dtype, head_dim, g0, page_size, num_kv_heads * head_dim) == 2
         if self.pair_eligible and not heads_per_workgroup:
-            self.heads_per_workgroup = 1 if num_kv_heads % 2 else 2
+            self.heads_per_workgroup = 1
         if self.pair_eligible and not (target_wgs_level0 or target_wgs):
             cus = torch.cuda.get_device_properties(self.device).multi_processor_count
-            t0 = cus * self.heads_per_workgroup
+            t0 = 2 * cus
             t1 = t0
         self.targets = (t0, t1)
         for sub in self.subgroups:
