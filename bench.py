@@ -119,6 +119,10 @@ def parse():
                    help="skip the streaming-read ceiling measurement")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    p.add_argument("--trace-graph", action="store_true",
+                   help="time the step only: --steps eager steps, then --steps steps replayed "
+                        "from HIP graphs of 30, in that order (for a kernel trace that "
+                        "tells the two apart by dispatch order); flat workloads")
     return p.parse_args()
 
 
@@ -259,6 +263,22 @@ def main():
                 fn(i)
                 i += 1
             torch.cuda.synchronize()
+
+    if args.trace_graph:
+        if partial_only is None:
+            print("bench.py: --trace-graph times the flat decode workloads", file=sys.stderr)
+            sys.exit(2)
+        settle(step)
+        run_steps(args.warmup, step)
+        step_s, _ = run_steps(args.steps, step)
+        g_step = graph_steps(args.steps, step)
+        print(json.dumps({"workload": w.name, "plan": plan, "eager_step_us": round(step_s * 1e6, 2),
+                          "graph_step_us": round(g_step * 1e6, 2),
+                          "dispatch_order": "settle + %d warmup + %d timed eager steps; then "
+                                            "3 eager steps, untimed replays of a 30-step graph "
+                                            "for 50 ms, and %d timed replays" % (
+                                                args.warmup, args.steps, max(1, args.steps // 30))}))
+        return
 
     # settle and warmup, then the timed steps (the metric)
     settle(step)

@@ -9,6 +9,8 @@ arguments and allocates caller-owned buffers with torch.
 """
 from __future__ import annotations
 
+import time
+
 import numpy as np
 import torch
 
@@ -622,11 +624,16 @@ class MlaDecode:
         return self.out, self.lse
 
 
-def graph_time(fn, n: int = 120, per_graph: int = 30) -> float:
+def graph_time(fn, n: int = 120, per_graph: int = 30, settle_s: float = 0.05) -> float:
     """GPU seconds per call of fn(i): per_graph calls are captured once in a
     HIP graph and the graph is replayed n // per_graph times between events
     on the current stream, so the host's per-launch cost is not counted.  fn
-    must launch work only (no allocation, no synchronization)."""
+    must launch work only (no allocation, no synchronization).  Before the
+    timed replays the graph is replayed, untimed, for settle_s seconds of
+    wall time: capture leaves the GPU idle, and a GPU coming out of idle runs
+    its first milliseconds of work measurably slower (on MI355X a kernel
+    trace of the long-context step showed each of four timed 30-step replays
+    faster than the one before without it, 71.2 down to 69.8 us per step)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -640,9 +647,13 @@ def graph_time(fn, n: int = 120, per_graph: int = 30) -> float:
             fn(i)
     torch.cuda.synchronize()
     reps = max(1, n // per_graph)
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
+    t_end = time.time() + settle_s
+    while True:
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        if time.time() >= t_end:
+            break
     cur = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
