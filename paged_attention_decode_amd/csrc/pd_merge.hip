@@ -164,11 +164,12 @@ constexpr int kWideUnroll = PD_MERGE_WIDE_UNROLL;
 // merge takes each slice in one wave (merge_wave_kernel below): without the
 // cross-wave LDS combine and its barrier the long-context step went from
 // 69.2 to 68.6-68.8 us on MI355X with 8 row lanes x 10 rows in flight; 16 x 5,
-// 4 x 20 and 8 x 16 measured no better.  The cascade merge, whose groups are
-// longer, keeps four waves of row lanes.
+// 4 x 20 and 8 x 16 measured no better.  The cascade merge takes the same
+// one-wave slices with 11 rows in flight per row lane (its launcher gives the
+// measurements).
 constexpr int kNarrowDL = 8;          // float4 dim lanes per slice, other widths
 constexpr int kWaveUnroll = 10;       // one-wave kernel: rows in flight per row lane
-constexpr int kSliceUnroll = 4;       // four-wave kernel: rows in flight per row lane
+constexpr int kCascadeWaveUnroll = 11;    // the same, for the cascade merge
 
 // State of a partial merge: running max m (NaN once a NaN lse was seen),
 // weight sum w relative to m, weighted sum a relative to m.
@@ -626,10 +627,15 @@ extern "C" int paged_cascade_merge_states(const float *v0, const float *lse0, in
     const CascadeRows rows{v0, lse0, v1, lse1, l0_desc, o_indptr1, n0,
                            num_qo_heads / num_kv_heads};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // 32-dim slices of four waves.  At 4 members x 8192 shared tokens (about
-    // 300 rows per group), 16- and 8-dim slices, or 8 rows in flight per lane,
-    // were as fast or slower (MI355X); the flat merge's one-wave kernel took
-    // the step from 20.6 to 21.2 us.
+    // 32-dim slices of one wave, 8 row lanes with 11 rows in flight each (88
+    // rows per pass).  The shared level's plan gives a group 64 level-0 rows
+    // plus the request's own level-1 rows, about 81 at 4 members x 8192
+    // shared tokens.  Measured on MI355X against four-wave slices (4 rows in
+    // flight per lane): step 18.4-18.6 against 19.0-19.1 us there, 34.1-34.2
+    // against 34.7 us at 4 x 32768 and 44.3 against 45.1 us at 16 x 8192;
+    // 10 rows in flight (two passes for 81 rows) 19.7 us, 12 rows 18.6 us.
+    // Under an earlier plan of about 300 rows per group the four-wave kernel
+    // was the faster one.
     const bool wide = head_dim % (4 * kWideDL) == 0;
     const int64_t nblk =
         int64_t(batch) * num_qo_heads * (head_dim / (4 * (wide ? kWideDL : kNarrowDL)));
@@ -639,8 +645,8 @@ extern "C" int paged_cascade_merge_states(const float *v0, const float *lse0, in
                            dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_qo_heads, head_dim,
                            v_out, lse_out);
     else
-        hipLaunchKernelGGL((merge_slice_kernel<kNarrowDL, kSliceUnroll, CascadeRows>),
-                           dim3(uint32_t(nblk)), dim3(256), 0, s, rows, num_qo_heads, head_dim,
+        hipLaunchKernelGGL((merge_wave_kernel<kNarrowDL, kCascadeWaveUnroll, CascadeRows>),
+                           dim3(uint32_t(nblk)), dim3(64), 0, s, rows, num_qo_heads, head_dim,
                            v_out, lse_out);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess)
