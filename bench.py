@@ -145,6 +145,10 @@ def main():
     B.load()
     B.paged_decode_set_kernel_choice(args.kernel_choice)
     dev = torch.device("cuda:0")
+    if args.trace_graph and args.workload in ("block_sparse_fp16", "mla_paged_fp16",
+                                              "dsa_sparse_fp16", "cascade_fp16"):
+        print("bench.py: --trace-graph times the flat decode workloads", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "block_sparse_fp16":
         return block_sparse(args, torch, B, PD, workloads, dev)
     if args.workload in ("mla_paged_fp16", "dsa_sparse_fp16"):
@@ -265,9 +269,6 @@ def main():
             torch.cuda.synchronize()
 
     if args.trace_graph:
-        if partial_only is None:
-            print("bench.py: --trace-graph times the flat decode workloads", file=sys.stderr)
-            sys.exit(2)
         settle(step)
         run_steps(args.warmup, step)
         step_s, _ = run_steps(args.steps, step)
