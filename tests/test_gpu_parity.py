@@ -648,9 +648,9 @@ def test_cascade_mixed_batch_and_subgroups(orc, members, hq, in_place):
 def test_cascade_in_place_merge_equals_gathered_merge(orc, members, hq, d):
     """The merge that reads the stacked level-0 rows in place and the merge
     of the gathered copy see the same rows (several stacked launches
-    included): they agree to rounding (the in-place merge folds a group with
-    four waves of row lanes, the flat merge with one), and both match the
-    oracle.  A row read from the wrong place would differ at the scale of the
+    included): they agree to rounding (the in-place merge folds a group in
+    load batches of 11 rows per row lane, the flat merge in batches of 10),
+    and both match the oracle.  A row read from the wrong place would differ at the scale of the
     values themselves."""
     w = workloads.cascade_fp16(seed=90 + members, members=members, prefix_tokens=1024,
                                suffix_lo=16, suffix_hi=400, hq=hq, hkv=hq // 4, d=d,
@@ -675,18 +675,24 @@ def test_cascade_in_place_merge_equals_gathered_merge(orc, members, hq, d):
     check_close(oa.cpu().numpy(), la.cpu().numpy(), ref_v, ref_l, w.dtype, "in-place cascade")
 
 
-@pytest.mark.parametrize("d", [128, 512, 64])
-def test_cascade_merge_states_against_oracle(orc, d):
+@pytest.mark.parametrize("d,n0,counts", [(128, 7, (2, 0, 1, 4, 3)), (512, 7, (2, 0, 1, 4, 3)),
+                                         (64, 7, (2, 0, 1, 4, 3)),
+                                         (128, 150, (2, 0, 61, 97, 3)),
+                                         (64, 88, (0, 0, 1, 130, 89))])
+def test_cascade_merge_states_against_oracle(orc, d, n0, counts):
     """The in-place cascade merge on synthetic states: members 0, 2, 3 of 5
     requests stacked two per launch (launches of 2 and 1 members), empty
     chunks (lse = -inf, V never read), a member with one own row, and a
     non-member with none (zeros, -inf).  The expected groups are gathered on
-    the host from the stacking rule and merged by the oracle."""
-    rng = np.random.default_rng(95 + d)
-    batch, hkv, g, n0, per = 5, 2, 4, 7, 2
+    the host from the stacking rule and merged by the oracle.  The long cases
+    (groups of up to 247 rows) take the one-wave merge through several
+    88-row load passes; one group ends one row past a pass (88 + 1), one
+    non-member group is exactly 89 rows."""
+    rng = np.random.default_rng(95 + d + n0)
+    batch, hkv, g, per = 5, 2, 4, 2
     hq = hkv * g
     members = np.array([0, 2, 3], np.int32)
-    counts = np.array([2, 0, 1, 4, 3])
+    counts = np.array(counts)
     o1 = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     n1 = int(o1[-1])
     rows0 = n0 * members.size * hq
