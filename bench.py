@@ -15,8 +15,9 @@ milliseconds of work about 5% slower).  Consecutive steps read
 different copies of the K/V pools (3 by default, each larger than the 256 MB
 last-level cache), so every step streams its KV bytes from HBM.  `value` =
 algorithmic KV bytes / (region time / K).  The partial kernel alone is timed
-the same way for the roofline entry, and an isolated step after a 1 GiB
-cache flush, bracketed by its own event pair, is reported for reference.
+the same way for the roofline entry; an isolated step after a 1 GiB cache
+flush, bracketed by its own event pair, and back-to-back steps that all read
+one pool copy ("warm") are reported for reference.
 
 The GPU result is checked against the f64 oracle on the same inputs before
 anything is reported (`parity`); the oracle's own time on the host cores is
@@ -344,6 +345,13 @@ def main():
     torch.cuda.synchronize()
     iso_s = np.array([a.elapsed_time(b) * 1e-3 for a, b in iso])
 
+    # reference: "warm" steps, back to back on one pool copy (whatever of it
+    # the last-level cache keeps between steps is found there)
+    warm = lambda i: runner.run(q, kv[0][0], kv[0][1], w.sm_scale)   # noqa: E731
+    settle(warm)
+    run_steps(args.warmup, warm)
+    warm_s, _ = run_steps(args.steps, warm)
+
     value = kv_bytes / step_s / 1e9
     total_tokens = int(w.visible_tokens.sum())
     res = {
@@ -380,6 +388,7 @@ def main():
                                      "p50": round(float(np.median(iso_s)) * 1e6, 2),
                                      "p90": round(float(np.percentile(iso_s, 90)) * 1e6, 2),
                                      "kv_gbs": round(kv_bytes / float(iso_s.mean()) / 1e9, 2)},
+        "warm_step_us": round(warm_s * 1e6, 2),
         "setup_s": round(setup_s, 1),
         "parity": {"max_abs_v": dv, "max_abs_lse2": dl, "tol_v": tv, "tol_lse2": tl,
                    "ok": bool(parity_ok)},
